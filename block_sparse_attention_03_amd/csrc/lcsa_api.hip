@@ -1,0 +1,195 @@
+// C-ABI entry points that enqueue device work. Every argument is validated
+// on the host (lcsa_host.cpp) before the first HIP call; on any failure
+// nothing is enqueued.
+#include <cmath>
+#include <numeric>
+
+#include "lcsa_host.h"
+#include "lcsa_kernels.h"
+
+using namespace lcsa;
+
+namespace {
+
+RingView make_view(const lcsa_kv_cache& c) {
+  RingView v{};
+  v.n = c.count;
+  for (int32_t i = 0; i < c.count; ++i) {
+    const int32_t s = (c.head + i) % c.n_slots;
+    v.slot[i] = s;
+    v.abs_tb[i] = c.abs_tb[s];
+  }
+  return v;
+}
+
+lcsa_status device_status(hipError_t e, const char* what) {
+  if (e != hipSuccess)
+    return fail(LCSA_ERR_DEVICE, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+lcsa_status lcsa_partition_pool(const lcsa_geom* g, const void* q, const void* k, const void* v,
+                                void* q_blk, double* q_pool, lcsa_kv_cache* cache,
+                                int32_t first_slot, void* stream) {
+  lcsa_status st;
+  if ((st = check_geom(g, "lcsa_partition_pool")) || (st = check_cache(cache)) ||
+      (st = check_matches_cache(g, cache)))
+    return st;
+  const bool has_q = q || q_blk || q_pool;
+  if (has_q && !(q && q_blk && q_pool))
+    return fail(LCSA_ERR_NULL, "q, q_blk and q_pool must be all NULL or all non-NULL");
+  if ((st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
+      (has_q && ((st = check_ptr(q, "q")) || (st = check_ptr(q_blk, "q_blk")) ||
+                 (st = check_ptr(q_pool, "q_pool")))))
+    return st;
+  const int32_t ntb = g->frames / 2;
+  if (ntb == 0) return ok();
+  if (first_slot < 0 || first_slot >= cache->n_slots)
+    return fail(LCSA_ERR_PARAM, "first_slot %d outside [0, %d)", first_slot, cache->n_slots);
+  for (int32_t t = 0; t < ntb; ++t) {
+    const int32_t slot = (first_slot + t) % cache->n_slots;
+    const int32_t pos = (slot - cache->head + cache->n_slots) % cache->n_slots;
+    if (pos >= cache->count)
+      return fail(LCSA_ERR_CAPACITY,
+                  "slot %d (TB %d of the chunk) is not held by the cache; append first", slot, t);
+  }
+  PartitionArgs a{};
+  a.q = has_q ? q : nullptr;
+  a.k = k;
+  a.v = v;
+  a.q_blk = q_blk;
+  a.q_pool = q_pool;
+  a.k_ring = cache->k_ring;
+  a.v_ring = cache->v_ring;
+  a.kpool_ring = cache->kpool_ring;
+  a.B = g->batch;
+  a.NH = g->heads;
+  a.D = g->head_dim;
+  a.T = g->frames;
+  a.H = g->height;
+  a.W = g->width;
+  a.n_slots = cache->n_slots;
+  a.first_slot = first_slot;
+  a.dtype = g->dtype;
+  return device_status(launch_partition_pool(a, (hipStream_t)stream), "lcsa_partition_pool");
+}
+
+lcsa_status lcsa_draft_mask(const lcsa_geom* gq, const double* q_pool, int64_t q_first_abs_tb,
+                            const lcsa_kv_cache* cache, const lcsa_select_params* params,
+                            int32_t kmax, int32_t* sel_idx, int32_t* sel_cnt, double* probs,
+                            void* stream) {
+  lcsa_status st;
+  if ((st = check_geom(gq, "lcsa_draft_mask")) || (st = check_params(params)) ||
+      (st = check_cache(cache)) || (st = check_matches_cache(gq, cache)) ||
+      (st = check_ptr(q_pool, "q_pool")) || (st = check_ptr(sel_idx, "sel_idx")) ||
+      (st = check_ptr(sel_cnt, "sel_cnt")) || (st = check_ptr(probs, "probs", true)))
+    return st;
+  if (q_first_abs_tb < 0) return fail(LCSA_ERR_PARAM, "q_first_abs_tb < 0");
+  const int32_t ntb = gq->frames / 2;
+  if (ntb == 0) return ok();
+  int64_t amax = 0;
+  const int32_t need = max_topk(*gq, q_first_abs_tb, *cache, *params, &amax);
+  if (kmax < need || kmax < 1)
+    return fail(LCSA_ERR_CAPACITY, "kmax %d is smaller than the largest k %d", kmax, need);
+  if (amax > LCSA_MAX_CANDIDATES)
+    return fail(LCSA_ERR_CAPACITY, "a row has %lld candidates; at most %d are supported",
+                (long long)amax, LCSA_MAX_CANDIDATES);
+
+  DraftArgs a{};
+  a.q_pool = q_pool;
+  a.kpool_ring = cache->kpool_ring;
+  a.sel_idx = sel_idx;
+  a.sel_cnt = sel_cnt;
+  a.probs = probs;
+  a.B = gq->batch;
+  a.NH = gq->heads;
+  a.D = gq->head_dim;
+  a.ntb_q = ntb;
+  a.nby = gq->height / 8;
+  a.nbx = gq->width / 8;
+  a.n_slots = cache->n_slots;
+  a.kmax = kmax;
+  a.q_first_abs_tb = q_first_abs_tb;
+  a.view = make_view(*cache);
+  a.local_range = params->local_range;
+  a.border = params->border;
+  a.topk_fixed = params->topk_fixed;
+  a.ratio_base = params->ratio_base;
+  if (params->topk_fixed == 0) {
+    __int128 num = (__int128)params->ratio_num *
+                   (params->scale_by_resolution ? (int64_t)params->ref_h * params->ref_w : 1);
+    __int128 den = (__int128)params->ratio_den *
+                   (params->scale_by_resolution ? (int64_t)params->out_h * params->out_w : 1);
+    // reduce the fraction so the device's 64 x 64-bit product is exact
+    __int128 x = num, y = den;
+    while (y) {
+      const __int128 t = x % y;
+      x = y;
+      y = t;
+    }
+    num /= x;
+    den /= x;
+    if (num > INT64_MAX || den > INT64_MAX)
+      return fail(LCSA_ERR_PARAM, "ratio rule does not reduce to 64-bit integers");
+    a.ratio_num = (int64_t)num;
+    a.ratio_den = (int64_t)den;
+  } else {
+    a.ratio_num = 1;
+    a.ratio_den = 1;
+  }
+  a.row_stride = (int32_t)((amax + 1) / 2 * 2);
+  if (a.row_stride < 2) a.row_stride = 2;
+  // Rows per workgroup: the most that still leave >= 2 workgroups per CU
+  // (but at least 2 rows, so a pooled key row serves two queries), then
+  // fewer if the scores would not fit in 64 KB of LDS.
+  const int64_t rows_per_col = (int64_t)a.B * a.NH * a.ntb_q * a.nby;
+  int gx = 8;
+  while (gx > 2 && rows_per_col * ((a.nbx + gx - 1) / gx) < 512) gx /= 2;
+  while (gx > 1 && (int64_t)gx * a.row_stride * 8 > 64 * 1024) gx /= 2;
+  a.gx = gx;
+  return device_status(launch_draft_mask(a, (hipStream_t)stream), "lcsa_draft_mask");
+}
+
+lcsa_status lcsa_block_sparse_attn(const lcsa_geom* gq, const void* q_blk,
+                                   const lcsa_kv_cache* cache, const int32_t* sel_idx,
+                                   const int32_t* sel_cnt, int32_t kmax, float scale, void* out,
+                                   float* lse, void* stream) {
+  lcsa_status st;
+  if ((st = check_geom(gq, "lcsa_block_sparse_attn")) || (st = check_cache(cache)) ||
+      (st = check_matches_cache(gq, cache)) || (st = check_ptr(q_blk, "q_blk")) ||
+      (st = check_ptr(sel_idx, "sel_idx")) || (st = check_ptr(sel_cnt, "sel_cnt")) ||
+      (st = check_ptr(out, "out")) || (st = check_ptr(lse, "lse", true)))
+    return st;
+  if (kmax < 1) return fail(LCSA_ERR_CAPACITY, "kmax %d < 1", kmax);
+  if (!std::isfinite(scale) || scale < 0.f)
+    return fail(LCSA_ERR_PARAM, "scale must be finite and >= 0 (0 = 1/sqrt(D))");
+  if (gq->frames == 0) return ok();
+  if (cache->count == 0)
+    return fail(LCSA_ERR_CAPACITY, "the cache holds no key blocks");
+  AttnArgs a{};
+  a.q_blk = q_blk;
+  a.k_ring = cache->k_ring;
+  a.v_ring = cache->v_ring;
+  a.sel_idx = sel_idx;
+  a.sel_cnt = sel_cnt;
+  a.out = out;
+  a.lse = lse;
+  a.B = gq->batch;
+  a.NH = gq->heads;
+  a.D = gq->head_dim;
+  a.T = gq->frames;
+  a.H = gq->height;
+  a.W = gq->width;
+  a.n_slots = cache->n_slots;
+  a.kmax = kmax;
+  a.view = make_view(*cache);
+  a.scale = scale == 0.f ? 1.f / std::sqrt((float)gq->head_dim) : scale;
+  return device_status(launch_block_sparse_attn(a, gq->dtype, (hipStream_t)stream),
+                       "lcsa_block_sparse_attn");
+}
+
+}  // extern "C"

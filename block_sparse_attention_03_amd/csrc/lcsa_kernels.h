@@ -1,0 +1,68 @@
+// Launch interface between the C-ABI entry points (lcsa_api.hip) and the
+// gfx950 kernels. Arguments are validated before these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "../../include/lcsa.h"
+
+namespace lcsa {
+
+// Order of the held temporal blocks, oldest first, passed by value so a
+// step needs no host-to-device copy.
+struct RingView {
+  int32_t n;                         // TBs in the view
+  int32_t slot[LCSA_MAX_SLOTS];      // ring slot of view position p
+  int64_t abs_tb[LCSA_MAX_SLOTS];    // absolute TB index of view position p
+};
+
+struct PartitionArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* q_blk;
+  double* q_pool;
+  void* k_ring;
+  void* v_ring;
+  double* kpool_ring;
+  int32_t B, NH, D, T, H, W;
+  int32_t n_slots, first_slot;
+  int32_t dtype;
+};
+
+struct DraftArgs {
+  const double* q_pool;     // [B][NH][nq][D]
+  const double* kpool_ring; // [B][NH][n_slots][D][nS]
+  int32_t* sel_idx;         // [B][NH][nq][kmax]
+  int32_t* sel_cnt;         // [B][NH][nq]
+  double* probs;            // [B][NH][nq][n_keys] or null
+  int32_t B, NH, D, ntb_q, nby, nbx, n_slots, kmax;
+  int64_t q_first_abs_tb;
+  RingView view;
+  int32_t local_range, border, topk_fixed, ratio_base;
+  int64_t ratio_num, ratio_den;      // reduced fraction incl. resolution scale
+  int32_t row_stride;                // LDS scores per row (>= max candidates)
+  int32_t gx;                        // query rows (consecutive bx) per workgroup
+};
+
+struct AttnArgs {
+  const void* q_blk;        // [B][NH][nq][128][D]
+  const void* k_ring;       // [B][NH][n_slots][nS][128][D]
+  const void* v_ring;       // [B][NH][n_slots][nS][D][128]
+  const int32_t* sel_idx;   // [B][NH][nq][kmax]
+  const int32_t* sel_cnt;   // [B][NH][nq]
+  void* out;                // [B][T][H][W][NH][D]
+  float* lse;               // [B][NH][nq][128] or null
+  int32_t B, NH, D, T, H, W;
+  int32_t n_slots, kmax;
+  RingView view;
+  float scale;              // softmax scale on q.k
+};
+
+hipError_t launch_partition_pool(const PartitionArgs& a, hipStream_t s);
+hipError_t launch_draft_mask(const DraftArgs& a, hipStream_t s);
+hipError_t launch_block_sparse_attn(const AttnArgs& a, int32_t dtype, hipStream_t s);
+
+}  // namespace lcsa

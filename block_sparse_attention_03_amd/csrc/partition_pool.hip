@@ -1,0 +1,192 @@
+// Steps 1-2 of LCSA: 3D window partition and block-mean pooling, fused.
+//
+// [HW] "How FlashVSR works" 2.2 step 1: q, k, v are cut into non-overlapping
+// windows of 2 latent frames x 8 x 8 tokens (128 tokens per block). Step 3
+// of the same section compresses each block of q and k into one vector by
+// its mean ([FN] "FlashVSR" note, Key design 2: block-mean pooling before
+// the coarse block map).
+//
+// One workgroup moves one (batch, head, block) for q, k and v. The token
+// layout keeps a token's D channels contiguous (D*esize = 128..512 bytes),
+// so every read is a run of whole 16-byte chunks; every write is a fully
+// contiguous 128 x D tile. V is written transposed ([D][128]) because the
+// attention kernel feeds V^T to the matrix cores as the A operand. Block
+// means are accumulated in float64 (exact for bf16 inputs) and written as
+// float64, so the draft selection downstream takes its decision on exact
+// pooled values. HBM-bound: the algorithmic traffic of one (block, head) is
+// 3 tiles read + 3 tiles written + 2 pooled rows.
+#include "lcsa_kernels.h"
+
+namespace lcsa {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <int ESZ>
+__device__ inline void widen_chunk(const uint4& v, double* out);
+
+template <>
+__device__ inline void widen_chunk<2>(const uint4& v, double* out) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = (double)__uint_as_float(w[i] << 16);
+    out[2 * i + 1] = (double)__uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+template <>
+__device__ inline void widen_chunk<4>(const uint4& v, double* out) {
+  out[0] = (double)__uint_as_float(v.x);
+  out[1] = (double)__uint_as_float(v.y);
+  out[2] = (double)__uint_as_float(v.z);
+  out[3] = (double)__uint_as_float(v.w);
+}
+
+template <int ESZ, int D>
+struct Geo {
+  static constexpr int EPC = 16 / ESZ;        // elements per 16-byte chunk
+  static constexpr int CPT = D / EPC;         // chunks per token row
+  static constexpr int ITERS = 128 * CPT / kThreads;
+  static constexpr int TPI = kThreads / CPT;  // tokens covered per iteration
+  static constexpr int PITCH = D * ESZ + 16;  // LDS row pitch of the V stage
+};
+
+// Token-layout element offset of in-block token tau of block (bt, by, bx).
+__device__ inline size_t token_offset(const PartitionArgs& a, int b, int h, int bt, int by, int bx,
+                                      int tau) {
+  const int t = 2 * bt + (tau >> 6);
+  const int y = 8 * by + ((tau >> 3) & 7);
+  const int x = 8 * bx + (tau & 7);
+  return ((((size_t)b * a.T + t) * a.H + y) * a.W + x) * a.NH * a.D + (size_t)h * a.D;
+}
+
+// Copy one 128 x D block to a contiguous tile and (optionally) write its
+// column means to pool[d * pool_stride].
+template <int ESZ, int D>
+__device__ inline void copy_pool(const PartitionArgs& a, const char* src, char* dst,
+                                 double* pool, size_t pool_stride, int b, int h, int bt, int by,
+                                 int bx, double (*red)[16 / ESZ]) {
+  using G = Geo<ESZ, D>;
+  const int tid = threadIdx.x;
+  const int c = tid % G::CPT;
+  const int tsub = tid / G::CPT;
+  uint4 v[G::ITERS];
+#pragma unroll
+  for (int it = 0; it < G::ITERS; ++it) {
+    const int tau = it * G::TPI + tsub;
+    v[it] = *reinterpret_cast<const uint4*>(
+        src + (token_offset(a, b, h, bt, by, bx, tau) + c * G::EPC) * ESZ);
+  }
+  double acc[G::EPC];
+#pragma unroll
+  for (int e = 0; e < G::EPC; ++e) acc[e] = 0.0;
+#pragma unroll
+  for (int it = 0; it < G::ITERS; ++it) {
+    const int tau = it * G::TPI + tsub;
+    *reinterpret_cast<uint4*>(dst + ((size_t)tau * D + c * G::EPC) * ESZ) = v[it];
+    if (pool) {
+      double w[G::EPC];
+      widen_chunk<ESZ>(v[it], w);
+#pragma unroll
+      for (int e = 0; e < G::EPC; ++e) acc[e] += w[e];
+    }
+  }
+  if (!pool) return;
+#pragma unroll
+  for (int e = 0; e < G::EPC; ++e) red[tid][e] = acc[e];
+  __syncthreads();
+  if (tid < D) {
+    const int cc = tid / G::EPC, e = tid % G::EPC;
+    double s = 0.0;
+    for (int ts = 0; ts < G::TPI; ++ts) s += red[ts * G::CPT + cc][e];
+    pool[(size_t)tid * pool_stride] = s / 128.0;
+  }
+  __syncthreads();
+}
+
+template <int ESZ, int D>
+__global__ __launch_bounds__(kThreads) void partition_pool_kernel(PartitionArgs a) {
+  using G = Geo<ESZ, D>;
+  __shared__ double red[kThreads][G::EPC];
+  __shared__ __attribute__((aligned(16))) char vstage[128 * G::PITCH];
+
+  const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int nby = a.H / 8, nbx = a.W / 8, nS = nby * nbx;
+  const int bt = n / nS, s = n % nS, by = s / nbx, bx = s % nbx;
+  const int nq = (a.T / 2) * nS;
+  const size_t tile = (size_t)128 * D;
+  const int slot = (a.first_slot + bt) % a.n_slots;
+  const size_t ring_blk = (((size_t)b * a.NH + h) * a.n_slots + slot) * nS + s;
+
+  if (a.q) {
+    const size_t qb = ((size_t)b * a.NH + h) * nq + n;
+    copy_pool<ESZ, D>(a, (const char*)a.q, (char*)a.q_blk + qb * tile * ESZ, a.q_pool + qb * D, 1,
+                      b, h, bt, by, bx, red);
+  }
+  // k: tile into the ring slot, means d-major into the pooled ring.
+  double* kp = a.kpool_ring + (((size_t)b * a.NH + h) * a.n_slots + slot) * D * nS + s;
+  copy_pool<ESZ, D>(a, (const char*)a.k, (char*)a.k_ring + ring_blk * tile * ESZ, kp, nS, b, h,
+                    bt, by, bx, red);
+
+  // v: stage the block in LDS, then write it transposed ([D][128]).
+  {
+    const int tid = threadIdx.x;
+    const int c = tid % G::CPT;
+    const int tsub = tid / G::CPT;
+    uint4 v[G::ITERS];
+#pragma unroll
+    for (int it = 0; it < G::ITERS; ++it) {
+      const int tau = it * G::TPI + tsub;
+      v[it] = *reinterpret_cast<const uint4*>(
+          (const char*)a.v + (token_offset(a, b, h, bt, by, bx, tau) + c * G::EPC) * ESZ);
+    }
+#pragma unroll
+    for (int it = 0; it < G::ITERS; ++it) {
+      const int tau = it * G::TPI + tsub;
+      *reinterpret_cast<uint4*>(vstage + tau * G::PITCH + c * 16) = v[it];
+    }
+    __syncthreads();
+    char* vdst = (char*)a.v_ring + ring_blk * tile * ESZ;
+    constexpr int KC = 128 / G::EPC;  // 16-byte chunks per transposed row
+#pragma unroll
+    for (int it = 0; it < G::ITERS; ++it) {
+      const int e = it * kThreads + tid;
+      const int d = e / KC, kc = e % KC;
+      uint32_t w[4];
+      if constexpr (ESZ == 2) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t lo = *reinterpret_cast<const uint16_t*>(
+              vstage + (kc * 8 + 2 * u) * G::PITCH + d * 2);
+          const uint32_t hi = *reinterpret_cast<const uint16_t*>(
+              vstage + (kc * 8 + 2 * u + 1) * G::PITCH + d * 2);
+          w[u] = lo | (hi << 16);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          w[u] = *reinterpret_cast<const uint32_t*>(vstage + (kc * 4 + u) * G::PITCH + d * 4);
+      }
+      *reinterpret_cast<uint4*>(vdst + ((size_t)d * 128 + kc * G::EPC) * ESZ) =
+          make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
+template <int ESZ, int D>
+hipError_t launch(const PartitionArgs& a, hipStream_t s) {
+  const int nblk = (a.T / 2) * (a.H / 8) * (a.W / 8);
+  dim3 grid(nblk, a.NH, a.B);
+  hipLaunchKernelGGL((partition_pool_kernel<ESZ, D>), grid, dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_partition_pool(const PartitionArgs& a, hipStream_t s) {
+  if (a.dtype == LCSA_BF16) return a.D == 64 ? launch<2, 64>(a, s) : launch<2, 128>(a, s);
+  return a.D == 64 ? launch<4, 64>(a, s) : launch<4, 128>(a, s);
+}
+
+}  // namespace lcsa

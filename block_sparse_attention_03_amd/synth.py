@@ -28,6 +28,7 @@ tests always use the host generator.
 from __future__ import annotations
 
 import math
+import os
 
 import numpy as np
 
@@ -44,26 +45,46 @@ def field_params(seed: int, tensor_id: int, heads: int, head_dim: int):
     return ft, fy, fx, phi
 
 
+def _frame(seed, tensor_id, params, t, y, x, noise_std):
+    ft, fy, fx, phi = params
+    frame = np.sin(2.0 * math.pi * (ft * t + fy * y + fx * x) + phi)
+    if noise_std:
+        rng = np.random.default_rng(np.random.SeedSequence([seed, tensor_id, t]))
+        frame += noise_std * rng.standard_normal(frame.shape)
+    return frame
+
+
 def field_frames(seed: int, tensor_id: int, heads: int, head_dim: int,
                  height: int, width: int, t0: int, t1: int,
                  batch: int = 1, noise_std: float = 0.5) -> np.ndarray:
     """float64 field for absolute latent frames [t0, t1): [B][T][H][W][NH][D].
 
-    Batch entries b > 0 use seed + 7919*b so that they differ.
+    Batch entries b > 0 use seed + 7919*b so that they differ. Frames are
+    independent (own noise seed), so they are generated on a thread pool.
     """
+    from concurrent.futures import ThreadPoolExecutor
+
     out = np.empty((batch, t1 - t0, height, width, heads, head_dim), np.float64)
     y = np.arange(height, dtype=np.float64)[:, None, None, None]
     x = np.arange(width, dtype=np.float64)[None, :, None, None]
+    jobs = []
     for b in range(batch):
         s = seed + 7919 * b
-        ft, fy, fx, phi = field_params(s, tensor_id, heads, head_dim)
+        params = field_params(s, tensor_id, heads, head_dim)
         for ti, t in enumerate(range(t0, t1)):
-            arg = 2.0 * math.pi * (ft * t + fy * y + fx * x) + phi
-            frame = np.sin(arg)
-            if noise_std:
-                rng = np.random.default_rng(np.random.SeedSequence([s, tensor_id, t]))
-                frame += noise_std * rng.standard_normal(frame.shape)
-            out[b, ti] = frame
+            jobs.append((b, ti, s, params, t))
+    workers = max(1, min(len(jobs), os.cpu_count() or 1, 16))
+
+    def work(job):
+        b, ti, s, params, t = job
+        out[b, ti] = _frame(s, tensor_id, params, t, y, x, noise_std)
+
+    if workers == 1:
+        for j in jobs:
+            work(j)
+    else:
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(work, jobs))
     return out
 
 

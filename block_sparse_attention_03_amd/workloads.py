@@ -1,0 +1,74 @@
+"""The five LCSA workloads: shapes of the pages' 768x1408 to 4K streaming runs.
+
+Token geometry ([HW] "How FlashVSR works" 5.3): one token is 16x16 output
+pixels, one block 8x8 tokens of 2 latent frames, 2 latent frames are 8 output
+frames. A 768x1408 video is a 48x88 token grid; 1536x2688 is 96x168; 4K
+(2176x3840 with padding) is 136x240. The local window is 11x11 blocks
+([HW] 2.2 step 2). k is 20 % of a row's candidates, scaled by
+768*1280/(H*W) for the two large resolutions ([HW] 2.2, topk_ratio rule).
+The streaming cache keeps 6 latent frames = 3 temporal blocks ([HW] 2.3).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    heads: int
+    head_dim: int
+    dtype: str                 # "bf16" or "f32"
+    height: int                # token rows
+    width: int                 # token cols
+    frames: int                # latent frames of query chunk
+    cache_frames: int          # latent frames primed into the cache before the first step
+    cap_tb: int                # cache capacity kept after each step, in temporal blocks
+    local_range: int = 11
+    border: int = 0            # 0 Boundary-Preserved, 1 Boundary-Truncated
+    topk_fixed: int = 0
+    ratio: tuple = (1, 5)
+    scale_by_resolution: bool = False
+    out_hw: tuple = (768, 1280)
+    ratio_base: int = 0        # 0: ratio of a row's candidates, 1: of all key blocks
+    steps: int = 1
+    seed: int = 2026
+    batch: int = 1
+
+    @property
+    def n_slots(self) -> int:
+        return self.cache_frames // 2 + self.frames // 2
+
+    @property
+    def nS(self) -> int:
+        return (self.height // 8) * (self.width // 8)
+
+    @property
+    def nq(self) -> int:
+        return (self.frames // 2) * self.nS
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny LCSA 4x16x16 tokens, 2 heads, d64, fp32", 2, 64, "f32", 16, 16,
+                     frames=4, cache_frames=0, cap_tb=2, topk_fixed=3, seed=1001),
+    "cold_768x1408": Workload("cold-start chunk 768x1408 (6 latent frames x 48x88 tokens)", 12, 128,
+                              "bf16", 48, 88, frames=6, cache_frames=0, cap_tb=3, seed=1002),
+    "step_768x1408": Workload("streaming step 768x1408 (2 new latent frames x 48x88 tokens, "
+                              "6-frame KV cache)", 12, 128, "bf16", 48, 88, frames=2,
+                              cache_frames=6, cap_tb=3, steps=100, seed=1003),
+    "step_1536x2688": Workload("streaming step 1536x2688 (2 new latent frames x 96x168 tokens, "
+                               "6-frame KV cache)", 12, 128, "bf16", 96, 168, frames=2,
+                               cache_frames=6, cap_tb=3, scale_by_resolution=True,
+                               out_hw=(1536, 2688), steps=50, seed=1004),
+    "step_4k": Workload("streaming step 4K 2176x3840 padded (2 new latent frames x 136x240 "
+                        "tokens, 6-frame KV cache)", 12, 128, "bf16", 136, 240, frames=2,
+                        cache_frames=6, cap_tb=3, scale_by_resolution=True,
+                        out_hw=(2176, 3840), steps=50, seed=1005),
+}
+
+ORDER = ["tiny", "cold_768x1408", "step_768x1408", "step_1536x2688", "step_4k"]
+
+
+def attention_flops_per_pair(head_dim: int) -> int:
+    """QK^T and PV of one 128 x 128 block pair: 2 * 2 * 128 * 128 * D."""
+    return 4 * 128 * 128 * head_dim

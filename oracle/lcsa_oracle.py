@@ -285,6 +285,19 @@ class KVCache:
         return kb, vb, kp
 
 
+def prime_cache(cache: KVCache, k: np.ndarray, v: np.ndarray, first_abs_tb: int) -> None:
+    """Append the k/v blocks of earlier frames (no queries), as a stream's
+    earlier steps would have left them ([HW] 2.3)."""
+    B, T, H, W, NH, D = k.shape
+    check_grid(T, H, W)
+    nS = (H // WIN_Y) * (W // WIN_X)
+    kb, vb = partition(k), partition(v)
+    kp = pool(kb)
+    for t in range(T // WIN_T):
+        sl = slice(t * nS, (t + 1) * nS)
+        cache.append(first_abs_tb + t, kb[:, :, sl], vb[:, :, sl], kp[:, :, sl])
+
+
 @dataclass
 class StepResult:
     out: np.ndarray            # [B][T][H][W][NH][D]
@@ -297,6 +310,7 @@ class StepResult:
     q_pool: np.ndarray         # [B][NH][nq][D]
     q_blocks: np.ndarray       # [B][NH][nq][128][D]
     key_tbs: list              # absolute TB of each key TB in the view
+    key_blocks: tuple          # (kb, vb) of the view [B][NH][nk][128][D]
 
 
 def lcsa_step(q: np.ndarray, k: np.ndarray, v: np.ndarray, cache: KVCache,
@@ -360,4 +374,4 @@ def lcsa_step(q: np.ndarray, k: np.ndarray, v: np.ndarray, cache: KVCache,
         cache.evict()
     return StepResult(out=unpartition(ob, T, H, W), lse=lse, scores=scores,
                       probs=probs, allowed=allowed, sel=sel, kcount=kcount,
-                      q_pool=pq, q_blocks=qb, key_tbs=key_tbs)
+                      q_pool=pq, q_blocks=qb, key_tbs=key_tbs, key_blocks=(kb, vb))

@@ -1,0 +1,187 @@
+"""CPU tests of the C-ABI library: it loads, exports every declared symbol,
+and its host-only logic (ring metadata, k rule, argument validation) behaves
+as include/lcsa.h states. No device work is enqueued: every call here either
+is host-only or fails validation before its first HIP call."""
+from __future__ import annotations
+
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+from block_sparse_attention_03_amd import lcsa as L
+from block_sparse_attention_03_amd.workloads import WORKLOADS
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return L.load_library()
+
+
+def declared_functions():
+    text = open(L.HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lcsa_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.lcsa_abi_version() == 1
+
+
+FAKE = 0x10000  # aligned, never dereferenced: validation fails first
+
+
+def fake_cache(nby=6, nbx=11, heads=12, D=128, dtype=L.LCSA_BF16, n_slots=4):
+    c = L.KvCacheStruct()
+    L.lcsa_kv_cache_init(c, 1, heads, D, nby, nbx, dtype, n_slots,
+                         type("P", (), {"data_ptr": lambda s: FAKE})(),
+                         type("P", (), {"data_ptr": lambda s: FAKE * 2})(),
+                         type("P", (), {"data_ptr": lambda s: FAKE * 3})())
+    return c
+
+
+def test_ring_append_evict_view_wraps(lib):
+    c = fake_cache(n_slots=4)
+    assert L.lcsa_kv_cache_view(c) == ([], [])
+    assert L.lcsa_kv_cache_append(c, 3, 0) == 0
+    assert L.lcsa_kv_cache_view(c) == ([0, 1, 2], [0, 1, 2])
+    for step in range(3, 12):
+        slot = L.lcsa_kv_cache_append(c, 1, step)
+        assert slot == step % 4
+        slots, tbs = L.lcsa_kv_cache_view(c)
+        assert tbs == [step - 3, step - 2, step - 1, step]
+        assert slots == [t % 4 for t in tbs]
+        L.lcsa_kv_cache_evict(c, 3)
+        assert L.lcsa_kv_cache_view(c)[1] == [step - 2, step - 1, step]
+
+
+def test_ring_capacity_and_order_errors(lib):
+    c = fake_cache(n_slots=4)
+    L.lcsa_kv_cache_append(c, 4, 10)
+    with pytest.raises(L.LcsaError) as e:
+        L.lcsa_kv_cache_append(c, 1, 14)
+    assert e.value.status == 6
+    L.lcsa_kv_cache_evict(c, 2)
+    with pytest.raises(L.LcsaError) as e:
+        L.lcsa_kv_cache_append(c, 1, 13)          # not newer than TB 13
+    assert e.value.status == 4
+    with pytest.raises(L.LcsaError):
+        L.lcsa_kv_cache_evict(c, -1)
+    L.lcsa_kv_cache_evict(c, 0)
+    assert L.lcsa_kv_cache_view(c) == ([], [])
+    L.lcsa_kv_cache_evict(c, 5)                   # keeping more than held is a no-op
+    with pytest.raises(L.LcsaError):
+        bad = L.KvCacheStruct()
+        L.lcsa_kv_cache_init(bad, 1, 1, 128, 2, 2, L.LCSA_BF16, 17, None, None, None)
+
+
+def test_topk_count_matches_hand_table(lib):
+    g = json.load(open(os.path.join(GOLDEN, "k_table.json")))
+    for case in g["k_rows"]:
+        if "topk_fixed" in case:
+            p = L.make_params(topk_fixed=case["topk_fixed"])
+        else:
+            p = L.make_params(ratio=tuple(case["ratio"]), scale_by_resolution=case["scale"],
+                              out_hw=tuple(case.get("out", (768, 1280))))
+        for n, k in zip(case["n_allowed"], case["k"]):
+            assert L.lcsa_topk_count(p, n, 10 ** 6) == k, case["name"]
+    assert L.lcsa_topk_count(L.make_params(), 0, 10) == 0
+
+
+@pytest.mark.parametrize("wl,k", [("cold_768x1408", 39), ("step_768x1408", 52),
+                                  ("step_1536x2688", 23), ("step_4k", 11), ("tiny", 3)])
+def test_max_topk_of_workloads(lib, wl, k):
+    w = WORKLOADS[wl]
+    c = fake_cache(w.height // 8, w.width // 8, w.heads, w.head_dim,
+                   L.LCSA_BF16 if w.dtype == "bf16" else L.LCSA_F32, w.n_slots)
+    L.lcsa_kv_cache_append(c, w.n_slots, 0)
+    geom = L.make_geom(1, w.heads, w.head_dim, w.frames, w.height, w.width, c.dtype)
+    p = L.make_params(local_range=w.local_range, topk_fixed=w.topk_fixed, ratio=w.ratio,
+                      scale_by_resolution=w.scale_by_resolution, out_hw=w.out_hw)
+    first = w.cache_frames // 2
+    assert L.lcsa_max_topk(geom, first, c, p) == k
+
+
+class _P:
+    def __init__(self, addr):
+        self.addr = addr
+
+    def data_ptr(self):
+        return self.addr
+
+
+def expect(status, fn, *args, **kw):
+    with pytest.raises(L.LcsaError) as e:
+        fn(*args, **kw)
+    assert e.value.status == status, str(e.value)
+    return str(e.value)
+
+
+def test_validation_rejects_bad_input_before_any_device_call(lib):
+    c = fake_cache()
+    L.lcsa_kv_cache_append(c, 1, 0)
+    ok = _P(FAKE)
+    geom = L.make_geom(1, 12, 128, 2, 48, 88, L.LCSA_BF16)
+    s = 0  # stream handle, never used
+    # shapes
+    expect(2, L.lcsa_partition_pool, L.make_geom(1, 12, 128, 3, 48, 88, 0), ok, ok, ok, ok, ok, c, 0, s)
+    expect(2, L.lcsa_partition_pool, L.make_geom(1, 12, 128, 2, 44, 88, 0), ok, ok, ok, ok, ok, c, 0, s)
+    expect(2, L.lcsa_partition_pool, L.make_geom(1, 12, 96, 2, 48, 88, 0), ok, ok, ok, ok, ok, c, 0, s)
+    expect(2, L.lcsa_partition_pool, L.make_geom(1, 12, 128, 2, 48, 96, 0), ok, ok, ok, ok, ok, c, 0, s)
+    expect(3, L.lcsa_partition_pool, L.make_geom(1, 12, 128, 2, 48, 88, 1), ok, ok, ok, ok, ok, c, 0, s)
+    expect(3, L.lcsa_partition_pool, L.make_geom(1, 12, 128, 2, 48, 88, 7), ok, ok, ok, ok, ok, c, 0, s)
+    # pointers
+    expect(1, L.lcsa_partition_pool, geom, ok, None, ok, ok, ok, c, 0, s)
+    expect(1, L.lcsa_partition_pool, geom, ok, ok, ok, None, ok, c, 0, s)
+    expect(5, L.lcsa_partition_pool, geom, _P(FAKE + 8), ok, ok, ok, ok, c, 0, s)
+    # slot not held
+    expect(6, L.lcsa_partition_pool, geom, ok, ok, ok, ok, ok, c, 2, s)
+    expect(4, L.lcsa_partition_pool, geom, ok, ok, ok, ok, ok, c, 9, s)
+    # selection parameters
+    expect(4, L.lcsa_draft_mask, geom, ok, 0, c, L.make_params(local_range=10), 64, ok, ok, None, s)
+    expect(4, L.lcsa_draft_mask, geom, ok, 0, c, L.make_params(local_range=0), 64, ok, ok, None, s)
+    expect(4, L.lcsa_draft_mask, geom, ok, 0, c, L.make_params(ratio=(0, 5)), 64, ok, ok, None, s)
+    expect(4, L.lcsa_draft_mask, geom, ok, 0, c, L.make_params(ratio=(1, -5)), 64, ok, ok, None, s)
+    expect(4, L.lcsa_draft_mask, geom, ok, 0, c, L.make_params(border=2), 64, ok, ok, None, s)
+    expect(4, L.lcsa_draft_mask, geom, ok, 0, c,
+           L.make_params(scale_by_resolution=True, out_hw=(0, 1280)), 64, ok, ok, None, s)
+    # kmax too small (k = 13 for one visible TB of 66 candidates)
+    msg = expect(6, L.lcsa_draft_mask, geom, ok, 0, c, L.make_params(), 12, ok, ok, None, s)
+    assert "13" in msg
+    expect(5, L.lcsa_draft_mask, geom, ok, 0, c, L.make_params(), 64, ok, ok, _P(FAKE + 4), s)
+    # geometry disagrees with the cache
+    expect(2, L.lcsa_draft_mask, L.make_geom(1, 8, 128, 2, 48, 88, 0), ok, 0, c, L.make_params(), 64,
+           ok, ok, None, s)
+    # attention
+    expect(4, L.lcsa_block_sparse_attn, geom, ok, c, ok, ok, 13, ok, None, float("nan"), s)
+    expect(4, L.lcsa_block_sparse_attn, geom, ok, c, ok, ok, 13, ok, None, -1.0, s)
+    expect(6, L.lcsa_block_sparse_attn, geom, ok, c, ok, ok, 0, ok, None, 0.0, s)
+    expect(1, L.lcsa_block_sparse_attn, geom, ok, c, None, ok, 13, ok, None, 0.0, s)
+
+
+def test_empty_chunk_is_a_no_op(lib):
+    c = fake_cache()
+    L.lcsa_kv_cache_append(c, 1, 0)
+    ok = _P(FAKE)
+    geom = L.make_geom(1, 12, 128, 0, 48, 88, L.LCSA_BF16)
+    L.lcsa_partition_pool(geom, ok, ok, ok, ok, ok, c, 0, 0)
+    L.lcsa_draft_mask(geom, ok, 0, c, L.make_params(), 1, ok, ok, None, 0)
+    L.lcsa_block_sparse_attn(geom, ok, c, ok, ok, 1, ok, None, 0.0, 0)
+    assert L.lcsa_last_error() == ""
+
+
+def test_too_many_candidates_is_refused(lib):
+    # 16 TBs of a 17x30 grid with an unbounded window: 8160 candidates > 4096
+    c = fake_cache(17, 30, 1, 128, L.LCSA_BF16, 16)
+    L.lcsa_kv_cache_append(c, 16, 0)
+    geom = L.make_geom(1, 1, 128, 2, 136, 240, L.LCSA_BF16)
+    expect(6, L.lcsa_draft_mask, geom, _P(FAKE), 15, c, L.make_params(local_range=99, topk_fixed=1),
+           4096, _P(FAKE), _P(FAKE), None, 0)
