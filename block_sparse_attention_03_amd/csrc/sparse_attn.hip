@@ -43,89 +43,102 @@ __device__ inline size_t out_offset(const AttnArgs& a, int b, int h, int i, int 
   return ((((size_t)b * a.T + t) * a.H + y) * a.W + x) * a.NH * a.D + (size_t)h * a.D + d;
 }
 
-// XOR swizzle of 16-byte chunk c in LDS row `row` (rows of D*2 bytes).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+// XOR swizzles of 16-byte chunk c in an LDS row: rows of 256 bytes (16
+// chunks) and rows of 128 bytes (8 chunks). Both are involutions, so the
+// same function maps logical -> physical and back. Sixteen consecutive
+// rows read at the same logical chunk hit sixteen different bank groups.
+__device__ inline int swz16(int row, int c) { return c ^ (row & 15); }
+__device__ inline int swz8(int row, int c) { return c ^ ((row >> 1) & 7); }
+
 template <int D>
 __device__ inline int swz_k(int row, int c) {
-  if constexpr (D == 128) return c ^ (row & 15);
-  else return c ^ ((row >> 1) & 7);
+  if constexpr (D == 128) return swz16(row, c);
+  else return swz8(row, c);
 }
 
-__device__ inline int swz_v(int row, int c) { return c ^ (row & 15); }
-
-// Fetch key block j's K tile and V^T tile (global -> registers).
-template <int D>
-__device__ __forceinline__ void fetch_kv(const AttnArgs& a, size_t bh_slots, int nS, int j, int tid,
-                                         u32x4 (&kreg)[128 * D * 2 / 16 / 256],
-                                         u32x4 (&vreg)[D * 128 * 2 / 32 / 256][2]) {
-  constexpr int KB = 128 * D * 2, VB = D * 128 * 2;
-  constexpr int KIT = KB / 16 / 256, VIT = VB / 32 / 256;
-  const int p = j / nS, s = j - p * nS;
-  const size_t blk = (bh_slots + a.view.slot[p]) * nS + s;
-  const u32x4* kp = reinterpret_cast<const u32x4*>((const char*)a.k_ring + blk * KB);
-  const u32x4* vp = reinterpret_cast<const u32x4*>((const char*)a.v_ring + blk * VB);
-#pragma unroll
-  for (int it = 0; it < KIT; ++it) kreg[it] = kp[it * 256 + tid];
-#pragma unroll
-  for (int it = 0; it < VIT; ++it) {
-    const int e = it * 256 + tid;
-    vreg[it][0] = vp[2 * e];
-    vreg[it][1] = vp[2 * e + 1];
-  }
-}
-
-// Registers -> one LDS buffer (K tile swizzled, V^T tile swizzled with its
-// keys permuted inside each 16-key group).
-template <int D>
-__device__ __forceinline__ void stash_kv(char* buf, int tid,
-                                         const u32x4 (&kreg)[128 * D * 2 / 16 / 256],
-                                         const u32x4 (&vreg)[D * 128 * 2 / 32 / 256][2]) {
-  constexpr int KB = 128 * D * 2, VB = D * 128 * 2;
-  constexpr int KIT = KB / 16 / 256, VIT = VB / 32 / 256, KCH = D / 8;
-#pragma unroll
-  for (int it = 0; it < KIT; ++it) {
-    const int e = it * 256 + tid, row = e / KCH, c = e % KCH;
-    *reinterpret_cast<u32x4*>(buf + row * (D * 2) + swz_k<D>(row, c) * 16) = kreg[it];
-  }
-  char* vb = buf + KB;
-#pragma unroll
-  for (int it = 0; it < VIT; ++it) {
-    const int e = it * 256 + tid, d = e >> 3, pp = e & 7;
-    const u32x4 A = vreg[it][0], B = vreg[it][1];  // keys 16pp+0..7, 16pp+8..15
-    // chunk 2pp <- keys 0-3, 8-11 (read by g = 0); chunk 2pp+1 <- keys 4-7, 12-15 (g = 1)
-    *reinterpret_cast<u32x4*>(vb + d * 256 + swz_v(d, 2 * pp) * 16) = u32x4{A.x, A.y, B.x, B.y};
-    *reinterpret_cast<u32x4*>(vb + d * 256 + swz_v(d, 2 * pp + 1) * 16) =
-        u32x4{A.z, A.w, B.z, B.w};
-  }
+// Key order inside a 32-key S^T tile. Lane (q, g) of an MFMA 32x32 output
+// holds rows 8i + 4g + j (i, j = 0..3); loading K row perm(r) into A row r
+// makes those rows the keys 16*(i/2) + 8g + 4*(i%2) + j, i.e. for the PV
+// k-step ks the lane holds exactly the 8 contiguous keys 16ks + 8g + e that
+// a plain V^T row chunk supplies as the A operand.
+__device__ inline int perm_key(int r) {
+  const int i = r >> 3, gg = (r >> 2) & 1, j = r & 3;
+  return 16 * (i >> 1) + 8 * gg + 4 * (i & 1) + j;
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
-  constexpr int KB = 128 * D * 2;        // K tile bytes
-  constexpr int VB = D * 128 * 2;        // V^T tile bytes
-  constexpr int BUF = KB + VB;
-  constexpr int KIT = KB / 16 / 256;     // K chunks per thread
-  constexpr int VIT = VB / 32 / 256;     // V chunk pairs per thread
-  constexpr int NS = D / 16;             // k-steps of S^T
-  constexpr int NO = D / 32;             // O^T tiles
-  __shared__ __attribute__((aligned(16))) char lds[2 * BUF];
+struct Tile {
+  static constexpr int KEYS = 64;                  // keys per sub-tile
+  static constexpr int KBYTES = KEYS * D * 2;      // K sub-tile  [64][D]
+  static constexpr int VBYTES = D * KEYS * 2;      // V^T sub-tile [D][64]
+  static constexpr int BUF = KBYTES + VBYTES;
+  static constexpr int KCH = D / 8;                // 16-byte chunks per K row
+  static constexpr int KLD = KBYTES / 1024 / 4;    // direct 1 KB loads per wave (K)
+  static constexpr int VLD = VBYTES / 1024 / 4;    // direct 1 KB loads per wave (V^T)
+  static constexpr int NS = D / 16;                // k-steps of S^T
+  static constexpr int NO = D / 32;                // O^T tiles
+};
+
+// Issue the direct global -> LDS loads of half `hf` (keys 64hf..64hf+63) of
+// a key block into one buffer. Each wave instruction fills 1 KB of LDS, lane
+// l landing at +16l; the lane fetches whichever global chunk belongs there
+// under the swizzle.
+template <int D>
+__device__ __forceinline__ void load_subtile(const char* kblk, const char* vblk, int hf, char* buf,
+                                             int w, int lane) {
+  using T = Tile<D>;
+#pragma unroll
+  for (int it = 0; it < T::KLD; ++it) {
+    const int unit = (it * 4 + w) * 64 + lane;
+    const int row = unit / T::KCH, c = swz_k<D>(row, unit % T::KCH);
+    const char* src = kblk + ((size_t)(64 * hf + row) * D + c * 8) * 2;
+    __builtin_amdgcn_global_load_lds(src, LDS_PTR(buf + (it * 4 + w) * 1024), 16, 0, 0);
+  }
+  char* vb = buf + T::KBYTES;
+#pragma unroll
+  for (int it = 0; it < T::VLD; ++it) {
+    const int unit = (it * 4 + w) * 64 + lane;
+    const int d = unit >> 3, c = swz8(d, unit & 7);
+    const char* src = vblk + ((size_t)d * 128 + 64 * hf + c * 8) * 2;
+    __builtin_amdgcn_global_load_lds(src, LDS_PTR(vb + (it * 4 + w) * 1024), 16, 0, 0);
+  }
+}
+
+__device__ inline void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
+  using T = Tile<D>;
+  constexpr int NS = T::NS, NO = T::NO;
+  constexpr float kLazy = 8.f;  // rescale O only when the row max grows by > 2^8
+  __shared__ __attribute__((aligned(16))) char lds[2 * T::BUF];
 
   const int nS = (a.H / 8) * (a.W / 8);
   const int nq = (a.T / 2) * nS;
-  const int task = blockIdx.x;
+  const int n_tasks = a.B * a.NH * nq;
+  // XCD-aware order: consecutive workgroups go to the 8 XCDs in turn, so XCD
+  // x gets the contiguous task range [x*per, (x+1)*per): neighbouring query
+  // blocks of one head (which select overlapping keys) share an L2.
+  const int per = (n_tasks + 7) / 8;
+  const int task = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (task >= n_tasks) return;
   const int i = task % nq;
   const int bh = task / nq;
   const int h = bh % a.NH, b = bh / a.NH;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
   const int cnt = min(a.sel_cnt[task], a.kmax);
   const int32_t* list = a.sel_idx + (size_t)task * a.kmax;
-  const int tau = 32 * wave + l32;  // this lane's query row in the block
-  const int n_keys = a.view.n * nS;  // ids outside [0, n_keys) are skipped, never loaded
+  const int tau = 32 * w + l32;          // this lane's query row in the block
+  const int n_keys = a.view.n * nS;      // ids outside [0, n_keys) are skipped, never loaded
+  uint16_t* out = (uint16_t*)a.out;
 
   if (cnt <= 0) {
     for (int e = tid; e < 128 * D / 8; e += 256) {
       const int row = e / (D / 8), c = e % (D / 8);
-      *reinterpret_cast<uint4*>((uint16_t*)a.out + out_offset(a, b, h, i, row, c * 8)) =
-          make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(out + out_offset(a, b, h, i, row, c * 8)) = make_uint4(0, 0, 0, 0);
     }
     if (a.lse && tid < 128) a.lse[(size_t)task * 128 + tid] = -INFINITY;
     return;
@@ -138,7 +151,14 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
     qf[s] = *reinterpret_cast<const bf16x8*>(qb + tau * D + 16 * s + 8 * g);
 
   const size_t bh_slots = (size_t)bh * a.n_slots;
-  u32x4 kreg[KIT], vreg[VIT][2];
+  auto block_base = [&](int j, const char*& kp, const char*& vp) {
+    j = (unsigned)j < (unsigned)n_keys ? j : 0;
+    const int p = j / nS, s = j - p * nS;
+    const size_t blk = (bh_slots + a.view.slot[p]) * nS + s;
+    kp = (const char*)a.k_ring + blk * (128 * D * 2);
+    vp = (const char*)a.v_ring + blk * (D * 128 * 2);
+  };
+
   f32x16 o[NO];
 #pragma unroll
   for (int t = 0; t < NO; ++t)
@@ -146,99 +166,111 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
     for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
   const float sl2 = a.scale * kLog2e;
   float m = -INFINITY, lsum = 0.f;
+  const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+  const int prow0 = perm_key(l32), prow1 = 32 + perm_key(l32);
 
-  int jnext = list[0];
-  fetch_kv<D>(a, bh_slots, nS, (unsigned)jnext < (unsigned)n_keys ? jnext : 0, tid, kreg, vreg);
-  stash_kv<D>(lds, tid, kreg, vreg);
-  __syncthreads();
-  for (int it = 0; it < cnt; ++it) {
-    const char* kb = lds + (it & 1) * BUF;
-    const char* vb = kb + KB;
-    const bool cur_ok = (unsigned)jnext < (unsigned)n_keys;
-    const bool more = it + 1 < cnt;
-    if (more) {
-      jnext = list[it + 1];
-      fetch_kv<D>(a, bh_slots, nS, (unsigned)jnext < (unsigned)n_keys ? jnext : 0, tid, kreg, vreg);
+  const char *kp, *vp;
+  block_base(list[0], kp, vp);
+  load_subtile<D>(kp, vp, 0, lds, w, lane);
+  const int total = 2 * cnt;
+  for (int t = 0; t < total; ++t) {
+    wait_vm_all();
+    __syncthreads();
+    if (t + 1 < total) {
+      block_base(list[(t + 1) >> 1], kp, vp);
+      load_subtile<D>(kp, vp, (t + 1) & 1, lds + ((t + 1) & 1) * T::BUF, w, lane);
     }
-    if (!cur_ok) {
-      if (more) stash_kv<D>(lds + ((it + 1) & 1) * BUF, tid, kreg, vreg);
-      __syncthreads();
-      continue;
+    if ((unsigned)list[t >> 1] >= (unsigned)n_keys) continue;  // uniform: skipped id
+    const char* kb = lds + (t & 1) * T::BUF;
+    const char* vb = kb + T::KBYTES;
+
+    // S^T (64 keys x 32 queries) = K Q^T
+    bf16x8 kf[2][NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      kf[0][s] = *reinterpret_cast<const bf16x8*>(kb + prow0 * (D * 2) + swz_k<D>(prow0, 2 * s + g) * 16);
+      kf[1][s] = *reinterpret_cast<const bf16x8*>(kb + prow1 * (D * 2) + swz_k<D>(prow1, 2 * s + g) * 16);
+    }
+    f32x16 sacc[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sacc[0][r] = sacc[1][r] = 0.f;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0][s], qf[s], sacc[0], 0, 0, 0);
+      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[1][s], qf[s], sacc[1], 0, 0, 0);
+    }
+    // V^T fragments for this sub-tile: plain key order, 8 contiguous keys
+    bf16x8 vf[NO][4];
+#pragma unroll
+    for (int dt = 0; dt < NO; ++dt) {
+      const int d = 32 * dt + l32;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        vf[dt][ks] = *reinterpret_cast<const bf16x8*>(vb + d * 128 + swz8(d, 2 * ks + g) * 16);
     }
 
-    f32x16 sacc[4];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kt][r] = 0.f;
-      const int row = 32 * kt + l32;
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const bf16x8 af =
-            *reinterpret_cast<const bf16x8*>(kb + row * (D * 2) + swz_k<D>(row, 2 * s + g) * 16);
-        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[s], sacc[kt], 0, 0, 0);
-      }
-    }
-
+    // online softmax (base 2), lazy rescale of O
     float mx = sacc[0][0];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(sacc[0][r], sacc[1][r]));
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+    if (__ballot(mx > m + kLazy)) {
+      const float mnew = fmaxf(m, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+      lsum *= alpha;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = fmaxf(m, mx * sl2);
-    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-    float rs = 0.f;
+      for (int dt = 0; dt < NO; ++dt)
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kt][r], sl2, -mnew));
-        sacc[kt][r] = pv;
-        rs += pv;
-      }
-    lsum = lsum * alpha + rs;
-    m = mnew;
-#pragma unroll
-    for (int t = 0; t < NO; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
-
-    bf16x8 pf[4][2];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pf[kt][hh][e] = (__bf16)sacc[kt][8 * hh + e];
-
-#pragma unroll
-    for (int t = 0; t < NO; ++t) {
-      const int d = 32 * t + l32;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 af = *reinterpret_cast<const bf16x8*>(vb + d * 256 + swz_v(d, 2 * ks + g) * 16);
-        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, pf[ks >> 1][ks & 1], o[t], 0, 0, 0);
-      }
+        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+      m = mnew;
     }
-    if (more) stash_kv<D>(lds + ((it + 1) & 1) * BUF, tid, kreg, vreg);
-    __syncthreads();
+    bf16x8 pf[2][2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          pf[kt][hh][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[kt][8 * hh + e], sl2, -m));
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const bf16x2 pr = {pf[kt][hh][e], pf[kt][hh][e + 1]};
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum, false);
+        }
+      }
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int dt = 0; dt < NO; ++dt)
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[dt][ks], pf[ks >> 1][ks & 1], o[dt], 0, 0, 0);
   }
 
+  // epilogue: normalise, stage the 128 x D tile in LDS, write whole rows
   const float lt = lsum + __shfl_xor(lsum, 32);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;  // 0 only if every listed id was skipped
-  uint16_t* out = (uint16_t*)a.out;
+  __syncthreads();
+  char* st = lds;
 #pragma unroll
-  for (int t = 0; t < NO; ++t)
+  for (int dt = 0; dt < NO; ++dt)
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
-      const int d = 32 * t + 8 * ii + 4 * g;
       __bf16 v4[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v4[j] = (__bf16)(o[t][4 * ii + j] * inv);
-      *reinterpret_cast<uint2*>(out + out_offset(a, b, h, i, tau, d)) =
+      for (int j = 0; j < 4; ++j) v4[j] = (__bf16)(o[dt][4 * ii + j] * inv);
+      const int c = 4 * dt + ii;  // 16-byte chunk of d = 32dt + 8ii .. +8
+      *reinterpret_cast<uint2*>(st + tau * (D * 2) + swz_k<D>(tau, c) * 16 + 8 * g) =
           *reinterpret_cast<const uint2*>(v4);
     }
+  __syncthreads();
+  constexpr int CH = D / 8;
+#pragma unroll
+  for (int e0 = 0; e0 < 128 * CH; e0 += 256) {
+    const int e = e0 + tid, row = e / CH, c = e % CH;
+    *reinterpret_cast<uint4*>(out + out_offset(a, b, h, i, row, c * 8)) =
+        *reinterpret_cast<const uint4*>(st + row * (D * 2) + swz_k<D>(row, c) * 16);
+  }
   if (a.lse && g == 0)
     a.lse[(size_t)task * 128 + tau] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
 }
@@ -318,7 +350,8 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(AttnArgs a) {
 template <int D>
 hipError_t launch_bf16(const AttnArgs& a, hipStream_t s) {
   const long long tasks = (long long)a.B * a.NH * (a.T / 2) * (a.H / 8) * (a.W / 8);
-  hipLaunchKernelGGL(attn_bf16_kernel<D>, dim3((unsigned)tasks), dim3(256), 0, s, a);
+  const long long per = (tasks + 7) / 8;
+  hipLaunchKernelGGL(attn_bf16_kernel<D>, dim3((unsigned)(8 * per)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
