@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--workload", default="step_768x1408")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-heads", type=int, default=12)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB before the warmup, as "
+                         "the calibration kernel for rocprofv3 FETCH_SIZE/WRITE_SIZE")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM bytes per attention launch measured by rocprofv3 counters")
     return ap.parse_args()
@@ -66,6 +69,13 @@ def main():
     L.load_library()
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     code = L.LCSA_BF16 if w.dtype == "bf16" else L.LCSA_F32
+
+    if args.copy_probe_mib:
+        src = torch.ones(args.copy_probe_mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ---- inputs resident in HBM: cache frames + one fresh chunk per step
     n_steps = K + W

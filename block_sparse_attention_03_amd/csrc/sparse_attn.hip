@@ -22,6 +22,8 @@
 // whole A fragment in the order the S^T accumulator layout produces P.
 // fp32 path (small validation workloads): one thread per query row on the
 // vector ALU.
+#include <type_traits>
+
 #include "lcsa_kernels.h"
 
 namespace lcsa {
@@ -109,6 +111,17 @@ __device__ __forceinline__ void load_subtile(const char* kblk, const char* vblk,
 
 __device__ inline void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
+__device__ inline float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+
+// Value held by lane l ^ 32 (the other half of this query's keys), through
+// v_permlane32_swap: a VALU lane exchange, no LDS round trip.
+__device__ inline float partner32(float x, int g) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(g ? r[0] : r[1]);
+}
+
+__device__ inline bf16x2 ones2() { return bf16x2{(__bf16)1.f, (__bf16)1.f}; }
+
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   using T = Tile<D>;
@@ -151,9 +164,12 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     qf[s] = *reinterpret_cast<const bf16x8*>(qb + tau * D + 16 * s + 8 * g);
 
   const size_t bh_slots = (size_t)bh * a.n_slots;
+  const float inv_ns = 1.f / (float)nS;
   auto block_base = [&](int j, const char*& kp, const char*& vp) {
     j = (unsigned)j < (unsigned)n_keys ? j : 0;
-    const int p = j / nS, s = j - p * nS;
+    // p = j / nS exactly: (j + 0.5) / nS lies strictly inside (p, p + 1)
+    const int p = (int)(((float)j + 0.5f) * inv_ns);
+    const int s = j - p * nS;
     const size_t blk = (bh_slots + a.view.slot[p]) * nS + s;
     kp = (const char*)a.k_ring + blk * (128 * D * 2);
     vp = (const char*)a.v_ring + blk * (D * 128 * 2);
@@ -166,55 +182,55 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
   const float sl2 = a.scale * kLog2e;
   float m = -INFINITY, lsum = 0.f;
-  const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
-  const int prow0 = perm_key(l32), prow1 = 32 + perm_key(l32);
 
-  const char *kp, *vp;
-  block_base(list[0], kp, vp);
-  load_subtile<D>(kp, vp, 0, lds, w, lane);
-  const int total = 2 * cnt;
-  for (int t = 0; t < total; ++t) {
-    wait_vm_all();
-    __syncthreads();
-    if (t + 1 < total) {
-      block_base(list[(t + 1) >> 1], kp, vp);
-      load_subtile<D>(kp, vp, (t + 1) & 1, lds + ((t + 1) & 1) * T::BUF, w, lane);
-    }
-    if ((unsigned)list[t >> 1] >= (unsigned)n_keys) continue;  // uniform: skipped id
-    const char* kb = lds + (t & 1) * T::BUF;
+  // Lane-invariant LDS fragment offsets. K rows prow and prow + 32 share
+  // the swizzle (it depends on row & 15), V^T rows 32dt + l32 share it for
+  // every dt, so tile and buffer selection are immediate offsets.
+  const int prow = perm_key(l32);
+  int koff[NS], voff[4];
+#pragma unroll
+  for (int s2 = 0; s2 < NS; ++s2) koff[s2] = prow * (D * 2) + swz_k<D>(prow, 2 * s2 + g) * 16;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) voff[ks] = l32 * 128 + swz8(l32, 2 * ks + g) * 16;
+
+  // one 64-key half of a key block held in LDS buffer HB
+  auto compute_half = [&](auto hb_tag) {
+    constexpr int HB = decltype(hb_tag)::value;
+    const char* kb = lds + HB * T::BUF;
     const char* vb = kb + T::KBYTES;
-
-    // S^T (64 keys x 32 queries) = K Q^T
     bf16x8 kf[2][NS];
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      kf[0][s] = *reinterpret_cast<const bf16x8*>(kb + prow0 * (D * 2) + swz_k<D>(prow0, 2 * s + g) * 16);
-      kf[1][s] = *reinterpret_cast<const bf16x8*>(kb + prow1 * (D * 2) + swz_k<D>(prow1, 2 * s + g) * 16);
+    for (int s2 = 0; s2 < NS; ++s2) {
+      kf[0][s2] = *reinterpret_cast<const bf16x8*>(kb + koff[s2]);
+      kf[1][s2] = *reinterpret_cast<const bf16x8*>(kb + koff[s2] + 32 * D * 2);
     }
     f32x16 sacc[2];
 #pragma unroll
     for (int r = 0; r < 16; ++r) sacc[0][r] = sacc[1][r] = 0.f;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0][s], qf[s], sacc[0], 0, 0, 0);
-      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[1][s], qf[s], sacc[1], 0, 0, 0);
+    for (int s2 = 0; s2 < NS; ++s2) {
+      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0][s2], qf[s2], sacc[0], 0, 0, 0);
+      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[1][s2], qf[s2], sacc[1], 0, 0, 0);
     }
-    // V^T fragments for this sub-tile: plain key order, 8 contiguous keys
     bf16x8 vf[NO][4];
 #pragma unroll
-    for (int dt = 0; dt < NO; ++dt) {
-      const int d = 32 * dt + l32;
+    for (int dt = 0; dt < NO; ++dt)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        vf[dt][ks] = *reinterpret_cast<const bf16x8*>(vb + d * 128 + swz8(d, 2 * ks + g) * 16);
-    }
+        vf[dt][ks] = *reinterpret_cast<const bf16x8*>(vb + voff[ks] + dt * 32 * 128);
 
-    // online softmax (base 2), lazy rescale of O
-    float mx = sacc[0][0];
+    // row max of the 64 logits (two lanes hold one query's halves)
+    float t3[11];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(sacc[0][r], sacc[1][r]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
-    if (__ballot(mx > m + kLazy)) {
+    for (int q3 = 0; q3 < 5; ++q3) {
+      t3[q3] = max3(sacc[0][3 * q3], sacc[0][3 * q3 + 1], sacc[0][3 * q3 + 2]);
+      t3[5 + q3] = max3(sacc[1][3 * q3], sacc[1][3 * q3 + 1], sacc[1][3 * q3 + 2]);
+    }
+    t3[10] = fmaxf(sacc[0][15], sacc[1][15]);
+    float mx = max3(max3(max3(t3[0], t3[1], t3[2]), max3(t3[3], t3[4], t3[5]),
+                         max3(t3[6], t3[7], t3[8])), t3[9], t3[10]);
+    mx = fmaxf(mx, partner32(mx, g)) * sl2;
+    if (__ballot(mx > m + kLazy)) {  // lazy rescale: only when the max grows by > 2^8
       const float mnew = fmaxf(m, mx);
       const float alpha = __builtin_amdgcn_exp2f(m - mnew);
       lsum *= alpha;
@@ -235,20 +251,38 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
           const bf16x2 pr = {pf[kt][hh][e], pf[kt][hh][e + 1]};
-          lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum, false);
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones2(), lsum, false);
         }
       }
-
-    // O^T += V^T P^T
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int dt = 0; dt < NO; ++dt)
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[dt][ks], pf[ks >> 1][ks & 1], o[dt], 0, 0, 0);
+  };
+
+  const char *kp, *vp;
+  block_base(list[0], kp, vp);
+  load_subtile<D>(kp, vp, 0, lds, w, lane);
+  for (int it = 0; it < cnt; ++it) {
+    const bool ok = (unsigned)list[it] < (unsigned)n_keys;  // uniform: skipped id
+    // half 0 of block it is in buffer 0; fetch half 1 into buffer 1
+    wait_vm_all();
+    __syncthreads();
+    load_subtile<D>(kp, vp, 1, lds + T::BUF, w, lane);
+    if (ok) compute_half(std::integral_constant<int, 0>{});
+    // half 1 is in buffer 1; fetch half 0 of the next block into buffer 0
+    wait_vm_all();
+    __syncthreads();
+    if (it + 1 < cnt) {
+      block_base(list[it + 1], kp, vp);
+      load_subtile<D>(kp, vp, 0, lds, w, lane);
+    }
+    if (ok) compute_half(std::integral_constant<int, 1>{});
   }
 
   // epilogue: normalise, stage the 128 x D tile in LDS, write whole rows
-  const float lt = lsum + __shfl_xor(lsum, 32);
+  const float lt = lsum + partner32(lsum, g);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;  // 0 only if every listed id was skipped
   __syncthreads();
   char* st = lds;
