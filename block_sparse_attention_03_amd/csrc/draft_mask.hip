@@ -9,14 +9,17 @@
 // the current and past temporal blocks; Key design 3: two border rules.
 //
 // No dense mask exists: candidates are enumerated from block coordinates.
-// A workgroup serves `gx` query rows that share (batch, head, temporal
-// block, block row) and have consecutive block columns; their candidate
-// windows overlap, so each pooled key row is fetched once and scored
-// against all the group's rows (phase A, scores land in LDS). Then one wave
-// per row takes the softmax and selects exactly k candidates with a radix
-// select over order-preserving 64-bit keys of the float64 scores, ties to the
-// lower logical id (phase B). Scores are float64 so that the selection is
-// decided on values that equal the exact ones up to summation order.
+// Two scoring layouts share one selection routine:
+//  * tile path (up to 768 candidates per row, e.g. the 11x11 window): a
+//    workgroup scores a 4x4 tile of query blocks against the union of their
+//    windows on the fp64 matrix cores;
+//  * row-group path (larger windows): a workgroup scores `gx` query rows of
+//    one block row with the vector ALU, each pooled key fetched once.
+// Scores land in LDS at each row's candidate index; then one wave per row
+// takes the softmax and selects exactly k candidates (value-range bucket
+// select, ties to the lower logical id). Scores are float64 so the
+// selection is decided on values equal to the exact ones up to summation
+// order.
 #include "lcsa_kernels.h"
 #include "lcsa_window.h"
 
@@ -26,10 +29,14 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 
-__device__ inline uint64_t order_key(double v) {
-  v = v + 0.0;  // -0 and +0 compare equal
-  const uint64_t u = (uint64_t)__double_as_longlong(v);
-  return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+// XCD-contiguous task order: workgroups are dealt to the 8 XCDs in turn, so
+// XCD x takes tasks [x*per, (x+1)*per) and neighbouring query tiles, whose
+// windows share pooled keys, hit the same L2. Launch 8*per workgroups;
+// returns -1 for the padding ones.
+__device__ inline int xcd_task(int n_tasks) {
+  const int per = (n_tasks + 7) / 8;
+  const int t = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+  return t < n_tasks ? t : -1;
 }
 
 __device__ inline void wave_sync() {
@@ -38,43 +45,9 @@ __device__ inline void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__device__ inline double wave_max_f64(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o));
-  return v;
-}
-
 __device__ inline double wave_sum_f64(double v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-
-__device__ inline uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const uint64_t w = __shfl_xor(v, o);
-    v = w > v ? w : v;
-  }
-  return v;
-}
-
-__device__ inline uint64_t wave_min_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const uint64_t w = __shfl_xor(v, o);
-    v = w < v ? w : v;
-  }
-  return v;
-}
-
-// Sum over lanes >= this lane.
-__device__ inline uint32_t wave_suffix_sum(uint32_t v, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t w = __shfl_down(v, o);
-    if (lane + o < 64) v += w;
-  }
   return v;
 }
 
@@ -82,10 +55,190 @@ __device__ inline int32_t topk_dev(const DraftArgs& a, int64_t n_allowed, int64_
   if (n_allowed <= 0) return 0;
   if (a.topk_fixed > 0) return (int32_t)(a.topk_fixed < n_allowed ? a.topk_fixed : n_allowed);
   const int64_t base = a.ratio_base == 0 ? n_allowed : n_keys;
-  const unsigned __int128 kk =
-      ((unsigned __int128)(uint64_t)base * (uint64_t)a.ratio_num) / (uint64_t)a.ratio_den;
-  int64_t k = kk > (unsigned __int128)n_allowed ? n_allowed : (int64_t)kk;
+  // the host reduced num/den and checked num < 2^32, so base * num < 2^56
+  const uint64_t kk = ((uint64_t)base * (uint64_t)a.ratio_num) / (uint64_t)a.ratio_den;
+  const int64_t k = kk > (uint64_t)n_allowed ? n_allowed : (int64_t)kk;
   return (int32_t)(k < 1 ? 1 : k);
+}
+
+// ---- DPP wave primitives (gfx9 row operations: no LDS round trip) --------
+template <int CTRL, int ROWS>
+__device__ inline double dpp_keep(double v) {  // lanes outside ROWS keep their value
+  const int lo = __double2loint(v), hi = __double2hiint(v);
+  return __hiloint2double(__builtin_amdgcn_update_dpp(hi, hi, CTRL, ROWS, 0xF, false),
+                          __builtin_amdgcn_update_dpp(lo, lo, CTRL, ROWS, 0xF, false));
+}
+
+__device__ inline double lane63_f64(double v) {
+  return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), 63),
+                          __builtin_amdgcn_readlane(__double2loint(v), 63));
+}
+
+// quad_perm [1,0,3,2], [2,3,0,1], row_half_mirror, row_mirror, row_bcast:15,
+// row_bcast:31: the full-wave result ends in lane 63.
+__device__ inline double wave_max_dpp(double v) {
+  v = fmax(v, dpp_keep<0xB1, 0xF>(v));
+  v = fmax(v, dpp_keep<0x4E, 0xF>(v));
+  v = fmax(v, dpp_keep<0x141, 0xF>(v));
+  v = fmax(v, dpp_keep<0x140, 0xF>(v));
+  v = fmax(v, dpp_keep<0x142, 0xA>(v));
+  v = fmax(v, dpp_keep<0x143, 0xC>(v));
+  return lane63_f64(v);
+}
+
+__device__ inline double wave_min_dpp(double v) {
+  v = fmin(v, dpp_keep<0xB1, 0xF>(v));
+  v = fmin(v, dpp_keep<0x4E, 0xF>(v));
+  v = fmin(v, dpp_keep<0x141, 0xF>(v));
+  v = fmin(v, dpp_keep<0x140, 0xF>(v));
+  v = fmin(v, dpp_keep<0x142, 0xA>(v));
+  v = fmin(v, dpp_keep<0x143, 0xC>(v));
+  return lane63_f64(v);
+}
+
+// Inclusive prefix sum over lanes 0..63 (row_shr 1,2,4,8 with zero fill,
+// then row_bcast:15 / :31 to carry across rows).
+__device__ inline uint32_t wave_prefix_sum_dpp(uint32_t x) {
+  int v = (int)x;
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);
+  return (uint32_t)v;
+}
+
+// One wave: softmax (optional probs), exact top-k and the sorted index list
+// of query row `row`, whose candidates are scores s[0 .. n) enumerated as
+// c = (p*ny + (y - ylo))*nx + (x - xlo) over visible TBs p < nvis.
+//
+// Exact top-k by value-range bucketing: the candidates in [lo, hi] are
+// binned into 256 equal-width bins (a monotone map of the value, so every
+// key in a higher bin is larger than every key in a lower one); the bin
+// holding the k-th largest becomes the new [lo, hi] (its own min and max)
+// and is refined again, until it is kept whole or holds one value, whose
+// copies are then taken lowest index first. Each level removes at least
+// one distinct value, so the loop ends; smooth score rows need 1-2 levels.
+__device__ void select_row(const DraftArgs& a, const double* s, size_t row, int nvis, int ylo,
+                           int ny, int gxlo, int gxhi, int64_t n_keys, uint32_t* hist, int lane) {
+  const int nby = a.nby, nbx = a.nbx, nS = nby * nbx;
+  const int yhi = ylo + ny - 1;
+  const int nx = gxhi - gxlo + 1;
+  const int n = nvis * ny * nx;
+  const int k = topk_dev(a, n, n_keys);
+  int32_t* out = a.sel_idx + row * a.kmax;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+  double lo = INFINITY, hi = -INFINITY;
+  for (int c = lane; c < n; c += 64) {
+    lo = fmin(lo, s[c]);
+    hi = fmax(hi, s[c]);
+  }
+  lo = wave_min_dpp(lo);
+  hi = wave_max_dpp(hi);
+
+  if (a.probs) {
+    double* pr = a.probs + row * n_keys;
+    double z = 0.0;
+    for (int c = lane; c < n; c += 64) z += exp(s[c] - hi);
+    z = wave_sum_f64(z);
+    for (int64_t j = lane; j < n_keys; j += 64) {
+      const int p = (int)(j / nS), rem = (int)(j % nS);
+      const int y = rem / nbx, x = rem % nbx;
+      double val = 0.0;
+      if (p < nvis && y >= ylo && y <= yhi && x >= gxlo && x <= gxhi)
+        val = exp(s[(p * ny + (y - ylo)) * nx + (x - gxlo)] - hi) / z;
+      pr[j] = val;
+    }
+  }
+
+  int kr = k;
+  if (k >= n) {  // every candidate kept: the range already covers them all
+    kr = n;
+  } else if (k > 0) {
+    for (int level = 0; level <= n && lo < hi; ++level) {
+      const double scale = 256.0 / (hi - lo);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) hist[lane * 4 + q] = 0u;
+      wave_sync();
+      for (int c = lane; c < n; c += 64) {
+        const double v = s[c];
+        if (v >= lo && v <= hi) {
+          int bn = (int)((v - lo) * scale);
+          bn = bn < 0 ? 0 : (bn > 255 ? 255 : bn);
+          atomicAdd(&hist[255 - bn], 1u);  // reversed: position 0 is the top bin
+        }
+      }
+      wave_sync();
+      uint32_t hb[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) hb[q] = hist[lane * 4 + q];
+      const uint32_t tot = hb[0] + hb[1] + hb[2] + hb[3];
+      uint32_t ab = wave_prefix_sum_dpp(tot) - tot;  // candidates in higher bins
+      int found = -1;
+      uint32_t fa = 0, fc = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (found < 0 && ab < (uint32_t)kr && ab + hb[q] >= (uint32_t)kr) {
+          found = 255 - (lane * 4 + q);
+          fa = ab;
+          fc = hb[q];
+        }
+        ab += hb[q];
+      }
+      const uint64_t bal = __ballot(found >= 0);
+      wave_sync();
+      if (bal == 0) break;  // only with NaN scores; the emit below stays in bounds
+      const int src = __ffsll((long long)bal) - 1;
+      const int bin = __builtin_amdgcn_readlane(found, src);
+      const int ca = __builtin_amdgcn_readlane((int)fa, src);
+      const int cb = __builtin_amdgcn_readlane((int)fc, src);
+      kr -= ca;
+      double nlo = INFINITY, nhi = -INFINITY;
+      for (int c = lane; c < n; c += 64) {
+        const double v = s[c];
+        if (v >= lo && v <= hi) {
+          int bn = (int)((v - lo) * scale);
+          bn = bn < 0 ? 0 : (bn > 255 ? 255 : bn);
+          if (bn == bin) {
+            nlo = fmin(nlo, v);
+            nhi = fmax(nhi, v);
+          }
+        }
+      }
+      lo = wave_min_dpp(nlo);
+      hi = wave_max_dpp(nhi);
+      if (cb == kr) break;  // the whole bin is kept
+    }
+  }
+  // Emit in ascending candidate order (= ascending logical id): values above
+  // the final range, then the first kr values inside it.
+  int eq_before = 0, sel_before = 0;
+  if (k > 0) {
+    for (int base = 0; base < n; base += 64) {
+      const int c = base + lane;
+      const bool valid = c < n;
+      const double v = valid ? s[c] : 0.0;
+      const bool gt = valid && v > hi;
+      const bool eq = valid && v >= lo && v <= hi;
+      const uint64_t beq = __ballot(eq);
+      const int r = eq_before + __popcll(beq & lt_mask);
+      const bool want = gt || (eq && r < kr);
+      const int pos = sel_before + __popcll(__ballot(want) & lt_mask);
+      const bool sel = want && pos < k;  // never more than k (only NaN scores could ask)
+      const uint64_t bsel = __ballot(sel);
+      if (sel) {
+        const int xx = c % nx, r3 = c / nx;
+        const int yy = r3 % ny, p = r3 / ny;
+        out[pos] = p * nS + (ylo + yy) * nbx + gxlo + xx;
+      }
+      eq_before += __popcll(beq);
+      sel_before += __popcll(bsel);
+    }
+  }
+  for (int pos = sel_before + lane; pos < a.kmax; pos += 64) out[pos] = -1;
+  if (lane == 0) a.sel_cnt[row] = sel_before;
 }
 
 template <int GX, int D>
@@ -98,7 +251,8 @@ __global__ __launch_bounds__(kThreads) void draft_mask_kernel(DraftArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int nby = a.nby, nbx = a.nbx, nS = nby * nbx;
   const int ngx = (nbx + GX - 1) / GX;
-  int task = blockIdx.x;
+  int task = xcd_task(a.B * a.NH * a.ntb_q * nby * ngx);
+  if (task < 0) return;
   const int gxi = task % ngx;
   task /= ngx;
   const int by = task % nby;
@@ -167,130 +321,170 @@ __global__ __launch_bounds__(kThreads) void draft_mask_kernel(DraftArgs a) {
 
   // Phase B: one wave per row: softmax, exact top-k, sorted index list.
   uint32_t* hist = hist_all + wave * 256;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int g = wave; g < ng; g += kWaves) {
-    const double* s = sc + (size_t)g * a.row_stride;
     int gxlo, gxhi;  // recomputed: a dynamic index into xlo[] would spill
     window_range(bx0 + g, nbx, a.local_range, a.border, &gxlo, &gxhi);
-    const int nx = gxhi - gxlo + 1;
-    const int n = nvis * ny * nx;
-    const int k = topk_dev(a, n, n_keys);
-    const size_t row = bh * nq + row0 + g;
-    int32_t* out = a.sel_idx + row * a.kmax;
-
-    if (a.probs) {
-      double* pr = a.probs + row * n_keys;
-      double mx = -INFINITY;
-      for (int c = lane; c < n; c += 64) mx = fmax(mx, s[c]);
-      mx = wave_max_f64(mx);
-      double z = 0.0;
-      for (int c = lane; c < n; c += 64) z += exp(s[c] - mx);
-      z = wave_sum_f64(z);
-      for (int64_t j = lane; j < n_keys; j += 64) {
-        const int p = (int)(j / nS), rem = (int)(j % nS);
-        const int y = rem / nbx, x = rem % nbx;
-        double val = 0.0;
-        if (p < nvis && y >= ylo && y <= yhi && x >= gxlo && x <= gxhi)
-          val = exp(s[(p * ny + (y - ylo)) * nx + (x - gxlo)] - mx) / z;
-        pr[j] = val;
-      }
-    }
-
-    // Radix select: find the bin (prefix under mask) holding the k-th
-    // largest key, and kr = how many to take from it (lowest index first).
-    uint64_t prefix = 0, mask = 0;
-    int kr = k;
-    if (k > 0 && k < n) {
-      uint64_t kmx = 0, kmn = ~0ull;
-      for (int c = lane; c < n; c += 64) {
-        const uint64_t key = order_key(s[c]);
-        kmx = key > kmx ? key : kmx;
-        kmn = key < kmn ? key : kmn;
-      }
-      kmx = wave_max_u64(kmx);
-      kmn = wave_min_u64(kmn);
-      const uint64_t diff = kmx ^ kmn;
-      if (diff == 0) {
-        mask = ~0ull;
-        prefix = kmx;
-      } else {
-        const int top = 63 - __clzll((long long)diff);
-        mask = top == 63 ? 0ull : (~0ull << (top + 1));
-        prefix = kmx & mask;
-        int shift = top + 1;
-        while (shift > 0) {
-          const int lo = shift > 8 ? shift - 8 : 0;
-          const uint32_t nb = 1u << (shift - lo);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) hist[lane * 4 + q] = 0u;
-          wave_sync();
-          for (int c = lane; c < n; c += 64) {
-            const uint64_t key = order_key(s[c]);
-            if ((key & mask) == prefix) atomicAdd(&hist[(uint32_t)(key >> lo) & (nb - 1)], 1u);
-          }
-          wave_sync();
-          uint32_t hb[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) hb[q] = hist[lane * 4 + q];
-          const uint32_t tot = hb[0] + hb[1] + hb[2] + hb[3];
-          uint32_t ab = wave_suffix_sum(tot, lane) - tot;  // count in higher lanes' bins
-          int found = -1;
-          uint32_t fa = 0, fc = 0;
-#pragma unroll
-          for (int q = 3; q >= 0; --q) {
-            if (found < 0 && ab < (uint32_t)kr && ab + hb[q] >= (uint32_t)kr) {
-              found = lane * 4 + q;
-              fa = ab;
-              fc = hb[q];
-            }
-            ab += hb[q];
-          }
-          const uint64_t bal = __ballot(found >= 0);
-          const int src = __ffsll((long long)bal) - 1;
-          const int bin = __shfl(found, src);
-          const uint32_t ca = __shfl(fa, src), cb = __shfl(fc, src);
-          kr -= (int)ca;
-          prefix |= (uint64_t)bin << lo;
-          mask |= (uint64_t)(nb - 1) << lo;
-          wave_sync();
-          if ((int)cb == kr) break;  // the whole bin is kept
-          shift = lo;
-        }
-      }
-    }
-    // Emit the kept candidates in ascending candidate order (= ascending
-    // logical id): keys above the bin, then the first kr keys inside it.
-    int eq_before = 0, sel_before = 0;
-    if (k > 0) {
-      for (int base = 0; base < n; base += 64) {
-        const int c = base + lane;
-        const bool valid = c < n;
-        const uint64_t km = valid ? (order_key(s[c]) & mask) : 0ull;
-        const bool gt = valid && km > prefix;
-        const bool eq = valid && km == prefix;
-        const uint64_t beq = __ballot(eq);
-        const int r = eq_before + __popcll(beq & lt_mask);
-        const bool sel = gt || (eq && r < kr);
-        const uint64_t bsel = __ballot(sel);
-        if (sel) {
-          const int pos = sel_before + __popcll(bsel & lt_mask);
-          const int xx = c % nx, r3 = c / nx;
-          const int yy = r3 % ny, p = r3 / ny;
-          out[pos] = p * nS + (ylo + yy) * nbx + gxlo + xx;
-        }
-        eq_before += __popcll(beq);
-        sel_before += __popcll(bsel);
-      }
-    }
-    for (int pos = k + lane; pos < a.kmax; pos += 64) out[pos] = -1;
-    if (lane == 0) a.sel_cnt[row] = k;
+    select_row(a, sc + (size_t)g * a.row_stride, bh * nq + row0 + g, nvis, ylo, ny, gxlo, gxhi,
+               n_keys, hist, lane);
   }
+}
+
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+// Matrix-core path for windows of up to kTileMaxCand candidates per row. A
+// workgroup scores a 4 x 4 tile of query blocks (16 rows, one
+// v_mfma_f64_16x16x4f64 row tile) against the union of their windows in
+// tiles of 16 keys: A = pooled queries (registers), B = pooled keys read
+// straight from the d-major pooled ring (16 consecutive keys per d are one
+// 128-byte run). Lane l holds A[l%16][l/16], B[l/16][l%16] and outputs
+// D[4j + l/16][l%16], j = 0..3. Each output lands in LDS at its row's
+// candidate index; then one wave per row runs select_row().
+constexpr int kTileMaxCand = 768;
+constexpr int kTileWaves = 8;  // 16 rows: two per wave in the selection phase
+
+template <int D>
+__global__ __launch_bounds__(64 * kTileWaves) void draft_tile_kernel(DraftArgs a) {
+  extern __shared__ double smem[];
+  double* sc = smem;                                                         // [16][row_stride]
+  uint32_t* hist_all = reinterpret_cast<uint32_t*>(sc + 16 * (size_t)a.row_stride);  // [waves][256]
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int nby = a.nby, nbx = a.nbx, nS = nby * nbx;
+  const int nty = (nby + 3) / 4, ntx = (nbx + 3) / 4;
+  int task = xcd_task(a.B * a.NH * a.ntb_q * nty * ntx);
+  if (task < 0) return;
+  const int tx = task % ntx;
+  task /= ntx;
+  const int ty = task % nty;
+  task /= nty;
+  const int tq = task % a.ntb_q;
+  task /= a.ntb_q;
+  const int h = task % a.NH;
+  const int b = task / a.NH;
+  const int by0 = 4 * ty, bx0 = 4 * tx;
+  const int by1 = min(by0 + 3, nby - 1), bx1 = min(bx0 + 3, nbx - 1);
+  const int64_t qtb = a.q_first_abs_tb + tq;
+  const int nq = a.ntb_q * nS;
+  const int64_t n_keys = (int64_t)a.view.n * nS;
+  const size_t bh = (size_t)b * a.NH + h;
+
+  int nvis = 0;
+  for (int p = 0; p < a.view.n; ++p)
+    if (a.view.abs_tb[p] <= qtb) nvis = p + 1;
+  int uylo, uyhi, uxlo, uxhi, tmp;
+  window_range(by0, nby, a.local_range, a.border, &uylo, &tmp);
+  window_range(by1, nby, a.local_range, a.border, &tmp, &uyhi);
+  window_range(bx0, nbx, a.local_range, a.border, &uxlo, &tmp);
+  window_range(bx1, nbx, a.local_range, a.border, &tmp, &uxhi);
+  const int nuy = uyhi - uylo + 1, nux = uxhi - uxlo + 1;
+  const int U = nvis * nuy * nux;
+
+  // A fragments: row lane%16 is query block (by0 + r/4, bx0 + r%4)
+  const int r = lane & 15, dq = lane >> 4;
+  const int aqy = by0 + (r >> 2), aqx = bx0 + (r & 3);
+  const bool arow = aqy < nby && aqx < nbx;
+  // clamped address: loads are unconditional (no per-load branches), the
+  // padding rows of an edge tile are zeroed afterwards
+  const double* qrow =
+      a.q_pool + (bh * nq + (size_t)tq * nS + min(aqy, nby - 1) * nbx + min(aqx, nbx - 1)) * D;
+  double af[D / 4];
+#pragma unroll
+  for (int s2 = 0; s2 < D / 4; ++s2) {
+    const double v = qrow[4 * s2 + dq];
+    af[s2] = arow ? v : 0.0;
+  }
+
+  // this lane's four output rows: (qy, qx) = (by0 + j, bx0 + dq)
+  const int oqx = bx0 + dq;
+  int oxlo, oxhi;
+  window_range(min(oqx, nbx - 1), nbx, a.local_range, a.border, &oxlo, &oxhi);
+  const double sqrt_d = sqrt((double)D);
+
+  // key u of tile t lives at (p, y, x); u >= U pads with key 0 (a valid
+  // address) and is zeroed after the load
+  auto key_ptr = [&](int u, int& p, int& y, int& x) {
+    const int uu = u < U ? u : 0;
+    const int ux = uu % nux, r2 = uu / nux;
+    y = uylo + r2 % nuy;
+    p = r2 / nuy;
+    x = uxlo + ux;
+    return a.kpool_ring + (bh * a.n_slots + a.view.slot[p]) * (size_t)D * nS + (size_t)y * nbx + x;
+  };
+  // Software pipeline over half tiles (16 of the 32 k-steps): the next
+  // half's 16 loads are in flight while the current half's MFMAs run.
+  constexpr int HS = D / 8;  // k-steps per half tile
+  auto load_half = [&](int q, double (&bf)[HS]) {
+    int p, y, x;
+    const int t = wave + (q >> 1) * kTileWaves;
+    const double* kp = key_ptr(16 * t + r, p, y, x) + (size_t)((q & 1) * HS * 4) * nS;
+#pragma unroll
+    for (int s2 = 0; s2 < HS; ++s2) bf[s2] = kp[(size_t)(4 * s2 + dq) * nS];
+  };
+  const int ntiles = U > 16 * wave ? (U - 16 * wave + 16 * kTileWaves - 1) / (16 * kTileWaves) : 0;
+  double b0[HS], b1[HS];
+  if (ntiles > 0) load_half(0, b0);
+  for (int it = 0; it < ntiles; ++it) {
+    load_half(2 * it + 1, b1);
+    const int t = wave + it * kTileWaves;
+    const int u = 16 * t + r;
+    const bool uval = u < U;
+    f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int s2 = 0; s2 < HS; ++s2)
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64(af[s2], uval ? b0[s2] : 0.0, acc, 0, 0, 0);
+    if (it + 1 < ntiles) load_half(2 * it + 2, b0);  // uniform
+#pragma unroll
+    for (int s2 = 0; s2 < HS; ++s2)
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64(af[HS + s2], uval ? b1[s2] : 0.0, acc, 0, 0, 0);
+    int p, y, x;
+    key_ptr(u, p, y, x);
+    if (uval && oqx < nbx && x >= oxlo && x <= oxhi) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int oqy = by0 + j;
+        if (oqy >= nby) continue;
+        int oylo, oyhi;
+        window_range(oqy, nby, a.local_range, a.border, &oylo, &oyhi);
+        if (y < oylo || y > oyhi) continue;
+        const int ny = oyhi - oylo + 1, nx = oxhi - oxlo + 1;
+        sc[(size_t)(4 * j + dq) * a.row_stride + (p * ny + (y - oylo)) * nx + (x - oxlo)] =
+            acc[j] / sqrt_d;
+      }
+    }
+  }
+  __syncthreads();
+
+  uint32_t* hist = hist_all + wave * 256;
+  for (int ro = wave; ro < 16; ro += kTileWaves) {
+    const int qy = by0 + (ro >> 2), qx = bx0 + (ro & 3);
+    if (qy >= nby || qx >= nbx) continue;  // uniform per wave
+    int ylo, yhi, xlo, xhi;
+    window_range(qy, nby, a.local_range, a.border, &ylo, &yhi);
+    window_range(qx, nbx, a.local_range, a.border, &xlo, &xhi);
+    select_row(a, sc + (size_t)ro * a.row_stride, bh * nq + (size_t)tq * nS + qy * nbx + qx, nvis,
+               ylo, yhi - ylo + 1, xlo, xhi, n_keys, hist, lane);
+  }
+}
+
+template <int D>
+hipError_t launch_tile(const DraftArgs& a, hipStream_t s) {
+  const long long tasks = (long long)a.B * a.NH * a.ntb_q * ((a.nby + 3) / 4) * ((a.nbx + 3) / 4);
+  const long long wgs = 8 * ((tasks + 7) / 8);
+  const size_t shmem = 16 * (size_t)a.row_stride * sizeof(double) + kTileWaves * 256 * 4;
+  if (shmem > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute((const void*)draft_tile_kernel<D>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(draft_tile_kernel<D>, dim3((unsigned)wgs), dim3(64 * kTileWaves), shmem, s, a);
+  return hipGetLastError();
 }
 
 template <int GX, int D>
 hipError_t launch(const DraftArgs& a, hipStream_t s) {
   const int ngx = (a.nbx + GX - 1) / GX;
-  const long long groups = (long long)a.B * a.NH * a.ntb_q * a.nby * ngx;
+  const long long tasks = (long long)a.B * a.NH * a.ntb_q * a.nby * ngx;
+  const long long groups = 8 * ((tasks + 7) / 8);
   const size_t shmem =
       (size_t)D * GX * sizeof(double) + (size_t)GX * a.row_stride * sizeof(double) + kWaves * 256 * 4;
   if (shmem > 64 * 1024) {
@@ -316,6 +510,8 @@ hipError_t launch_d(const DraftArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_draft_mask(const DraftArgs& a, hipStream_t s) {
+  if (a.row_stride <= kTileMaxCand)
+    return a.D == 64 ? launch_tile<64>(a, s) : launch_tile<128>(a, s);
   return a.D == 64 ? launch_d<64>(a, s) : launch_d<128>(a, s);
 }
 

@@ -133,8 +133,9 @@ lcsa_status lcsa_draft_mask(const lcsa_geom* gq, const double* q_pool, int64_t q
     }
     num /= x;
     den /= x;
-    if (num > INT64_MAX || den > INT64_MAX)
-      return fail(LCSA_ERR_PARAM, "ratio rule does not reduce to 64-bit integers");
+    if (num > UINT32_MAX || den > INT64_MAX)
+      return fail(LCSA_ERR_PARAM,
+                  "ratio rule does not reduce to a 32-bit numerator and 64-bit denominator");
     a.ratio_num = (int64_t)num;
     a.ratio_den = (int64_t)den;
   } else {

@@ -22,11 +22,13 @@ namespace {
 
 constexpr int kThreads = 256;
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // native vector: stays in VGPRs
+
 template <int ESZ>
-__device__ inline void widen_chunk(const uint4& v, double* out);
+__device__ inline void widen_chunk(const u32x4& v, double* out);
 
 template <>
-__device__ inline void widen_chunk<2>(const uint4& v, double* out) {
+__device__ inline void widen_chunk<2>(const u32x4& v, double* out) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -36,7 +38,7 @@ __device__ inline void widen_chunk<2>(const uint4& v, double* out) {
 }
 
 template <>
-__device__ inline void widen_chunk<4>(const uint4& v, double* out) {
+__device__ inline void widen_chunk<4>(const u32x4& v, double* out) {
   out[0] = (double)__uint_as_float(v.x);
   out[1] = (double)__uint_as_float(v.y);
   out[2] = (double)__uint_as_float(v.z);
@@ -61,124 +63,132 @@ __device__ inline size_t token_offset(const PartitionArgs& a, int b, int h, int 
   return ((((size_t)b * a.T + t) * a.H + y) * a.W + x) * a.NH * a.D + (size_t)h * a.D;
 }
 
-// Copy one 128 x D block to a contiguous tile and (optionally) write its
-// column means to pool[d * pool_stride].
+// Load this thread's chunks of one 128 x D block (token layout source).
 template <int ESZ, int D>
-__device__ inline void copy_pool(const PartitionArgs& a, const char* src, char* dst,
-                                 double* pool, size_t pool_stride, int b, int h, int bt, int by,
-                                 int bx, double (*red)[16 / ESZ]) {
+__device__ inline void load_block(const PartitionArgs& a, const char* src, int b, int h, int bt,
+                                  int by, int bx, u32x4 (&v)[Geo<ESZ, D>::ITERS]) {
   using G = Geo<ESZ, D>;
-  const int tid = threadIdx.x;
-  const int c = tid % G::CPT;
-  const int tsub = tid / G::CPT;
-  uint4 v[G::ITERS];
+  const int c = threadIdx.x % G::CPT, tsub = threadIdx.x / G::CPT;
 #pragma unroll
   for (int it = 0; it < G::ITERS; ++it) {
     const int tau = it * G::TPI + tsub;
-    v[it] = *reinterpret_cast<const uint4*>(
+    v[it] = *reinterpret_cast<const u32x4*>(
         src + (token_offset(a, b, h, bt, by, bx, tau) + c * G::EPC) * ESZ);
   }
+}
+
+// Store the chunks as a contiguous [128][D] tile and return the thread's
+// float64 partial column sums in red[tid][0 .. EPC).
+template <int ESZ, int D>
+__device__ inline void store_tile_sum(char* dst, const u32x4 (&v)[Geo<ESZ, D>::ITERS],
+                                      double* red_row) {
+  using G = Geo<ESZ, D>;
+  const int c = threadIdx.x % G::CPT, tsub = threadIdx.x / G::CPT;
   double acc[G::EPC];
 #pragma unroll
   for (int e = 0; e < G::EPC; ++e) acc[e] = 0.0;
 #pragma unroll
   for (int it = 0; it < G::ITERS; ++it) {
     const int tau = it * G::TPI + tsub;
-    *reinterpret_cast<uint4*>(dst + ((size_t)tau * D + c * G::EPC) * ESZ) = v[it];
-    if (pool) {
-      double w[G::EPC];
-      widen_chunk<ESZ>(v[it], w);
+    *reinterpret_cast<u32x4*>(dst + ((size_t)tau * D + c * G::EPC) * ESZ) = v[it];
+    double w[G::EPC];
+    widen_chunk<ESZ>(v[it], w);
 #pragma unroll
-      for (int e = 0; e < G::EPC; ++e) acc[e] += w[e];
-    }
+    for (int e = 0; e < G::EPC; ++e) acc[e] += w[e];
   }
-  if (!pool) return;
 #pragma unroll
-  for (int e = 0; e < G::EPC; ++e) red[tid][e] = acc[e];
-  __syncthreads();
-  if (tid < D) {
-    const int cc = tid / G::EPC, e = tid % G::EPC;
-    double s = 0.0;
-    for (int ts = 0; ts < G::TPI; ++ts) s += red[ts * G::CPT + cc][e];
-    pool[(size_t)tid * pool_stride] = s / 128.0;
-  }
-  __syncthreads();
+  for (int e = 0; e < G::EPC; ++e) red_row[e] = acc[e];
+}
+
+// Column d's block mean from the partial sums (fixed summation order).
+template <int ESZ, int D>
+__device__ inline double block_mean(const double* red, int d) {
+  using G = Geo<ESZ, D>;
+  const int cc = d / G::EPC, e = d % G::EPC;
+  double s = 0.0;
+  for (int ts = 0; ts < G::TPI; ++ts) s += red[(ts * G::CPT + cc) * G::EPC + e];
+  return s / 128.0;
 }
 
 template <int ESZ, int D>
 __global__ __launch_bounds__(kThreads) void partition_pool_kernel(PartitionArgs a) {
   using G = Geo<ESZ, D>;
-  __shared__ double red[kThreads][G::EPC];
+  __shared__ double red_q[kThreads * G::EPC];
+  __shared__ double red_k[kThreads * G::EPC];
   __shared__ __attribute__((aligned(16))) char vstage[128 * G::PITCH];
 
-  const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // heads vary fastest across workgroups: the heads of one block read the
+  // same 128 token rows ([NH][D] contiguous per token) at about the same time
   const int nby = a.H / 8, nbx = a.W / 8, nS = nby * nbx;
+  const int nblk = (a.T / 2) * nS;
+  const int h = blockIdx.x % a.NH;
+  const int n = (blockIdx.x / a.NH) % nblk;
+  const int b = blockIdx.x / (a.NH * nblk);
   const int bt = n / nS, s = n % nS, by = s / nbx, bx = s % nbx;
-  const int nq = (a.T / 2) * nS;
+  const int nq = nblk;
   const size_t tile = (size_t)128 * D;
   const int slot = (a.first_slot + bt) % a.n_slots;
   const size_t ring_blk = (((size_t)b * a.NH + h) * a.n_slots + slot) * nS + s;
+  const int tid = threadIdx.x;
+  const bool has_q = a.q != nullptr;
 
-  if (a.q) {
-    const size_t qb = ((size_t)b * a.NH + h) * nq + n;
-    copy_pool<ESZ, D>(a, (const char*)a.q, (char*)a.q_blk + qb * tile * ESZ, a.q_pool + qb * D, 1,
-                      b, h, bt, by, bx, red);
-  }
-  // k: tile into the ring slot, means d-major into the pooled ring.
-  double* kp = a.kpool_ring + (((size_t)b * a.NH + h) * a.n_slots + slot) * D * nS + s;
-  copy_pool<ESZ, D>(a, (const char*)a.k, (char*)a.k_ring + ring_blk * tile * ESZ, kp, nS, b, h,
-                    bt, by, bx, red);
+  // all global loads first: up to 3 x 128 bytes per thread in flight
+  u32x4 vq[G::ITERS], vk[G::ITERS], vv[G::ITERS];
+  if (has_q) load_block<ESZ, D>(a, (const char*)a.q, b, h, bt, by, bx, vq);
+  load_block<ESZ, D>(a, (const char*)a.k, b, h, bt, by, bx, vk);
+  load_block<ESZ, D>(a, (const char*)a.v, b, h, bt, by, bx, vv);
 
-  // v: stage the block in LDS, then write it transposed ([D][128]).
+  const size_t qb = ((size_t)b * a.NH + h) * nq + n;
+  if (has_q) store_tile_sum<ESZ, D>((char*)a.q_blk + qb * tile * ESZ, vq, red_q + tid * G::EPC);
+  store_tile_sum<ESZ, D>((char*)a.k_ring + ring_blk * tile * ESZ, vk, red_k + tid * G::EPC);
   {
-    const int tid = threadIdx.x;
-    const int c = tid % G::CPT;
-    const int tsub = tid / G::CPT;
-    uint4 v[G::ITERS];
+    const int c = tid % G::CPT, tsub = tid / G::CPT;
 #pragma unroll
     for (int it = 0; it < G::ITERS; ++it) {
       const int tau = it * G::TPI + tsub;
-      v[it] = *reinterpret_cast<const uint4*>(
-          (const char*)a.v + (token_offset(a, b, h, bt, by, bx, tau) + c * G::EPC) * ESZ);
+      *reinterpret_cast<u32x4*>(vstage + tau * G::PITCH + c * 16) = vv[it];
     }
+  }
+  __syncthreads();
+
+  if (tid < D) {
+    if (has_q) a.q_pool[qb * D + tid] = block_mean<ESZ, D>(red_q, tid);
+    // k means go d-major into the pooled ring
+    a.kpool_ring[((((size_t)b * a.NH + h) * a.n_slots + slot) * D + tid) * nS + s] =
+        block_mean<ESZ, D>(red_k, tid);
+  }
+  // v: write the staged block transposed ([D][128])
+  char* vdst = (char*)a.v_ring + ring_blk * tile * ESZ;
+  constexpr int KC = 128 / G::EPC;  // 16-byte chunks per transposed row
 #pragma unroll
-    for (int it = 0; it < G::ITERS; ++it) {
-      const int tau = it * G::TPI + tsub;
-      *reinterpret_cast<uint4*>(vstage + tau * G::PITCH + c * 16) = v[it];
-    }
-    __syncthreads();
-    char* vdst = (char*)a.v_ring + ring_blk * tile * ESZ;
-    constexpr int KC = 128 / G::EPC;  // 16-byte chunks per transposed row
+  for (int it = 0; it < G::ITERS; ++it) {
+    const int e = it * kThreads + tid;
+    const int d = e / KC, kc = e % KC;
+    uint32_t w[4];
+    if constexpr (ESZ == 2) {
 #pragma unroll
-    for (int it = 0; it < G::ITERS; ++it) {
-      const int e = it * kThreads + tid;
-      const int d = e / KC, kc = e % KC;
-      uint32_t w[4];
-      if constexpr (ESZ == 2) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const uint32_t lo = *reinterpret_cast<const uint16_t*>(
-              vstage + (kc * 8 + 2 * u) * G::PITCH + d * 2);
-          const uint32_t hi = *reinterpret_cast<const uint16_t*>(
-              vstage + (kc * 8 + 2 * u + 1) * G::PITCH + d * 2);
-          w[u] = lo | (hi << 16);
-        }
-      } else {
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          w[u] = *reinterpret_cast<const uint32_t*>(vstage + (kc * 4 + u) * G::PITCH + d * 4);
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t lo =
+            *reinterpret_cast<const uint16_t*>(vstage + (kc * 8 + 2 * u) * G::PITCH + d * 2);
+        const uint32_t hi =
+            *reinterpret_cast<const uint16_t*>(vstage + (kc * 8 + 2 * u + 1) * G::PITCH + d * 2);
+        w[u] = lo | (hi << 16);
       }
-      *reinterpret_cast<uint4*>(vdst + ((size_t)d * 128 + kc * G::EPC) * ESZ) =
-          make_uint4(w[0], w[1], w[2], w[3]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        w[u] = *reinterpret_cast<const uint32_t*>(vstage + (kc * 4 + u) * G::PITCH + d * 4);
     }
+    *reinterpret_cast<u32x4*>(vdst + ((size_t)d * 128 + kc * G::EPC) * ESZ) =
+        u32x4{w[0], w[1], w[2], w[3]};
   }
 }
 
 template <int ESZ, int D>
 hipError_t launch(const PartitionArgs& a, hipStream_t s) {
-  const int nblk = (a.T / 2) * (a.H / 8) * (a.W / 8);
-  dim3 grid(nblk, a.NH, a.B);
-  hipLaunchKernelGGL((partition_pool_kernel<ESZ, D>), grid, dim3(kThreads), 0, s, a);
+  const long long nblk = (long long)(a.T / 2) * (a.H / 8) * (a.W / 8);
+  const long long wgs = nblk * a.NH * a.B;
+  hipLaunchKernelGGL((partition_pool_kernel<ESZ, D>), dim3((unsigned)wgs), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
