@@ -21,6 +21,7 @@ import argparse
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -39,16 +40,26 @@ def parse():
     ap.add_argument("--workload", default="step_768x1408")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-heads", type=int, default=12)
+    ap.add_argument("--cpu-sample-steps", type=int, default=4)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before the warmup, as "
                          "the calibration kernel for rocprofv3 FETCH_SIZE/WRITE_SIZE")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM bytes per attention launch measured by rocprofv3 counters")
+    ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU work: turn the rocprofv3 output of a --kernel-trace --stats run "
+                         "and of --pmc FETCH_SIZE / --pmc WRITE_SIZE runs of this script into "
+                         "profiles/<kernels>_<workload>.md and the workload's traffic.json entry")
+    ap.add_argument("--bench-log", default=None,
+                    help="with --summarize-profiles: a log whose last line is this script's JSON")
     return ap.parse_args()
 
 
 def main():
     args = parse()
+    if args.summarize_profiles:
+        summarize_profiles(args)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the LCSA path "
               "shards by head with no communication, so one GPU's figure is the per-GPU rate.",
@@ -71,6 +82,8 @@ def main():
     code = L.LCSA_BF16 if w.dtype == "bf16" else L.LCSA_F32
 
     if args.copy_probe_mib:
+        # the first device-to-device copy of the process: a plain copy kernel
+        # of known size that calibrates the FETCH_SIZE / WRITE_SIZE counters
         src = torch.ones(args.copy_probe_mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         dst.copy_(src)
@@ -161,8 +174,8 @@ def main():
     try:
         with open(args.traffic_json) as f:
             tj = json.load(f)
-        if tj.get("workload") == args.workload:
-            traffic = tj.get("bytes_per_launch")
+        entry = tj.get(args.workload) or {}
+        traffic = entry.get("bytes_per_launch")
     except (OSError, ValueError):
         pass
 
@@ -192,13 +205,15 @@ def main():
     }
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_heads, flops_pair)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_heads, args.cpu_sample_steps,
+                                              flops_pair)
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(w, sample_heads, flops_pair):
-    """The float64 oracle, as it stands, on one streaming step of the same
-    workload (the first `sample_heads` heads), timed on the host."""
+def cpu_baseline(w, sample_heads, sample_steps, flops_pair):
+    """The float64 oracle, as it stands, on the first `sample_steps`
+    consecutive steps of the same workload's stream (the first
+    `sample_heads` heads), timed on the host."""
     import numpy as np
 
     from block_sparse_attention_03_amd import synth
@@ -219,16 +234,122 @@ def cpu_baseline(w, sample_heads, flops_pair):
         d0 = synth.make_qkv(w.seed, nh, w.head_dim, w.height, w.width, 0, w.cache_frames,
                             dtype=w.dtype, which="kv")
         O.prime_cache(cache, d0["k"][1], d0["v"][1], 0)
-    t0 = w.cache_frames
-    d = synth.make_qkv(w.seed, nh, w.head_dim, w.height, w.width, t0, t0 + w.frames, dtype=w.dtype)
-    tic = time.perf_counter()
-    res = O.lcsa_step(d["q"][1], d["k"][1], d["v"][1], cache, t0 // 2, p)
-    sec = time.perf_counter() - tic
-    pairs = int(sum(len(r) for bh in res.sel for hh in bh for r in hh))
+    steps = sample_steps if w.cache_frames else 1
+    sec, pairs = 0.0, 0
+    for n in range(steps):
+        t0 = w.cache_frames + n * w.frames
+        d = synth.make_qkv(w.seed, nh, w.head_dim, w.height, w.width, t0, t0 + w.frames,
+                           dtype=w.dtype)
+        tic = time.perf_counter()
+        res = O.lcsa_step(d["q"][1], d["k"][1], d["v"][1], cache, t0 // 2, p)
+        sec += time.perf_counter() - tic
+        pairs += int(sum(len(r) for bh in res.sel for hh in bh for r in hh))
     return {"value": round(pairs * flops_pair / sec / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
             "kind": "oracle", "seconds": round(sec, 3),
-            "sample": f"one full LCSA step (partition, pool, draft, top-k, attention) of the "
-                      f"same workload, heads 0..{nh - 1} of {w.heads}, float64 NumPy"}
+            "sample": f"{steps} consecutive full LCSA steps (partition, pool, draft, top-k, "
+                      f"attention, cache update) of the same workload's stream, heads 0..{nh - 1} "
+                      f"of {w.heads}, float64 NumPy"}
+
+
+ATTN_KERNEL = "attn_bf16"
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def _csv_rows(d, suffix):
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True))
+    if not files:
+        raise SystemExit(f"no *{suffix} under {d}")
+    with open(files[0], newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _short(name):
+    m = re.search(r"lcsa::\(anonymous namespace\)::(\w+)(<[^>]*>)?", name)
+    return m.group(1) + (m.group(2) or "") if m else None
+
+
+def _counter_per_dispatch(d, counter):
+    """(calibration copy value, mean value over the attention dispatches, n) in KiB."""
+    rows = [r for r in _csv_rows(d, "counter_collection.csv") if r["Counter_Name"] == counter]
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    copy = next((float(r["Counter_Value"]) for r in rows if COPY_KERNEL in r["Kernel_Name"]), None)
+    attn = [float(r["Counter_Value"]) for r in rows if ATTN_KERNEL in r["Kernel_Name"]]
+    if copy is None or not attn:
+        raise SystemExit(f"{d}: calibration copy or attention dispatches missing for {counter}")
+    return copy, sum(attn) / len(attn), len(attn)
+
+
+def summarize_profiles(args):
+    """Host-only: write the kernel-trace summary and the counter-derived HBM
+    traffic of the attention kernel for one workload."""
+    if not args.copy_probe_mib:
+        raise SystemExit("--summarize-profiles needs --copy-probe-mib (the calibration size)")
+    trace_dir, fetch_dir, write_dir = args.summarize_profiles
+    probe_bytes = args.copy_probe_mib * (1 << 20)
+    fc, fa, nf = _counter_per_dispatch(fetch_dir, "FETCH_SIZE")
+    wc, wa, nw = _counter_per_dispatch(write_dir, "WRITE_SIZE")
+    f_factor = probe_bytes / (fc * 1024.0)
+    w_factor = probe_bytes / (wc * 1024.0)
+    fetch_b = fa * 1024.0 * f_factor
+    write_b = wa * 1024.0 * w_factor
+    stats = [r for r in _csv_rows(trace_dir, "kernel_stats.csv") if _short(r["Name"])]
+    bench = None
+    if args.bench_log:
+        with open(args.bench_log) as f:
+            bench = json.loads([ln for ln in f if ln.startswith("{")][-1])
+    entry = {"kernel": ATTN_KERNEL, "bytes_per_launch": round(fetch_b + write_b),
+             "fetch_bytes_per_launch": round(fetch_b), "write_bytes_per_launch": round(write_b),
+             "fetch_kib_raw": round(fa, 1), "write_kib_raw": round(wa, 1),
+             "calibration": {"copy_bytes": probe_bytes, "fetch_kib": round(fc, 1),
+                             "write_kib": round(wc, 1), "fetch_factor": round(f_factor, 4),
+                             "write_factor": round(w_factor, 4)},
+             "dispatches": [nf, nw]}
+    try:
+        with open(args.traffic_json) as f:
+            tj = json.load(f)
+    except (OSError, ValueError):
+        tj = {}
+    tj[args.workload] = entry
+    with open(args.traffic_json, "w") as f:
+        json.dump(tj, f, indent=1, sort_keys=True)
+        f.write("\n")
+
+    sw = (f"--steps {bench['steps']} --warmup {bench['warmup']}" if bench else "--steps S --warmup W")
+    kernels = sorted({_short(r["Name"]) for r in stats})
+    tag = "_".join(k.split("<")[0].replace("_kernel", "") for k in kernels)
+    out = os.path.join(ROOT, "profiles", f"{tag}_{args.workload}.md")
+    cmd_b = (f"python3 bench.py --workload {args.workload} {sw} "
+             f"--no-cpu-baseline --copy-probe-mib {args.copy_probe_mib}")
+    lines = [f"# Kernel trace and HBM traffic: workload {args.workload}", "",
+             "Commands (from the repository root, with `TMPDIR=/tmp` exported for the profiler's "
+             "scratch files):", "",
+             f"    rocprofv3 --kernel-trace --stats --output-format csv -d TRACE_DIR -o tr -- {cmd_b}",
+             f"    rocprofv3 --pmc FETCH_SIZE --output-format csv -d FETCH_DIR -o pmc -- {cmd_b}",
+             f"    rocprofv3 --pmc WRITE_SIZE --output-format csv -d WRITE_DIR -o pmc -- {cmd_b}",
+             f"    python3 bench.py --workload {args.workload} --copy-probe-mib {args.copy_probe_mib} "
+             "--summarize-profiles TRACE_DIR FETCH_DIR WRITE_DIR --bench-log BENCH_LOG", "",
+             "## Kernel durations (rocprofv3 --stats)", "",
+             "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append(f"| {_short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
+    if bench:
+        lines += ["", f"bench.py, same workload, HIP events on the launch stream: attention "
+                  f"{bench['attn_ms'] * 1e3:.1f} us per launch, step {bench['ms_per_step'] * 1e3:.1f} us, "
+                  f"{bench['config']['selected_pairs_per_step']} block pairs per step "
+                  f"(steps={bench['steps']}, warmup={bench['warmup']})."]
+    lines += ["", "## HBM traffic of the attention kernel (rocprofv3 --pmc)", "",
+              f"Calibration: the plain {args.copy_probe_mib} MiB device copy ({COPY_KERNEL}) reads "
+              f"FETCH_SIZE {fc:.0f} KiB and WRITE_SIZE {wc:.0f} KiB, so one counted KiB is "
+              f"{f_factor:.3f} KiB fetched and {w_factor:.3f} KiB written.", "",
+              "| counter | raw KiB per launch | calibrated MB per launch | launches |", "|---|---|---|---|",
+              f"| FETCH_SIZE | {fa:.0f} | {fetch_b / 1e6:.1f} | {nf} |",
+              f"| WRITE_SIZE | {wa:.0f} | {write_b / 1e6:.1f} | {nw} |", ""]
+    with open(out, "w") as f:
+        f.write("\n".join(lines))
+    print(json.dumps({"wrote": [out, args.traffic_json], args.workload: entry}))
 
 
 if __name__ == "__main__":

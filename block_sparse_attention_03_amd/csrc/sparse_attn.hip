@@ -14,12 +14,17 @@
 //                   accumulators (each lane owns one query column, so the
 //                   row softmax needs one cross-lane exchange per block)
 // with an online softmax in base 2 (exp2 of a log2e-prescaled logit).
-// K and V^T tiles (2 x 32 KB at D = 128) are double-buffered in LDS: the
-// next block's tiles are fetched into registers while the current block is
-// computed, then written to the other buffer. LDS rows are XOR-swizzled in
-// 16-byte chunks so the fragment reads are bank-conflict free, and V^T's
-// keys are permuted inside each 16-key group so one 16-byte read yields a
-// whole A fragment in the order the S^T accumulator layout produces P.
+// A key block is consumed in two 64-key halves. Each half (K [64][D] plus
+// V^T [D][64], 32 KB at D = 128) goes straight from global memory into one
+// of two LDS buffers (global_load_lds, no register staging): while one
+// half is computed the next one is in flight, so 64 KB of LDS per
+// workgroup and two workgroups per CU. LDS rows are XOR-swizzled in
+// 16-byte chunks so the fragment reads are bank-conflict free, and K rows
+// are permuted inside each 32-key tile so the S^T accumulator rows come out
+// in the key order of V^T's A fragments. The row max is a max3 tree plus
+// one cross-half exchange (v_permlane32_swap); O is rescaled only when the
+// running max grows by more than 2^8, and row sums use v_dot2 on the bf16
+// probabilities actually multiplied into V.
 // fp32 path (small validation workloads): one thread per query row on the
 // vector ALU.
 #include <type_traits>
