@@ -63,6 +63,12 @@ def load_library(path: str = LIB_PATH):
     if not os.path.exists(path):
         raise OSError(f"{path} is missing: build it with "
                       "`python -m block_sparse_attention_03_amd.build_lib`")
+    try:
+        # torch first: the library then binds to the HIP runtime torch has
+        # loaded, so both see the same devices, streams and allocations
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     G, P, C = POINTER(Geom), POINTER(SelectParams), POINTER(KvCacheStruct)
     sig = {
