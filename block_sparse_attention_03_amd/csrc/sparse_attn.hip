@@ -143,26 +143,30 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   const int per = (n_tasks + 7) / 8;
   const int task = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
   if (task >= n_tasks) return;
-  const int i = task % nq;
+  // longest lists first: query TBs in descending order (a later TB sees more
+  // key blocks), so the short lists of the first TBs fill the tail
+  const int r = task % nq, n_tb = a.T / 2;
+  const int i = (n_tb - 1 - r / nS) * nS + r % nS;
   const int bh = task / nq;
   const int h = bh % a.NH, b = bh / a.NH;
+  const size_t row = (size_t)bh * nq + i;  // flat query-block row of the lists and q_blk
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
-  const int cnt = min(a.sel_cnt[task], a.kmax);
-  const int32_t* list = a.sel_idx + (size_t)task * a.kmax;
+  const int cnt = min(a.sel_cnt[row], a.kmax);
+  const int32_t* list = a.sel_idx + row * a.kmax;
   const int tau = 32 * w + l32;          // this lane's query row in the block
   const int n_keys = a.view.n * nS;      // ids outside [0, n_keys) are skipped, never loaded
   uint16_t* out = (uint16_t*)a.out;
 
   if (cnt <= 0) {
     for (int e = tid; e < 128 * D / 8; e += 256) {
-      const int row = e / (D / 8), c = e % (D / 8);
-      *reinterpret_cast<uint4*>(out + out_offset(a, b, h, i, row, c * 8)) = make_uint4(0, 0, 0, 0);
+      const int trow = e / (D / 8), c = e % (D / 8);
+      *reinterpret_cast<uint4*>(out + out_offset(a, b, h, i, trow, c * 8)) = make_uint4(0, 0, 0, 0);
     }
-    if (a.lse && tid < 128) a.lse[(size_t)task * 128 + tid] = -INFINITY;
+    if (a.lse && tid < 128) a.lse[row * 128 + tid] = -INFINITY;
     return;
   }
 
-  const uint16_t* qb = (const uint16_t*)a.q_blk + (size_t)task * 128 * D;
+  const uint16_t* qb = (const uint16_t*)a.q_blk + row * 128 * D;
   bf16x8 qf[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s)
@@ -306,12 +310,12 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   constexpr int CH = D / 8;
 #pragma unroll
   for (int e0 = 0; e0 < 128 * CH; e0 += 256) {
-    const int e = e0 + tid, row = e / CH, c = e % CH;
-    *reinterpret_cast<uint4*>(out + out_offset(a, b, h, i, row, c * 8)) =
-        *reinterpret_cast<const uint4*>(st + row * (D * 2) + swz_k<D>(row, c) * 16);
+    const int e = e0 + tid, trow = e / CH, c = e % CH;
+    *reinterpret_cast<uint4*>(out + out_offset(a, b, h, i, trow, c * 8)) =
+        *reinterpret_cast<const uint4*>(st + trow * (D * 2) + swz_k<D>(trow, c) * 16);
   }
   if (a.lse && g == 0)
-    a.lse[(size_t)task * 128 + tau] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
+    a.lse[row * 128 + tau] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
 }
 
 // fp32 path: one thread per query row, scalar online softmax in chunks of 32

@@ -1,4 +1,5 @@
-"""The five LCSA workloads: shapes of the pages' 768x1408 to 4K streaming runs.
+"""The LCSA workloads: shapes of the pages' 768x1408 to 4K streaming runs and
+of the parallel (all frames at once) training forward.
 
 Token geometry ([HW] "How FlashVSR works" 5.3): one token is 16x16 output
 pixels, one block 8x8 tokens of 2 latent frames, 2 latent frames are 8 output
@@ -7,6 +8,9 @@ frames. A 768x1408 video is a 48x88 token grid; 1536x2688 is 96x168; 4K
 ([HW] 2.2 step 2). k is 20 % of a row's candidates, scaled by
 768*1280/(H*W) for the two large resolutions ([HW] 2.2, topk_ratio rule).
 The streaming cache keeps 6 latent frames = 3 temporal blocks ([HW] 2.3).
+The parallel forward takes a whole training clip at once ([FN] Key design 1:
+Stage 1 trains on 89-frame 768x1280 clips, and the student is trained on
+all frames in parallel under the block-sparse causal mask).
 """
 from __future__ import annotations
 
@@ -60,13 +64,19 @@ WORKLOADS = {
                                "6-frame KV cache)", 12, 128, "bf16", 96, 168, frames=2,
                                cache_frames=6, cap_tb=3, scale_by_resolution=True,
                                out_hw=(1536, 2688), steps=50, seed=1004),
+    # Stage-1/2 training shape: 89-frame 768x1280 clips give 23 latent frames,
+    # padded to 24 (12 temporal blocks of 6x10 blocks); every query block
+    # sees its own and all earlier temporal blocks, lists grow with the TB
+    "longT_768x1280": Workload("long-T parallel forward 768x1280 (24 latent frames x 48x80 "
+                               "tokens, block-causal over 12 temporal blocks)", 12, 128, "bf16",
+                               48, 80, frames=24, cache_frames=0, cap_tb=12, steps=10, seed=1006),
     "step_4k": Workload("streaming step 4K 2176x3840 padded (2 new latent frames x 136x240 "
                         "tokens, 6-frame KV cache)", 12, 128, "bf16", 136, 240, frames=2,
                         cache_frames=6, cap_tb=3, scale_by_resolution=True,
                         out_hw=(2176, 3840), steps=50, seed=1005),
 }
 
-ORDER = ["tiny", "cold_768x1408", "step_768x1408", "step_1536x2688", "step_4k"]
+ORDER = ["tiny", "cold_768x1408", "step_768x1408", "step_1536x2688", "step_4k", "longT_768x1280"]
 
 
 def attention_flops_per_pair(head_dim: int) -> int:

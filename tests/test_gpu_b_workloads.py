@@ -119,3 +119,19 @@ def test_streaming_step_large(dev, name):
     say(f"{name}: {stats}")
 
 
+
+
+def test_long_t_parallel_forward_768x1280(dev):
+    """The parallel training-shape forward: 24 latent frames (12 TBs) at once,
+    every query block over its own and all earlier TBs. Selections on every
+    row; outputs on rows from the first, a middle and the last TB of every
+    head (list lengths 12 to 144 blocks)."""
+    w = WORKLOADS["longT_768x1280"]
+    st = Stream(w, dev)
+    nS = w.nS
+    rows = [(0, h, i) for h in range(w.heads)
+            for i in (0, nS + 1, 5 * nS + 7, 11 * nS, 11 * nS + nS - 1)]
+    g, ref = st.step(rows=rows, want_probs=False)
+    assert sorted(set(int(x) for x in ref.kcount)) == [12 * (t + 1) for t in range(12)]
+    stats = compare_step(w, g, ref, rows=rows, check_probs=False)
+    say(f"long-T 768x1280: {stats}")
