@@ -34,7 +34,9 @@ notes of the repository):
   grid; Boundary-Truncated = the centred window clipped at the grid edge;
 * causality is at temporal-block granularity: a query block sees every key
   block whose temporal block is not later than its own;
-* the cache keeps whole temporal blocks and drops the oldest first.
+* the cache keeps whole temporal blocks and drops the oldest first;
+* Stage-1 segments are runs of whole latent frames (an image is a segment of
+  one frame); the mask is applied per token, not per block.
 
 All floating point is float64. Inputs are the exact values the GPU receives
 (bf16 or fp32), widened.
@@ -375,3 +377,52 @@ def lcsa_step(q: np.ndarray, k: np.ndarray, v: np.ndarray, cache: KVCache,
     return StepResult(out=unpartition(ob, T, H, W), lse=lse, scores=scores,
                       probs=probs, allowed=allowed, sel=sel, kcount=kcount,
                       q_pool=pq, q_blocks=qb, key_tbs=key_tbs, key_blocks=(kb, vb))
+
+
+# ------------------------------------------------------------ Stage 1 ------
+def segment_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, frame_seg,
+                      scale: float | None = None, queries=None) -> np.ndarray:
+    """Segment-masked full attention of the Stage-1 teacher.
+
+    [FN] Key design 1, Stage 1: images are treated as one-frame videos inside
+    the same 3D attention, and a block-diagonal segment mask keeps attention
+    within a segment: the weight of key token j for query token i is
+    exp(q_i k_j / sqrt(d)) * [seg(i) = seg(j)], normalised by the same sum
+    over all keys. There is no block sparsity and no causality in this stage.
+
+    q, k, v: float64 token layout [B][T][H][W][NH][D]; frame_seg: T segment
+    ids, one per latent frame (a token's segment is its frame's). Keys with
+    another segment contribute exactly zero to both sums, so each query is
+    computed over the keys of its own segment only.
+
+    queries: None for every token (returns [B][T][H][W][NH][D]), or a list
+    of (b, t, y, x) query tokens (returns [len(queries)][NH][D]).
+    """
+    B, T, H, W, NH, D = q.shape
+    seg = np.asarray(frame_seg)
+    if seg.shape != (T,):
+        raise ValueError("frame_seg needs one id per latent frame")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    L = T * H * W
+    qt, kt, vt = (x.reshape(B, L, NH, D) for x in (q, k, v))
+    tok_seg = np.repeat(seg, H * W)  # token (t, y, x) row-major -> its frame's segment
+    if queries is None:
+        qidx = [(b, n) for b in range(B) for n in range(L)]
+    else:
+        qidx = [(b, (t * H + y) * W + x) for (b, t, y, x) in queries]
+    out = np.zeros((len(qidx), NH, D))
+    by_key = {}
+    for r, (b, n) in enumerate(qidx):
+        by_key.setdefault((b, tok_seg[n]), []).append(r)
+    for (b, sg), rs in by_key.items():
+        keys = np.nonzero(tok_seg == sg)[0]
+        toks = np.array([qidx[r][1] for r in rs])
+        for h in range(NH):
+            s = (qt[b, toks, h] @ kt[b, keys, h].T) * scale
+            s = s - s.max(axis=1, keepdims=True)
+            e = np.exp(s)
+            out[rs, h] = (e / e.sum(axis=1, keepdims=True)) @ vt[b, keys, h]
+    if queries is None:
+        return out.reshape(B, T, H, W, NH, D)
+    return out
