@@ -71,9 +71,14 @@ def main():
 
     from block_sparse_attention_03_amd import lcsa as L
     from block_sparse_attention_03_amd import synth
-    from block_sparse_attention_03_amd.workloads import WORKLOADS, attention_flops_per_pair
+    from block_sparse_attention_03_amd.workloads import (WORKLOADS, attention_flops_per_pair,
+                                                         segment_pair_quarters)
 
     w = WORKLOADS[args.workload]
+    specs = [WORKLOADS[n] for n in w.layers] if w.layers else [w]
+    for sp in specs:  # the layers of a stack share the step's token geometry
+        assert (sp.heads, sp.head_dim, sp.dtype, sp.height, sp.width, sp.frames, sp.batch) == \
+            (w.heads, w.head_dim, w.dtype, w.height, w.width, w.frames, w.batch), sp.name
     K = args.steps if args.steps is not None else max(w.steps, 20)
     W = args.warmup
     dev = torch.device("cuda:0")
@@ -92,7 +97,7 @@ def main():
 
     # ---- inputs resident in HBM: cache frames + one fresh chunk per step
     n_steps = K + W
-    t_first = w.cache_frames
+    t_first = max(sp.cache_frames for sp in specs)
     t_end = t_first + w.frames * n_steps
     qkv = {}
     for name, tid in synth.TENSOR_IDS.items():
@@ -100,73 +105,113 @@ def main():
         qkv[name] = synth.field_frames_device(w.seed, tid, w.heads, w.head_dim, w.height, w.width,
                                               t0, t_end, dev, tdt, batch=w.batch)
     torch.cuda.synchronize()
-
-    cache = L.KVCache(w.batch, w.heads, w.head_dim, w.height, w.width, tdt, w.n_slots, device=dev)
-    params = L.make_params(local_range=w.local_range, border=w.border, topk_fixed=w.topk_fixed,
-                           ratio=w.ratio, scale_by_resolution=w.scale_by_resolution,
-                           out_hw=w.out_hw, ratio_base=w.ratio_base)
     geom = L.make_geom(w.batch, w.heads, w.head_dim, w.frames, w.height, w.width, code)
-    if w.cache_frames:
-        first = cache.append(w.cache_frames // 2, 0)
-        gp = L.make_geom(w.batch, w.heads, w.head_dim, w.cache_frames, w.height, w.width, code)
-        L.lcsa_partition_pool(gp, None, qkv["k"][:, :w.cache_frames], qkv["v"][:, :w.cache_frames],
-                              None, None, cache.c, first)
-
-    # buffers sized for the steady state: kmax from a metadata-only copy of
-    # the ring with the first chunk appended
-    import ctypes
-    probe = L.KvCacheStruct()
-    ctypes.memmove(ctypes.byref(probe), ctypes.byref(cache.c), ctypes.sizeof(probe))
-    tb_first = t_first // 2
-    L.lcsa_kv_cache_append(probe, w.frames // 2, tb_first)
-    kmax = L.lcsa_max_topk(geom, tb_first, probe, params)
-    bufs = L.StepBuffers(geom, kmax, device=dev)
-
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(n_steps)]
-    keep = w.cap_tb if w.cache_frames else None
+    tb_first = t_first // 2
 
-    def step(n, timed_attn=None):
+    import ctypes
+
+    class Layer:
+        """One attention layer of the step: its own ring cache, list rule
+        (draft top-k, local lists or Stage-1 segment lists) and buffers."""
+
+        def __init__(self, sp):
+            self.sp = sp
+            self.seg = list(sp.frame_seg) if sp.frame_seg else None
+            self.cache = L.KVCache(w.batch, w.heads, w.head_dim, w.height, w.width, tdt,
+                                   sp.n_slots, device=dev)
+            self.params = L.make_params(local_range=sp.local_range, border=sp.border,
+                                        topk_fixed=sp.topk_fixed, ratio=sp.ratio,
+                                        scale_by_resolution=sp.scale_by_resolution,
+                                        out_hw=sp.out_hw, ratio_base=sp.ratio_base)
+            if sp.cache_frames:
+                t0 = t_first - sp.cache_frames
+                first = self.cache.append(sp.cache_frames // 2, t0 // 2)
+                gp = L.make_geom(w.batch, w.heads, w.head_dim, sp.cache_frames, w.height,
+                                 w.width, code)
+                L.lcsa_partition_pool(gp, None, qkv["k"][:, t0:t_first], qkv["v"][:, t0:t_first],
+                                      None, None, self.cache.c, first)
+            # buffers sized for the steady state: kmax from a metadata-only
+            # copy of the ring with the first chunk appended
+            probe = L.KvCacheStruct()
+            ctypes.memmove(ctypes.byref(probe), ctypes.byref(self.cache.c), ctypes.sizeof(probe))
+            L.lcsa_kv_cache_append(probe, w.frames // 2, tb_first)
+            if self.seg:
+                self.kmax = L.lcsa_segment_max_list(geom, self.seg)
+            elif sp.lists == "local":
+                self.kmax = L.lcsa_max_candidates(geom, tb_first, probe, self.params)
+            else:
+                self.kmax = L.lcsa_max_topk(geom, tb_first, probe, self.params)
+            self.bufs = L.StepBuffers(geom, self.kmax, device=dev)
+            self.keep = sp.cap_tb if sp.cache_frames else 0  # cold chunks: empty after each step
+
+        def run(self, tb, q, k, v, ev=None):
+            c, b = self.cache, self.bufs
+            slot = c.append(w.frames // 2, tb)
+            L.lcsa_partition_pool(geom, q, k, v, b.q_blk, b.q_pool, c.c, slot, stream)
+            if self.seg:
+                L.lcsa_segment_lists(geom, tb, c.c, self.seg, self.kmax, b.sel_idx, b.sel_cnt,
+                                     stream)
+            elif self.sp.lists == "local":
+                L.lcsa_local_lists(geom, tb, c.c, self.params, self.kmax, b.sel_idx, b.sel_cnt,
+                                   stream)
+            else:
+                L.lcsa_draft_mask(geom, b.q_pool, tb, c.c, self.params, self.kmax, b.sel_idx,
+                                  b.sel_cnt, None, stream)
+            if ev is not None:
+                ev[0].record(stream)
+            if self.seg:
+                L.lcsa_segment_attn(geom, b.q_blk, tb, c.c, self.seg, b.sel_idx, b.sel_cnt,
+                                    self.kmax, b.out, None, 0.0, stream)
+            else:
+                L.lcsa_block_sparse_attn(geom, b.q_blk, c.c, b.sel_idx, b.sel_cnt, self.kmax,
+                                         b.out, None, 0.0, stream)
+            if ev is not None:
+                ev[1].record(stream)
+            c.evict(self.keep)
+
+        def flops(self):
+            fp = attention_flops_per_pair(w.head_dim)
+            if self.seg:  # only the frame pairs of a listed block pair that share a segment
+                quarters = sum(segment_pair_quarters(self.seg).values()) * w.nS * w.nS
+                return quarters * w.batch * w.heads * fp // 4
+            return int(self.bufs.sel_cnt.to(torch.int64).sum().item()) * fp
+
+    layers = [Layer(sp) for sp in specs]
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in layers] for _ in range(n_steps)]
+
+    def step(n, timed=False):
         tb = tb_first + n * (w.frames // 2)
         f0 = t_first + n * w.frames
         fq = n * w.frames
         q = qkv["q"][:, fq:fq + w.frames]
         k = qkv["k"][:, f0:f0 + w.frames]
         v = qkv["v"][:, f0:f0 + w.frames]
-        slot = cache.append(w.frames // 2, tb)
-        L.lcsa_partition_pool(geom, q, k, v, bufs.q_blk, bufs.q_pool, cache.c, slot, stream)
-        L.lcsa_draft_mask(geom, bufs.q_pool, tb, cache.c, params, kmax, bufs.sel_idx,
-                          bufs.sel_cnt, None, stream)
-        if timed_attn is not None:
-            timed_attn[0].record(stream)
-        L.lcsa_block_sparse_attn(geom, bufs.q_blk, cache.c, bufs.sel_idx, bufs.sel_cnt, kmax,
-                                 bufs.out, None, 0.0, stream)
-        if timed_attn is not None:
-            timed_attn[1].record(stream)
-        if keep is not None:
-            cache.evict(keep)
-        else:  # cold chunks: start each step from an empty cache
-            cache.evict(0)
+        for li, layer in enumerate(layers):
+            layer.run(tb, q, k, v, ev[n][li] if timed else None)
 
     for n in range(W):
         step(n)
     torch.cuda.synchronize()
-    pairs = int(bufs.sel_cnt.to(torch.int64).sum().item())
+    pairs = sum(int(la.bufs.sel_cnt.to(torch.int64).sum().item()) for la in layers)
+    flops_step = sum(la.flops() for la in layers)
 
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
     for n in range(W, W + K):
-        step(n, ev[n])
+        step(n, timed=True)
     end.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
-    attn_ms = [ev[n][0].elapsed_time(ev[n][1]) for n in range(W, W + K)]
+    # attention time of one step: its launches (one per layer), summed
+    attn_ms = [sum(e0.elapsed_time(e1) for (e0, e1) in ev[n]) for n in range(W, W + K)]
     ms_step = total_ms / K
     attn_avg = float(np.mean(attn_ms))
     flops_pair = attention_flops_per_pair(w.head_dim)
-    flops_step = pairs * flops_pair
+    kmax = max(la.kmax for la in layers)
+    seg = layers[0].seg
     value = flops_step / (ms_step * 1e-3) / 1e12
     achieved = flops_step / (attn_avg * 1e-3) / 1e12
 
@@ -195,6 +240,8 @@ def main():
         "config": {"workload": w.name, "heads": w.heads, "head_dim": w.head_dim,
                    "token_grid": [w.frames, w.height, w.width], "cache_frames": w.cache_frames,
                    "local_range": w.local_range, "selected_pairs_per_step": pairs,
+                   **({"frame_segments": seg} if seg else {}),
+                   **({"layers": list(w.layers)} if w.layers else {}),
                    "kmax": kmax, "parallelism": "single GPU"},
         "attn_ms": round(attn_avg, 4),
         "attn_ms_p10_p90": [round(float(np.percentile(attn_ms, 10)), 4),

@@ -28,6 +28,87 @@ lcsa_status device_status(hipError_t e, const char* what) {
   return ok();
 }
 
+// Stage-1 segment tables from a host array of per-frame segment ids:
+// key TBs of the chunk listed for each query TB (any frame pair shares a
+// segment) and, per (query TB, key TB), which of the four frame pairs do.
+lcsa_status segment_tables(const lcsa_geom* gq, const int32_t* frame_seg, const char* fn,
+                           int32_t n_tb[LCSA_MAX_SLOTS], int8_t tb[LCSA_MAX_SLOTS][LCSA_MAX_SLOTS],
+                           uint8_t qmask[LCSA_MAX_SLOTS][LCSA_MAX_SLOTS], int32_t* maxlen) {
+  if (!frame_seg) return fail(LCSA_ERR_NULL, "%s: frame_seg is NULL", fn);
+  const int32_t n = gq->frames / 2;
+  if (n > LCSA_MAX_SLOTS)
+    return fail(LCSA_ERR_CAPACITY, "%s: %d frames; segment attention takes at most %d", fn,
+                gq->frames, 2 * LCSA_MAX_SLOTS);
+  const int32_t nS = (gq->height / 8) * (gq->width / 8);
+  int32_t most = 0;
+  for (int32_t a = 0; a < n; ++a) {
+    n_tb[a] = 0;
+    for (int32_t p = 0; p < n; ++p) {
+      uint8_t m = 0;
+      for (int dq = 0; dq < 2; ++dq)
+        for (int dk = 0; dk < 2; ++dk)
+          if (frame_seg[2 * a + dq] == frame_seg[2 * p + dk]) m |= (uint8_t)(1u << (2 * dq + dk));
+      qmask[a][p] = m;
+      if (m) tb[a][n_tb[a]++] = (int8_t)p;
+    }
+    most = n_tb[a] > most ? n_tb[a] : most;
+  }
+  *maxlen = most * nS;
+  return ok();
+}
+
+// The segment calls take the chunk as a cold start: the cache view must be
+// exactly the chunk's temporal blocks, oldest first.
+lcsa_status check_cold_view(const lcsa_geom* gq, int64_t q_first_abs_tb,
+                            const lcsa_kv_cache* cache, const char* fn) {
+  const int32_t n = gq->frames / 2;
+  if (q_first_abs_tb < 0) return fail(LCSA_ERR_PARAM, "%s: q_first_abs_tb < 0", fn);
+  bool same = cache->count == n;
+  for (int32_t p = 0; same && p < n; ++p)
+    same = cache->abs_tb[(cache->head + p) % cache->n_slots] == q_first_abs_tb + p;
+  if (!same)
+    return fail(LCSA_ERR_PARAM,
+                "%s: the cache must hold exactly the chunk's %d temporal blocks from %lld", fn, n,
+                (long long)q_first_abs_tb);
+  return ok();
+}
+
+// Validation and argument setup shared by the two attention entry points.
+lcsa_status attn_args(const lcsa_geom* gq, const void* q_blk, const lcsa_kv_cache* cache,
+                      const int32_t* sel_idx, const int32_t* sel_cnt, int32_t kmax, float scale,
+                      void* out, float* lse, const char* fn, AttnArgs* a) {
+  lcsa_status st;
+  if ((st = check_geom(gq, fn)) || (st = check_cache(cache)) ||
+      (st = check_matches_cache(gq, cache)) || (st = check_ptr(q_blk, "q_blk")) ||
+      (st = check_ptr(sel_idx, "sel_idx")) || (st = check_ptr(sel_cnt, "sel_cnt")) ||
+      (st = check_ptr(out, "out")) || (st = check_ptr(lse, "lse", true)))
+    return st;
+  if (kmax < 1) return fail(LCSA_ERR_CAPACITY, "kmax %d < 1", kmax);
+  if (!std::isfinite(scale) || scale < 0.f)
+    return fail(LCSA_ERR_PARAM, "scale must be finite and >= 0 (0 = 1/sqrt(D))");
+  if (gq->frames > 0 && cache->count == 0)
+    return fail(LCSA_ERR_CAPACITY, "the cache holds no key blocks");
+  *a = AttnArgs{};
+  a->q_blk = q_blk;
+  a->k_ring = cache->k_ring;
+  a->v_ring = cache->v_ring;
+  a->sel_idx = sel_idx;
+  a->sel_cnt = sel_cnt;
+  a->out = out;
+  a->lse = lse;
+  a->B = gq->batch;
+  a->NH = gq->heads;
+  a->D = gq->head_dim;
+  a->T = gq->frames;
+  a->H = gq->height;
+  a->W = gq->width;
+  a->n_slots = cache->n_slots;
+  a->kmax = kmax;
+  a->view = make_view(*cache);
+  a->scale = scale == 0.f ? 1.f / std::sqrt((float)gq->head_dim) : scale;
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -159,38 +240,105 @@ lcsa_status lcsa_block_sparse_attn(const lcsa_geom* gq, const void* q_blk,
                                    const lcsa_kv_cache* cache, const int32_t* sel_idx,
                                    const int32_t* sel_cnt, int32_t kmax, float scale, void* out,
                                    float* lse, void* stream) {
+  AttnArgs a;
+  lcsa_status st = attn_args(gq, q_blk, cache, sel_idx, sel_cnt, kmax, scale, out, lse,
+                             "lcsa_block_sparse_attn", &a);
+  if (st || gq->frames == 0) return st;
+  return device_status(launch_block_sparse_attn(a, gq->dtype, false, (hipStream_t)stream),
+                       "lcsa_block_sparse_attn");
+}
+
+lcsa_status lcsa_local_lists(const lcsa_geom* gq, int64_t q_first_abs_tb,
+                             const lcsa_kv_cache* cache, const lcsa_select_params* params,
+                             int32_t kmax, int32_t* sel_idx, int32_t* sel_cnt, void* stream) {
+  const char* fn = "lcsa_local_lists";
   lcsa_status st;
-  if ((st = check_geom(gq, "lcsa_block_sparse_attn")) || (st = check_cache(cache)) ||
-      (st = check_matches_cache(gq, cache)) || (st = check_ptr(q_blk, "q_blk")) ||
-      (st = check_ptr(sel_idx, "sel_idx")) || (st = check_ptr(sel_cnt, "sel_cnt")) ||
-      (st = check_ptr(out, "out")) || (st = check_ptr(lse, "lse", true)))
+  if ((st = check_geom(gq, fn)) || (st = check_params(params)) || (st = check_cache(cache)) ||
+      (st = check_matches_cache(gq, cache)) || (st = check_ptr(sel_idx, "sel_idx")) ||
+      (st = check_ptr(sel_cnt, "sel_cnt")))
     return st;
-  if (kmax < 1) return fail(LCSA_ERR_CAPACITY, "kmax %d < 1", kmax);
-  if (!std::isfinite(scale) || scale < 0.f)
-    return fail(LCSA_ERR_PARAM, "scale must be finite and >= 0 (0 = 1/sqrt(D))");
-  if (gq->frames == 0) return ok();
-  if (cache->count == 0)
-    return fail(LCSA_ERR_CAPACITY, "the cache holds no key blocks");
-  AttnArgs a{};
-  a.q_blk = q_blk;
-  a.k_ring = cache->k_ring;
-  a.v_ring = cache->v_ring;
+  if (q_first_abs_tb < 0) return fail(LCSA_ERR_PARAM, "q_first_abs_tb < 0");
+  const int32_t ntb = gq->frames / 2;
+  if (ntb == 0) return ok();
+  if (ntb > LCSA_MAX_SLOTS)
+    return fail(LCSA_ERR_CAPACITY, "%s: a chunk of %d TBs; at most %d", fn, ntb, LCSA_MAX_SLOTS);
+  int64_t amax = 0;
+  max_topk(*gq, q_first_abs_tb, *cache, *params, &amax);
+  if (kmax < amax)
+    return fail(LCSA_ERR_CAPACITY, "%s: kmax %d is smaller than the largest list %lld", fn,
+                kmax, (long long)amax);
+  LocalListArgs a{};
   a.sel_idx = sel_idx;
   a.sel_cnt = sel_cnt;
-  a.out = out;
-  a.lse = lse;
-  a.B = gq->batch;
-  a.NH = gq->heads;
-  a.D = gq->head_dim;
-  a.T = gq->frames;
-  a.H = gq->height;
-  a.W = gq->width;
-  a.n_slots = cache->n_slots;
+  a.nby = gq->height / 8;
+  a.nbx = gq->width / 8;
+  a.nq = ntb * a.nby * a.nbx;
+  a.rows = gq->batch * gq->heads * a.nq;
   a.kmax = kmax;
-  a.view = make_view(*cache);
-  a.scale = scale == 0.f ? 1.f / std::sqrt((float)gq->head_dim) : scale;
-  return device_status(launch_block_sparse_attn(a, gq->dtype, (hipStream_t)stream),
-                       "lcsa_block_sparse_attn");
+  a.local_range = params->local_range;
+  a.border = params->border;
+  for (int32_t t = 0; t < ntb; ++t) a.n_vis[t] = visible_tbs(*cache, q_first_abs_tb + t);
+  return device_status(launch_local_lists(a, (hipStream_t)stream), fn);
+}
+
+lcsa_status lcsa_segment_max_list(const lcsa_geom* gq, const int32_t* frame_seg,
+                                  int32_t* kmax_out) {
+  lcsa_status st;
+  if ((st = check_geom(gq, "lcsa_segment_max_list"))) return st;
+  if (!kmax_out) return fail(LCSA_ERR_NULL, "kmax_out is NULL");
+  int32_t n_tb[LCSA_MAX_SLOTS];
+  int8_t tb[LCSA_MAX_SLOTS][LCSA_MAX_SLOTS];
+  uint8_t qmask[LCSA_MAX_SLOTS][LCSA_MAX_SLOTS];
+  int32_t most = 0;
+  if ((st = segment_tables(gq, frame_seg, "lcsa_segment_max_list", n_tb, tb, qmask, &most)))
+    return st;
+  *kmax_out = most;
+  return ok();
+}
+
+lcsa_status lcsa_segment_lists(const lcsa_geom* gq, int64_t q_first_abs_tb,
+                               const lcsa_kv_cache* cache, const int32_t* frame_seg,
+                               int32_t kmax, int32_t* sel_idx, int32_t* sel_cnt, void* stream) {
+  const char* fn = "lcsa_segment_lists";
+  lcsa_status st;
+  if ((st = check_geom(gq, fn)) || (st = check_cache(cache)) ||
+      (st = check_matches_cache(gq, cache)) || (st = check_ptr(sel_idx, "sel_idx")) ||
+      (st = check_ptr(sel_cnt, "sel_cnt")))
+    return st;
+  if (gq->frames == 0) return ok();
+  SegListArgs a{};
+  uint8_t qmask[LCSA_MAX_SLOTS][LCSA_MAX_SLOTS];
+  int32_t most = 0;
+  if ((st = segment_tables(gq, frame_seg, fn, a.n_tb, a.tb, qmask, &most)) ||
+      (st = check_cold_view(gq, q_first_abs_tb, cache, fn)))
+    return st;
+  if (kmax < most)
+    return fail(LCSA_ERR_CAPACITY, "%s: kmax %d is smaller than the longest list %d", fn, kmax,
+                most);
+  a.sel_idx = sel_idx;
+  a.sel_cnt = sel_cnt;
+  a.nS = (gq->height / 8) * (gq->width / 8);
+  a.nq = (gq->frames / 2) * a.nS;
+  a.rows = gq->batch * gq->heads * a.nq;
+  a.kmax = kmax;
+  return device_status(launch_segment_lists(a, (hipStream_t)stream), fn);
+}
+
+lcsa_status lcsa_segment_attn(const lcsa_geom* gq, const void* q_blk, int64_t q_first_abs_tb,
+                              const lcsa_kv_cache* cache, const int32_t* frame_seg,
+                              const int32_t* sel_idx, const int32_t* sel_cnt, int32_t kmax,
+                              float scale, void* out, float* lse, void* stream) {
+  const char* fn = "lcsa_segment_attn";
+  AttnArgs a;
+  lcsa_status st = attn_args(gq, q_blk, cache, sel_idx, sel_cnt, kmax, scale, out, lse, fn, &a);
+  if (st || gq->frames == 0) return st;
+  int32_t n_tb[LCSA_MAX_SLOTS];
+  int8_t tb[LCSA_MAX_SLOTS][LCSA_MAX_SLOTS];
+  int32_t most = 0;
+  if ((st = segment_tables(gq, frame_seg, fn, n_tb, tb, a.qmask, &most)) ||
+      (st = check_cold_view(gq, q_first_abs_tb, cache, fn)))
+    return st;
+  return device_status(launch_block_sparse_attn(a, gq->dtype, true, (hipStream_t)stream), fn);
 }
 
 }  // extern "C"

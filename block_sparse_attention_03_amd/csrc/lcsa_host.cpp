@@ -255,6 +255,21 @@ lcsa_status lcsa_max_topk(const lcsa_geom* gq, int64_t q_first_abs_tb, const lcs
 
 const char* lcsa_last_error(void) { return g_err; }
 
-int32_t lcsa_abi_version(void) { return 1; }
+lcsa_status lcsa_max_candidates(const lcsa_geom* gq, int64_t q_first_abs_tb,
+                                const lcsa_kv_cache* cache, const lcsa_select_params* params,
+                                int32_t* n_out) {
+  lcsa_status st;
+  if ((st = check_geom(gq, "lcsa_max_candidates")) || (st = check_params(params)) ||
+      (st = check_cache(cache)) || (st = check_matches_cache(gq, cache)))
+    return st;
+  if (!n_out) return fail(LCSA_ERR_NULL, "n_out is NULL");
+  int64_t amax = 0;
+  max_topk(*gq, q_first_abs_tb, *cache, *params, &amax);
+  if (amax > INT32_MAX) return fail(LCSA_ERR_CAPACITY, "more than 2^31 candidates in a row");
+  *n_out = (int32_t)amax;
+  return ok();
+}
+
+int32_t lcsa_abi_version(void) { return 2; }
 
 }  // extern "C"

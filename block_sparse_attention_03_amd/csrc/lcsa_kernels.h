@@ -59,10 +59,31 @@ struct AttnArgs {
   int32_t n_slots, kmax;
   RingView view;
   float scale;              // softmax scale on q.k
+  // segment-masked kernels only: bit 2*dq + dk of qmask[a][p] is set when
+  // frame dq of query TB a and frame dk of key view position p share a segment
+  uint8_t qmask[LCSA_MAX_SLOTS][LCSA_MAX_SLOTS];
+};
+
+struct SegListArgs {
+  int32_t* sel_idx;         // [B][NH][nq][kmax]
+  int32_t* sel_cnt;         // [B][NH][nq]
+  int32_t rows, nq, nS, kmax;
+  int32_t n_tb[LCSA_MAX_SLOTS];                 // key TBs listed for query TB a
+  int8_t tb[LCSA_MAX_SLOTS][LCSA_MAX_SLOTS];    // those TBs, ascending
+};
+
+struct LocalListArgs {
+  int32_t* sel_idx;         // [B][NH][nq][kmax]
+  int32_t* sel_cnt;         // [B][NH][nq]
+  int32_t rows, nq, nby, nbx, kmax;
+  int32_t local_range, border;
+  int32_t n_vis[LCSA_MAX_SLOTS];  // view positions visible to query TB a (a prefix)
 };
 
 hipError_t launch_partition_pool(const PartitionArgs& a, hipStream_t s);
 hipError_t launch_draft_mask(const DraftArgs& a, hipStream_t s);
-hipError_t launch_block_sparse_attn(const AttnArgs& a, int32_t dtype, hipStream_t s);
+hipError_t launch_block_sparse_attn(const AttnArgs& a, int32_t dtype, bool segment, hipStream_t s);
+hipError_t launch_segment_lists(const SegListArgs& a, hipStream_t s);
+hipError_t launch_local_lists(const LocalListArgs& a, hipStream_t s);
 
 }  // namespace lcsa

@@ -127,7 +127,10 @@ __device__ inline float partner32(float x, int g) {
 
 __device__ inline bf16x2 ones2() { return bf16x2{(__bf16)1.f, (__bf16)1.f}; }
 
-template <int D>
+// SEG: Stage-1 segment mask. Waves 0-1 hold the block's first latent frame
+// (rows 0-63), waves 2-3 the second; key half hf of a block is its frame hf.
+// A wave skips a key half whose frame is in another segment than its own.
+template <int D, bool SEG>
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   using T = Tile<D>;
   constexpr int NS = T::NS, NO = T::NO;
@@ -270,16 +273,26 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[dt][ks], pf[ks >> 1][ks & 1], o[dt], 0, 0, 0);
   };
 
+  const int qtb = i / nS;                                   // query TB (segment mask)
+  const int dq = __builtin_amdgcn_readfirstlane(w) >> 1;   // this wave's query frame
   const char *kp, *vp;
   block_base(list[0], kp, vp);
   load_subtile<D>(kp, vp, 0, lds, w, lane);
   for (int it = 0; it < cnt; ++it) {
-    const bool ok = (unsigned)list[it] < (unsigned)n_keys;  // uniform: skipped id
+    const int j = list[it];
+    const bool ok = (unsigned)j < (unsigned)n_keys;  // uniform: skipped id
+    bool ok0 = ok, ok1 = ok;
+    if constexpr (SEG) {
+      const int p = ok ? (int)(((float)j + 0.5f) * inv_ns) : 0;
+      const uint32_t m = (uint32_t)a.qmask[qtb][p] >> (2 * dq);
+      ok0 = ok && (m & 1u);
+      ok1 = ok && (m & 2u);
+    }
     // half 0 of block it is in buffer 0; fetch half 1 into buffer 1
     wait_vm_all();
     __syncthreads();
     load_subtile<D>(kp, vp, 1, lds + T::BUF, w, lane);
-    if (ok) compute_half(std::integral_constant<int, 0>{});
+    if (ok0) compute_half(std::integral_constant<int, 0>{});
     // half 1 is in buffer 1; fetch half 0 of the next block into buffer 0
     wait_vm_all();
     __syncthreads();
@@ -287,7 +300,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
       block_base(list[it + 1], kp, vp);
       load_subtile<D>(kp, vp, 0, lds, w, lane);
     }
-    if (ok) compute_half(std::integral_constant<int, 1>{});
+    if (ok1) compute_half(std::integral_constant<int, 1>{});
   }
 
   // epilogue: normalise, stage the 128 x D tile in LDS, write whole rows
@@ -320,7 +333,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
 
 // fp32 path: one thread per query row, scalar online softmax in chunks of 32
 // keys. Meant for small validation workloads, not for throughput.
-template <int D>
+template <int D, bool SEG>
 __global__ __launch_bounds__(128) void attn_f32_kernel(AttnArgs a) {
   __shared__ float ks[128 * D];   // K tile [128][D]
   __shared__ float vts[D * 128];  // V^T tile [D][128]
@@ -360,6 +373,9 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(AttnArgs a) {
     }
     __syncthreads();
     for (int c0 = 0; c0 < 128; c0 += 32) {
+      if constexpr (SEG) {  // key frame c0 / 64 against this row's frame tau / 64
+        if (!((a.qmask[i / nS][p] >> (2 * (tau >> 6) + (c0 >> 6))) & 1u)) continue;
+      }
       float sv[32];
       float mx = -INFINITY;
 #pragma unroll
@@ -390,26 +406,33 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(AttnArgs a) {
   if (a.lse) a.lse[(size_t)task * 128 + tau] = l > 0.f ? m + logf(l) : -INFINITY;
 }
 
-template <int D>
+template <int D, bool SEG>
 hipError_t launch_bf16(const AttnArgs& a, hipStream_t s) {
   const long long tasks = (long long)a.B * a.NH * (a.T / 2) * (a.H / 8) * (a.W / 8);
   const long long per = (tasks + 7) / 8;
-  hipLaunchKernelGGL(attn_bf16_kernel<D>, dim3((unsigned)(8 * per)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((attn_bf16_kernel<D, SEG>), dim3((unsigned)(8 * per)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool SEG>
 hipError_t launch_f32(const AttnArgs& a, hipStream_t s) {
   const long long tasks = (long long)a.B * a.NH * (a.T / 2) * (a.H / 8) * (a.W / 8);
-  hipLaunchKernelGGL(attn_f32_kernel<D>, dim3((unsigned)tasks), dim3(128), 0, s, a);
+  hipLaunchKernelGGL((attn_f32_kernel<D, SEG>), dim3((unsigned)tasks), dim3(128), 0, s, a);
   return hipGetLastError();
+}
+
+template <bool SEG>
+hipError_t launch(const AttnArgs& a, int32_t dtype, hipStream_t s) {
+  if (dtype == LCSA_BF16)
+    return a.D == 64 ? launch_bf16<64, SEG>(a, s) : launch_bf16<128, SEG>(a, s);
+  return a.D == 64 ? launch_f32<64, SEG>(a, s) : launch_f32<128, SEG>(a, s);
 }
 
 }  // namespace
 
-hipError_t launch_block_sparse_attn(const AttnArgs& a, int32_t dtype, hipStream_t s) {
-  if (dtype == LCSA_BF16) return a.D == 64 ? launch_bf16<64>(a, s) : launch_bf16<128>(a, s);
-  return a.D == 64 ? launch_f32<64>(a, s) : launch_f32<128>(a, s);
+hipError_t launch_block_sparse_attn(const AttnArgs& a, int32_t dtype, bool segment,
+                                    hipStream_t s) {
+  return segment ? launch<true>(a, dtype, s) : launch<false>(a, dtype, s);
 }
 
 }  // namespace lcsa

@@ -85,6 +85,13 @@ def load_library(path: str = LIB_PATH):
                             c_void_p],
         "lcsa_block_sparse_attn": [G, c_void_p, C, c_void_p, c_void_p, c_int32, c_float,
                                    c_void_p, c_void_p, c_void_p],
+        "lcsa_max_candidates": [G, c_int64, C, P, POINTER(c_int32)],
+        "lcsa_local_lists": [G, c_int64, C, P, c_int32, c_void_p, c_void_p, c_void_p],
+        "lcsa_segment_max_list": [G, POINTER(c_int32), POINTER(c_int32)],
+        "lcsa_segment_lists": [G, c_int64, C, POINTER(c_int32), c_int32, c_void_p, c_void_p,
+                               c_void_p],
+        "lcsa_segment_attn": [G, c_void_p, c_int64, C, POINTER(c_int32), c_void_p, c_void_p,
+                              c_int32, c_float, c_void_p, c_void_p, c_void_p],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -207,6 +214,53 @@ def lcsa_block_sparse_attn(geom: Geom, q_blk, cache: KvCacheStruct, sel_idx, sel
                                       _ptr(out), _ptr(lse), _stream(stream)))
 
 
+def lcsa_max_candidates(geom: Geom, q_first_abs_tb: int, cache: KvCacheStruct,
+                        params: SelectParams) -> int:
+    lib = load_library()
+    n = c_int32(-1)
+    _check(lib.lcsa_max_candidates(ctypes.byref(geom), q_first_abs_tb, ctypes.byref(cache),
+                                   ctypes.byref(params), ctypes.byref(n)))
+    return n.value
+
+
+def lcsa_local_lists(geom: Geom, q_first_abs_tb: int, cache: KvCacheStruct, params: SelectParams,
+                     kmax: int, sel_idx, sel_cnt, stream=None):
+    lib = load_library()
+    _check(lib.lcsa_local_lists(ctypes.byref(geom), q_first_abs_tb, ctypes.byref(cache),
+                                ctypes.byref(params), kmax, _ptr(sel_idx), _ptr(sel_cnt),
+                                _stream(stream)))
+
+
+def _frame_seg(frame_seg):
+    arr = (c_int32 * len(frame_seg))(*[int(x) for x in frame_seg])
+    return arr
+
+
+def lcsa_segment_max_list(geom: Geom, frame_seg) -> int:
+    lib = load_library()
+    k = c_int32(-1)
+    _check(lib.lcsa_segment_max_list(ctypes.byref(geom), _frame_seg(frame_seg), ctypes.byref(k)))
+    return k.value
+
+
+def lcsa_segment_lists(geom: Geom, q_first_abs_tb: int, cache: KvCacheStruct, frame_seg,
+                       kmax: int, sel_idx, sel_cnt, stream=None):
+    lib = load_library()
+    _check(lib.lcsa_segment_lists(ctypes.byref(geom), q_first_abs_tb, ctypes.byref(cache),
+                                  _frame_seg(frame_seg), kmax, _ptr(sel_idx), _ptr(sel_cnt),
+                                  _stream(stream)))
+
+
+def lcsa_segment_attn(geom: Geom, q_blk, q_first_abs_tb: int, cache: KvCacheStruct, frame_seg,
+                      sel_idx, sel_cnt, kmax: int, out, lse=None, scale: float = 0.0,
+                      stream=None):
+    lib = load_library()
+    _check(lib.lcsa_segment_attn(ctypes.byref(geom), _ptr(q_blk), q_first_abs_tb,
+                                 ctypes.byref(cache), _frame_seg(frame_seg), _ptr(sel_idx),
+                                 _ptr(sel_cnt), kmax, c_float(scale), _ptr(out), _ptr(lse),
+                                 _stream(stream)))
+
+
 def lcsa_last_error() -> str:
     return load_library().lcsa_last_error().decode()
 
@@ -270,23 +324,52 @@ class StepBuffers:
 
 def run_step(geom: Geom, q, k, v, cache: KVCache, first_abs_tb: int, params: SelectParams,
              bufs: StepBuffers | None = None, keep_tb: int | None = None, stream=None,
-             want_probs=False, want_lse=False, scale: float = 0.0):
-    """One LCSA invocation through the C-ABI: append, partition+pool, draft,
-    attention, evict. Returns the StepBuffers holding the results."""
+             want_probs=False, want_lse=False, scale: float = 0.0, local: bool = False):
+    """One LCSA invocation through the C-ABI: append, partition+pool, draft
+    (or, with local=True, the FlashVSR+ local lists: every allowed key
+    block), attention, evict. Returns the StepBuffers holding the results."""
     n_tb = geom.frames // 2
     first_slot = cache.append(n_tb, first_abs_tb)
-    kmax = lcsa_max_topk(geom, first_abs_tb, cache.c, params)
+    if local:
+        kmax = lcsa_max_candidates(geom, first_abs_tb, cache.c, params)
+    else:
+        kmax = lcsa_max_topk(geom, first_abs_tb, cache.c, params)
     if bufs is None:
         n_keys = cache.c.count * cache.nby * cache.nbx
         bufs = StepBuffers(geom, kmax, device=q.device,
-                           with_probs_keys=n_keys if want_probs else 0, with_lse=want_lse)
+                           with_probs_keys=n_keys if want_probs and not local else 0,
+                           with_lse=want_lse)
     lcsa_partition_pool(geom, q, k, v, bufs.q_blk, bufs.q_pool, cache.c, first_slot, stream)
-    lcsa_draft_mask(geom, bufs.q_pool, first_abs_tb, cache.c, params, bufs.kmax, bufs.sel_idx,
-                    bufs.sel_cnt, bufs.probs, stream)
+    if local:
+        lcsa_local_lists(geom, first_abs_tb, cache.c, params, bufs.kmax, bufs.sel_idx,
+                         bufs.sel_cnt, stream)
+    else:
+        lcsa_draft_mask(geom, bufs.q_pool, first_abs_tb, cache.c, params, bufs.kmax,
+                        bufs.sel_idx, bufs.sel_cnt, bufs.probs, stream)
     lcsa_block_sparse_attn(geom, bufs.q_blk, cache.c, bufs.sel_idx, bufs.sel_cnt, bufs.kmax,
                            bufs.out, bufs.lse, scale, stream)
     if keep_tb is not None:
         cache.evict(keep_tb)
+    return bufs
+
+
+def run_segment_step(geom: Geom, q, k, v, cache: KVCache, first_abs_tb: int, frame_seg,
+                     bufs: StepBuffers | None = None, stream=None, want_lse=False,
+                     scale: float = 0.0):
+    """Stage-1 segment-masked attention of one chunk through the C-ABI, as a
+    cold start: append, partition+pool, segment lists, masked attention,
+    then the cache is emptied again. Returns the StepBuffers."""
+    n_tb = geom.frames // 2
+    first_slot = cache.append(n_tb, first_abs_tb)
+    kmax = lcsa_segment_max_list(geom, frame_seg)
+    if bufs is None:
+        bufs = StepBuffers(geom, kmax, device=q.device, with_lse=want_lse)
+    lcsa_partition_pool(geom, q, k, v, bufs.q_blk, bufs.q_pool, cache.c, first_slot, stream)
+    lcsa_segment_lists(geom, first_abs_tb, cache.c, frame_seg, bufs.kmax, bufs.sel_idx,
+                       bufs.sel_cnt, stream)
+    lcsa_segment_attn(geom, bufs.q_blk, first_abs_tb, cache.c, frame_seg, bufs.sel_idx,
+                      bufs.sel_cnt, bufs.kmax, bufs.out, bufs.lse, scale, stream)
+    cache.evict(0)
     return bufs
 
 

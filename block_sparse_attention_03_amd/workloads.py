@@ -38,6 +38,9 @@ class Workload:
     steps: int = 1
     seed: int = 2026
     batch: int = 1
+    frame_seg: tuple | None = None  # Stage-1 segment id per latent frame (segment-masked path)
+    lists: str = "draft"           # "draft": top-k selection; "local": every allowed key block
+    layers: tuple = ()             # a stack of workloads run one after another per step
 
     @property
     def n_slots(self) -> int:
@@ -70,13 +73,51 @@ WORKLOADS = {
     "longT_768x1280": Workload("long-T parallel forward 768x1280 (24 latent frames x 48x80 "
                                "tokens, block-causal over 12 temporal blocks)", 12, 128, "bf16",
                                48, 80, frames=24, cache_frames=0, cap_tb=12, steps=10, seed=1006),
+    # Stage-1 joint video-image training shape: an 89-frame 768x1280 clip
+    # (23 latent frames) and one image as a one-frame segment, 24 frames
+    "stage1_768x1280": Workload("Stage-1 segment-masked attention 768x1280 (23-frame video "
+                                "segment + 1 image segment, 48x80 tokens)", 12, 128, "bf16",
+                                48, 80, frames=24, cache_frames=0, cap_tb=12, steps=10,
+                                seed=1007, frame_seg=(0,) * 23 + (1,)),
+    # FlashVSR+ hybrid attention at 4K: local layers attend every causal key
+    # block of a 3x3-block window over the current and previous TB (18 of the
+    # 2,040 valid key blocks, about 1 %); global layers keep the draft top-k
+    # over every causal key block (no spatial window), k = 20 % scaled by
+    # resolution; one global layer every 4
+    "hybrid_local_4k": Workload("FlashVSR+ local layer 4K (3x3 blocks x 2 TBs, every block)", 12,
+                                128, "bf16", 136, 240, frames=2, cache_frames=2, cap_tb=1,
+                                local_range=3, ratio=(1, 1), lists="local", steps=50, seed=1008),
+    "hybrid_global_4k": Workload("FlashVSR+ global layer 4K (draft top-k over all causal key "
+                                 "blocks)", 12, 128, "bf16", 136, 240, frames=2, cache_frames=6,
+                                 cap_tb=3, local_range=255, scale_by_resolution=True,
+                                 out_hw=(2176, 3840), steps=50, seed=1008),
+    "hybrid_4k": Workload("FlashVSR+ hybrid stack 4K (3 local layers + 1 global layer per "
+                          "step)", 12, 128, "bf16", 136, 240, frames=2, cache_frames=6, cap_tb=3,
+                          steps=30, seed=1008,
+                          layers=("hybrid_local_4k",) * 3 + ("hybrid_global_4k",)),
     "step_4k": Workload("streaming step 4K 2176x3840 padded (2 new latent frames x 136x240 "
                         "tokens, 6-frame KV cache)", 12, 128, "bf16", 136, 240, frames=2,
                         cache_frames=6, cap_tb=3, scale_by_resolution=True,
                         out_hw=(2176, 3840), steps=50, seed=1005),
 }
 
-ORDER = ["tiny", "cold_768x1408", "step_768x1408", "step_1536x2688", "step_4k", "longT_768x1280"]
+ORDER = ["tiny", "cold_768x1408", "step_768x1408", "step_1536x2688", "step_4k", "longT_768x1280",
+         "stage1_768x1280", "hybrid_local_4k", "hybrid_global_4k", "hybrid_4k"]
+
+
+def segment_pair_quarters(frame_seg) -> dict:
+    """(query TB a, key TB p) -> number of (query frame, key frame) pairs of
+    the two blocks that share a segment (0..4); each is a quarter of a
+    block pair's attention work."""
+    n = len(frame_seg) // 2
+    out = {}
+    for a in range(n):
+        for p in range(n):
+            qn = sum(frame_seg[2 * a + dq] == frame_seg[2 * p + dk]
+                     for dq in range(2) for dk in range(2))
+            if qn:
+                out[(a, p)] = qn
+    return out
 
 
 def attention_flops_per_pair(head_dim: int) -> int:

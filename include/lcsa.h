@@ -219,10 +219,74 @@ lcsa_status lcsa_block_sparse_attn(const lcsa_geom* gq, const void* q_blk,
                                    int32_t kmax, float scale, void* out, float* lse,
                                    void* stream);
 
+/* ---- FlashVSR+ local lists ----------------------------------------------- */
+
+/* [FP] "FlashVSR+" project page (flashvsr.tech), Abstract and Hybrid
+ * Attention: most DiT blocks of the hybrid student attend a compact local
+ * space-time neighbourhood, and periodic global blocks keep sparse global
+ * interaction. A local layer needs no draft: its list is every key block of
+ * the allowed set of lcsa_draft_mask (key TB not later than the query's, and
+ * inside the params->local_range window under params->border), with the k
+ * fields of params ignored; the temporal extent of the neighbourhood is the
+ * cache that the caller keeps for that layer. A global layer is
+ * lcsa_draft_mask with a window covering the whole grid. */
+
+/* Largest number of allowed key blocks over the query rows of a chunk
+ * against the TBs held by `cache`. Host only. */
+lcsa_status lcsa_max_candidates(const lcsa_geom* gq, int64_t q_first_abs_tb,
+                                const lcsa_kv_cache* cache,
+                                const lcsa_select_params* params, int32_t* n_out);
+
+/* sel_idx[i] = every allowed key block of query block i, ascending logical
+ * ids, padded with -1 up to kmax; sel_cnt[i] the count. kmax >=
+ * lcsa_max_candidates() (LCSA_ERR_CAPACITY otherwise). */
+lcsa_status lcsa_local_lists(const lcsa_geom* gq, int64_t q_first_abs_tb,
+                             const lcsa_kv_cache* cache, const lcsa_select_params* params,
+                             int32_t kmax, int32_t* sel_idx, int32_t* sel_cnt, void* stream);
+
+/* ---- Stage-1 segment-masked attention ---------------------------------- */
+
+/* [FN] Key design 1, Stage 1: images are one-frame videos in the same 3D
+ * attention, and a block-diagonal segment mask keeps every token's attention
+ * inside its own segment (weights exp(q.k/sqrt(d)) times the same-segment
+ * indicator, normalised over the same masked sum; no block sparsity, no
+ * causality). frame_seg is a HOST array of gq->frames segment ids, one per
+ * latent frame of the chunk; a token's segment is its frame's. These calls
+ * take the chunk as a cold start: the cache must hold exactly the chunk's
+ * temporal blocks, in order (view position p = temporal block
+ * q_first_abs_tb + p), else LCSA_ERR_PARAM. At most 2 * LCSA_MAX_SLOTS
+ * frames. */
+
+/* Longest segment list of the chunk: nS times the largest number of the
+ * chunk's temporal blocks that share a segment with one temporal block. The
+ * smallest kmax lcsa_segment_lists accepts. Host only. */
+lcsa_status lcsa_segment_max_list(const lcsa_geom* gq, const int32_t* frame_seg,
+                                  int32_t* kmax_out);
+
+/* For each query block i (temporal block a): sel_idx[i] = every key block of
+ * every temporal block p of the chunk with a frame in the segment of one of
+ * a's frames, ascending logical ids (p * nS + s), padded with -1 up to kmax;
+ * sel_cnt[i] the count. kmax >= lcsa_segment_max_list() (LCSA_ERR_CAPACITY
+ * otherwise). */
+lcsa_status lcsa_segment_lists(const lcsa_geom* gq, int64_t q_first_abs_tb,
+                               const lcsa_kv_cache* cache, const int32_t* frame_seg,
+                               int32_t kmax, int32_t* sel_idx, int32_t* sel_cnt,
+                               void* stream);
+
+/* Attention of lcsa_block_sparse_attn over the listed key blocks, with the
+ * token-level segment mask: key token b of a listed block is used by query
+ * token a only if frame_seg of their latent frames are equal. Layouts,
+ * scale, out and lse as in lcsa_block_sparse_attn; a query token with no
+ * usable key gets out = 0 and lse = -inf. */
+lcsa_status lcsa_segment_attn(const lcsa_geom* gq, const void* q_blk, int64_t q_first_abs_tb,
+                              const lcsa_kv_cache* cache, const int32_t* frame_seg,
+                              const int32_t* sel_idx, const int32_t* sel_cnt, int32_t kmax,
+                              float scale, void* out, float* lse, void* stream);
+
 /* Text of the last error on this thread ("" after success). */
 const char* lcsa_last_error(void);
 
-/* Interface version of this header: 1. */
+/* Interface version of this header: 2. */
 int32_t lcsa_abi_version(void);
 
 #ifdef __cplusplus

@@ -87,8 +87,9 @@ class Stream:
         q, k, v = (to_dev(d[n][0], w.dtype, self.dev) for n in "qkv")
         say(f"step frames {t0}..{t0 + w.frames} ({w.height}x{w.width}, heads {w.heads}, "
             f"D {w.head_dim}, {w.dtype})")
+        local = w.lists == "local"
         bufs = L.run_step(self.geom, q, k, v, self.gcache, tb0, self.lp, keep_tb=w.cap_tb,
-                          want_probs=want_probs, want_lse=True)
+                          want_probs=want_probs and not local, want_lse=True, local=local)
         torch.cuda.synchronize()
         g = {"sel_idx": bufs.sel_idx.cpu().numpy(), "sel_cnt": bufs.sel_cnt.cpu().numpy(),
              "out": bufs.out, "lse": bufs.lse.cpu().numpy(),

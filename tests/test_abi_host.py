@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(lib):
     assert len(names) >= 10
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.lcsa_abi_version() == 1
+    assert lib.lcsa_abi_version() == 2
 
 
 FAKE = 0x10000  # aligned, never dereferenced: validation fails first
@@ -185,3 +185,40 @@ def test_too_many_candidates_is_refused(lib):
     geom = L.make_geom(1, 1, 128, 2, 136, 240, L.LCSA_BF16)
     expect(6, L.lcsa_draft_mask, geom, _P(FAKE), 15, c, L.make_params(local_range=99, topk_fixed=1),
            4096, _P(FAKE), _P(FAKE), None, 0)
+
+
+# ------------------------------------------------------------ Stage-1 segments
+
+@pytest.mark.parametrize("seg,T,expect_tbs", [
+    ([0] * 23 + [1], 24, 12),              # 23-frame video + one image: the video spans all TBs
+    ([0, 0, 0, 0, 0, 1, 2, 3], 8, 3),      # 5-frame video + 3 images: TB 0..2 share the video
+    ([0, 1, 2, 3, 4, 5], 6, 1),            # every frame its own segment: a TB lists itself
+    ([0, 1, 0, 1], 4, 2),                  # interleaved ids: both TBs share both segments
+    ([4] * 8, 8, 4),                       # one segment: every TB
+])
+def test_segment_max_list(lib, seg, T, expect_tbs):
+    g = L.make_geom(1, 2, 128, T, 48, 80, L.LCSA_BF16)
+    assert L.lcsa_segment_max_list(g, seg) == expect_tbs * 60
+
+
+def test_segment_validation_before_any_device_call(lib):
+    g = L.make_geom(1, 2, 128, 8, 48, 80, L.LCSA_BF16)
+    seg = [0, 0, 0, 0, 0, 1, 2, 3]
+    P = type("P", (), {"data_ptr": lambda s: FAKE})()
+    c = fake_cache(nby=6, nbx=10, heads=2, n_slots=4)
+    # the cache does not yet hold the chunk
+    with pytest.raises(L.LcsaError, match="LCSA_ERR_PARAM"):
+        L.lcsa_segment_lists(g, 0, c, seg, 180, P, P, stream=0)
+    L.lcsa_kv_cache_append(c, 4, 10)
+    with pytest.raises(L.LcsaError, match="LCSA_ERR_PARAM"):   # chunk starts at TB 10, not 0
+        L.lcsa_segment_lists(g, 0, c, seg, 180, P, P, stream=0)
+    with pytest.raises(L.LcsaError, match="LCSA_ERR_CAPACITY"):  # kmax below the longest list
+        L.lcsa_segment_lists(g, 10, c, seg, 179, P, P, stream=0)
+    with pytest.raises(L.LcsaError, match="LCSA_ERR_PARAM"):
+        L.lcsa_segment_attn(g, P, 0, c, seg, P, P, 180, P, stream=0)
+    lib_ = L.load_library()
+    assert lib_.lcsa_segment_lists(ctypes.byref(g), 10, ctypes.byref(c), None, 180, FAKE, FAKE,
+                                   None) == 1  # LCSA_ERR_NULL
+    big = L.make_geom(1, 2, 128, 34, 48, 80, L.LCSA_BF16)
+    with pytest.raises(L.LcsaError, match="LCSA_ERR_CAPACITY"):
+        L.lcsa_segment_max_list(big, [0] * 34)

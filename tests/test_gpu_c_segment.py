@@ -1,0 +1,129 @@
+"""GPU parity of the Stage-1 segment-masked attention.
+
+The HIP path (partition, segment lists, masked block attention) through the
+C-ABI against the float64 oracle's token-space formula on the same seeded
+inputs. Lists are integer work and are compared exactly with their
+definition (every key block of every temporal block holding a frame of one
+of the query block's segments); outputs element by element on every token of
+every head for small cases, and on every token of sampled query blocks at
+the full 768x1280 training shape.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import pytest
+
+from block_sparse_attention_03_amd import lcsa as L
+from block_sparse_attention_03_amd import synth
+from block_sparse_attention_03_amd.workloads import WORKLOADS, Workload
+from oracle import lcsa_oracle as O
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+from gpu_harness import say, to_dev, to_host64  # noqa: E402
+from parity_util import assert_close  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    L.load_library()
+    return torch.device("cuda:0")
+
+
+def expected_lists(frame_seg, nS):
+    n = len(frame_seg) // 2
+    lists = []
+    for a in range(n):
+        tbs = [p for p in range(n)
+               if any(frame_seg[2 * a + dq] == frame_seg[2 * p + dk]
+                      for dq in range(2) for dk in range(2))]
+        lists.append([p * nS + s for p in tbs for s in range(nS)])
+    return lists
+
+
+def block_tokens(w, b, i):
+    nbx, nS = w.width // 8, w.nS
+    bt, s = divmod(i, nS)
+    by, bx = divmod(s, nbx)
+    return [(b, 2 * bt + (tau >> 6), 8 * by + ((tau >> 3) & 7), 8 * bx + (tau & 7))
+            for tau in range(128)]
+
+
+def run_case(dev, w: Workload, blocks=None, first_abs_tb=0):
+    seg = list(w.frame_seg)
+    T = w.frames
+    say(f"segment case {w.name}: T {T} {w.height}x{w.width} heads {w.heads} D {w.head_dim} "
+        f"{w.dtype} seg {seg}")
+    d = synth.make_qkv(w.seed, w.heads, w.head_dim, w.height, w.width, 0, T, dtype=w.dtype,
+                       batch=w.batch)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    code = L.LCSA_BF16 if w.dtype == "bf16" else L.LCSA_F32
+    geom = L.make_geom(w.batch, w.heads, w.head_dim, T, w.height, w.width, code)
+    cache = L.KVCache(w.batch, w.heads, w.head_dim, w.height, w.width, tdt, T // 2, device=dev)
+    q, k, v = (to_dev(d[n][0], w.dtype, dev) for n in "qkv")
+    bufs = L.run_segment_step(geom, q, k, v, cache, first_abs_tb, seg, want_lse=True)
+    torch.cuda.synchronize()
+    sel_idx, sel_cnt = bufs.sel_idx.cpu().numpy(), bufs.sel_cnt.cpu().numpy()
+    out = to_host64(bufs.out)
+    assert cache.view() == ([], [])
+
+    # lists: exact
+    nS = w.nS
+    exp = expected_lists(seg, nS)
+    kmax = sel_idx.shape[-1]
+    for b in range(w.batch):
+        for h in range(w.heads):
+            for i in range(w.nq):
+                e = exp[i // nS]
+                assert sel_cnt[b, h, i] == len(e)
+                assert list(sel_idx[b, h, i, :len(e)]) == e
+                assert (sel_idx[b, h, i, len(e):] == -1).all()
+    assert kmax == max(len(e) for e in exp)
+
+    # outputs: every token (all heads) of the chosen query blocks
+    if blocks is None:
+        blocks = [(b, i) for b in range(w.batch) for i in range(w.nq)]
+    toks = [t for (b, i) in blocks for t in block_tokens(w, b, i)]
+    ref = O.segment_attention(d["q"][1], d["k"][1], d["v"][1], seg, queries=toks)
+    got = np.stack([out[b, t, y, x] for (b, t, y, x) in toks])
+    stats = assert_close(got, ref, w.dtype)
+    # lse is finite everywhere (every token sees at least its own frame)
+    lse = bufs.lse.cpu().numpy()
+    assert np.isfinite(lse).all()
+    say(f"segment case ok: {stats}, blocks {len(blocks)}")
+    return stats
+
+
+def small(**kw) -> Workload:
+    base = dict(name="small segment", heads=2, head_dim=128, dtype="bf16", height=16,
+                width=24, frames=8, cache_frames=0, cap_tb=4, seed=91,
+                frame_seg=(0, 0, 0, 0, 0, 1, 2, 3))
+    base.update(kw)
+    return Workload(**base)
+
+
+@pytest.mark.parametrize("case", [
+    dict(),                                                            # video 5 + 3 images
+    dict(head_dim=64, frames=6, frame_seg=(0, 1, 0, 1, 0, 1)),         # interleaved ids
+    dict(frames=4, frame_seg=(3, 3, 3, 3), height=24, width=40),       # one segment
+    dict(frames=6, frame_seg=(0, 1, 2, 3, 4, 5)),                      # every frame alone
+    dict(dtype="f32", head_dim=64, frames=4, frame_seg=(0, 1, 1, 2)),  # fp32 path
+    dict(batch=2, frames=4, frame_seg=(0, 0, 0, 1)),                   # batch 2
+], ids=["video+images", "interleaved-d64", "one-segment", "per-frame", "f32", "batch2"])
+def test_segment_small_all_tokens(dev, case):
+    run_case(dev, small(**case))
+
+
+def test_segment_stage1_768x1280(dev):
+    """The full training shape: 12 heads, 24 latent frames of 48x80 tokens,
+    a 23-frame video segment and one image. Sampled query blocks: the first
+    TB, a middle TB, and the last TB (whose second frame is the image)."""
+    w = WORKLOADS["stage1_768x1280"]
+    nS = w.nS
+    blocks = [(0, 0), (0, 5 * nS + 7), (0, 11 * nS), (0, 11 * nS + nS - 1)]
+    run_case(dev, w, blocks=blocks)
