@@ -36,7 +36,9 @@ notes of the repository):
   block whose temporal block is not later than its own;
 * the cache keeps whole temporal blocks and drops the oldest first;
 * Stage-1 segments are runs of whole latent frames (an image is a segment of
-  one frame); the mask is applied per token, not per block.
+  one frame); the mask is applied per token, not per block;
+* the backward holds the top-k selection fixed (a discrete choice has no
+  gradient) and differentiates the attention over the selected pairs.
 
 All floating point is float64. Inputs are the exact values the GPU receives
 (bf16 or fp32), widened.
@@ -426,3 +428,55 @@ def segment_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, frame_seg,
     if queries is None:
         return out.reshape(B, T, H, W, NH, D)
     return out
+
+
+# ------------------------------------------------------------ backward -----
+def sparse_attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray,
+                              sel, scale: float | None = None, rows=None):
+    """Gradients of the block-sparse attention of a chunk w.r.t. q, k and v.
+
+    The forward is the attention of [FN] Key design 2 on the selected block
+    pairs: query block i attends the union of the key blocks in sel[b][h][i]
+    (ids into the chunk's own blocks, the training-shape forward where every
+    frame is computed at once). The selection is a discrete choice and is
+    held fixed; the gradient flows through the attention only. For one query
+    block with selected keys K, V (rows of their 128-token blocks):
+        P  = softmax(scale * Q K^T)          (row-wise)
+        dV += P^T dO        dP = dO V^T
+        dS = P * (dP - rowsum(P * dP))       (softmax Jacobian, row-wise)
+        dQ = scale * dS K   dK += scale * dS^T Q
+
+    q, k, v, dout: float64 token layout [B][T][H][W][NH][D]; sel: [B][NH]
+    lists of per-row ascending key ids. rows: None for every row, or a set of
+    (b, h, i) rows whose terms are computed (dq of the other rows stays 0,
+    and dk / dv hold only the listed rows' contributions).
+    Returns (dq, dk, dv) in block layout [B][NH][nblk][128][D].
+    """
+    B, T, H, W, NH, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    qb, kb, vb, gb = partition(q), partition(k), partition(v), partition(dout)
+    nq = qb.shape[2]
+    dq, dk, dv = np.zeros_like(qb), np.zeros_like(kb), np.zeros_like(vb)
+    want = None if rows is None else set(map(tuple, rows))
+    for b in range(B):
+        for h in range(NH):
+            for i in range(nq):
+                ids = list(sel[b][h][i])
+                if not ids or (want is not None and (b, h, i) not in want):
+                    continue
+                K = kb[b, h, ids].reshape(-1, D)
+                V = vb[b, h, ids].reshape(-1, D)
+                Q, dO = qb[b, h, i], gb[b, h, i]
+                logits = (Q @ K.T) * scale
+                e = np.exp(logits - logits.max(axis=1, keepdims=True))
+                P = e / e.sum(axis=1, keepdims=True)
+                dP = dO @ V.T
+                dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+                dq[b, h, i] = scale * (dS @ K)
+                gK = scale * (dS.T @ Q)
+                gV = P.T @ dO
+                for n, j in enumerate(ids):
+                    dk[b, h, j] += gK[n * BLOCK_TOKENS:(n + 1) * BLOCK_TOKENS]
+                    dv[b, h, j] += gV[n * BLOCK_TOKENS:(n + 1) * BLOCK_TOKENS]
+    return dq, dk, dv
