@@ -72,6 +72,7 @@ def main():
     from block_sparse_attention_03_amd import lcsa as L
     from block_sparse_attention_03_amd import synth
     from block_sparse_attention_03_amd.workloads import (WORKLOADS, attention_flops_per_pair,
+                                                         backward_flops_per_pair,
                                                          segment_pair_quarters)
 
     w = WORKLOADS[args.workload]
@@ -142,10 +143,18 @@ def main():
                 self.kmax = L.lcsa_max_candidates(geom, tb_first, probe, self.params)
             else:
                 self.kmax = L.lcsa_max_topk(geom, tb_first, probe, self.params)
-            self.bufs = L.StepBuffers(geom, self.kmax, device=dev)
+            self.bufs = L.StepBuffers(geom, self.kmax, device=dev, with_lse=sp.backward)
             self.keep = sp.cap_tb if sp.cache_frames else 0  # cold chunks: empty after each step
+            if sp.backward:  # training shape: the keys are the chunk's own blocks
+                assert sp.cache_frames == 0 and not self.seg
+                self.dout = synth.field_frames_device(w.seed, synth.FIELD_IDS["dout"], w.heads,
+                                                      w.head_dim, w.height, w.width, 0, w.frames,
+                                                      dev, tdt, batch=w.batch)
+                self.ws = torch.empty(L.lcsa_attn_bwd_workspace_size(geom), dtype=torch.uint8,
+                                      device=dev)
+                self.grads = [torch.empty_like(self.dout) for _ in range(3)]
 
-        def run(self, tb, q, k, v, ev=None):
+        def run(self, tb, q, k, v, ev=None, evb=None):
             c, b = self.cache, self.bufs
             slot = c.append(w.frames // 2, tb)
             L.lcsa_partition_pool(geom, q, k, v, b.q_blk, b.q_pool, c.c, slot, stream)
@@ -165,9 +174,17 @@ def main():
                                     self.kmax, b.out, None, 0.0, stream)
             else:
                 L.lcsa_block_sparse_attn(geom, b.q_blk, c.c, b.sel_idx, b.sel_cnt, self.kmax,
-                                         b.out, None, 0.0, stream)
+                                         b.out, b.lse, 0.0, stream)
             if ev is not None:
                 ev[1].record(stream)
+            if self.sp.backward:
+                if evb is not None:
+                    evb[0].record(stream)
+                L.lcsa_block_sparse_attn_bwd(geom, q, k, v, b.out, self.dout, b.lse, b.sel_idx,
+                                             b.sel_cnt, self.kmax, *self.grads, self.ws,
+                                             stream=stream)
+                if evb is not None:
+                    evb[1].record(stream)
             c.evict(self.keep)
 
         def flops(self):
@@ -175,11 +192,15 @@ def main():
             if self.seg:  # only the frame pairs of a listed block pair that share a segment
                 quarters = sum(segment_pair_quarters(self.seg).values()) * w.nS * w.nS
                 return quarters * w.batch * w.heads * fp // 4
-            return int(self.bufs.sel_cnt.to(torch.int64).sum().item()) * fp
+            pairs = int(self.bufs.sel_cnt.to(torch.int64).sum().item())
+            return pairs * (fp + (backward_flops_per_pair(w.head_dim) if self.sp.backward else 0))
 
     layers = [Layer(sp) for sp in specs]
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in layers] for _ in range(n_steps)]
+
+    evb = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in layers] for _ in range(n_steps)]
 
     def step(n, timed=False):
         tb = tb_first + n * (w.frames // 2)
@@ -189,7 +210,7 @@ def main():
         k = qkv["k"][:, f0:f0 + w.frames]
         v = qkv["v"][:, f0:f0 + w.frames]
         for li, layer in enumerate(layers):
-            layer.run(tb, q, k, v, ev[n][li] if timed else None)
+            layer.run(tb, q, k, v, ev[n][li] if timed else None, evb[n][li] if timed else None)
 
     for n in range(W):
         step(n)
@@ -207,6 +228,11 @@ def main():
     total_ms = start.elapsed_time(end)
     # attention time of one step: its launches (one per layer), summed
     attn_ms = [sum(e0.elapsed_time(e1) for (e0, e1) in ev[n]) for n in range(W, W + K)]
+    has_bwd = any(la.sp.backward for la in layers)
+    if has_bwd:  # the attention of a training step: forward and backward launches
+        bwd_ms = [sum(e0.elapsed_time(e1) for (e0, e1), la in zip(evb[n], layers)
+                      if la.sp.backward) for n in range(W, W + K)]
+        attn_ms = [a + b_ for a, b_ in zip(attn_ms, bwd_ms)]
     ms_step = total_ms / K
     attn_avg = float(np.mean(attn_ms))
     flops_pair = attention_flops_per_pair(w.head_dim)
@@ -244,6 +270,7 @@ def main():
                    **({"layers": list(w.layers)} if w.layers else {}),
                    "kmax": kmax, "parallelism": "single GPU"},
         "attn_ms": round(attn_avg, 4),
+        **({"bwd_ms": round(float(np.mean(bwd_ms)), 4)} if has_bwd else {}),
         "attn_ms_p10_p90": [round(float(np.percentile(attn_ms, 10)), 4),
                             round(float(np.percentile(attn_ms, 90)), 4)],
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,

@@ -18,7 +18,7 @@ ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
 
 HIP_SOURCES = ["lcsa_api.hip", "partition_pool.hip", "draft_mask.hip", "sparse_attn.hip",
-               "fixed_lists.hip"]
+               "fixed_lists.hip", "attn_bwd.hip"]
 CXX_SOURCES = ["lcsa_host.cpp"]
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-Wall",
              # keep hand-written float code off the packed-fp32 instructions

@@ -1,0 +1,477 @@
+// Backward of the block-sparse attention: dQ, dK, dV over the same lists.
+//
+// [FN] "FlashVSR" note, Key design 2 computes full 128 x 128 attention on
+// the selected block pairs only; Key design 1 trains the student on all
+// frames of a clip in parallel under the block-sparse causal mask. The
+// selection is a discrete choice and is held fixed: the gradient is that of
+// softmax attention over the listed blocks. Per query block i with listed
+// keys (rows of their blocks):
+//   P = exp(scale Q K^T - lse)       (the forward's log-sum-exp)
+//   dV += P^T dO     dP = dO V^T     dS = P * (dP - delta),  delta = rowsum(dO * O)
+//   dQ = scale dS K  dK += scale dS^T Q
+// This is the training-shape backward: keys are the chunk's own blocks, and
+// q, k, v, O, dO and the gradients are in the token layout.
+//
+// Four kernels, all bf16 on the gfx950 matrix cores (v_mfma_f32_32x32x16_bf16,
+// float32 accumulation):
+//  * prep:  per (block, head) the transposed tiles Q^T, K^T, dO^T ([D][128])
+//           and delta, into the workspace;
+//  * inverse lists: for each key block, the query blocks whose list holds
+//           it, ascending (binary search in the sorted lists, wave ballot),
+//           so dK / dV need no atomics and are deterministic;
+//  * dQ:    one workgroup per query block, walking its list;
+//           S^T = K Q^T and dP^T = V dO^T (A = K, V rows from LDS, B = Q, dO
+//           rows in registers), then dQ^T += K^T dS^T (A = K^T rows from LDS,
+//           B = dS^T straight from the accumulators);
+//  * dK/dV: one workgroup per key block, walking its inverse list;
+//           S = Q K^T and dP = dO V^T (A = Q, dO rows from LDS, B = K, V rows
+//           in registers), then dV^T += dO^T P and dK^T += Q^T dS (A = the
+//           transposed tiles from LDS, B = P, dS from the accumulators).
+// As in the forward, the rows of the first products' A operands are read in
+// a permuted order so that each lane's accumulator values form the 8
+// contiguous k-elements of the next product's B fragment. Tiles are staged
+// in 32-row quarters, double-buffered in LDS with direct global->LDS loads,
+// and rows are XOR-swizzled in 16-byte chunks (conflict-free fragment reads).
+#include "lcsa_kernels.h"
+
+namespace lcsa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// XOR swizzles of 16-byte chunk c in LDS rows of 256, 128 and 64 bytes: 16
+// consecutive rows read at one logical chunk hit 16 different bank groups.
+// Involutions: the same map goes logical -> physical and back.
+__device__ inline int swz16(int row, int c) { return c ^ (row & 15); }
+__device__ inline int swz8(int row, int c) { return c ^ ((row >> 1) & 7); }
+__device__ inline int swz4(int row, int c) { return c ^ ((row >> 2) & 3); }
+template <int D>
+__device__ inline int swz_row(int row, int c) {  // rows of D bf16
+  if constexpr (D == 128) return swz16(row, c);
+  else return swz8(row, c);
+}
+
+// Row order of a 32-row A operand whose product feeds the next MFMA as B:
+// lane (l, g) of a 32x32 accumulator holds rows 8i + 4g + j; reading source
+// row perm(r) into A row r makes them the source rows 16*(i/2) + 8g +
+// 4*(i%2) + j, so accumulator elements 8ks .. 8ks+7 are source rows
+// 16ks + 8g .. 16ks + 8g + 7: one B fragment of k-step ks.
+__device__ inline int perm32(int r) {
+  const int i = r >> 3, gg = (r >> 2) & 1, j = r & 3;
+  return 16 * (i >> 1) + 8 * gg + 4 * (i & 1) + j;
+}
+
+__device__ inline void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+template <int D>
+struct Q4 {                                   // one 32-row quarter of a block
+  static constexpr int ROWB = 32 * D * 2;     // [32][D] row tile bytes
+  static constexpr int TRB = D * 32 * 2;      // [D][32] transposed tile bytes
+  static constexpr int KCH = D / 8;           // 16-byte chunks per row
+  static constexpr int NS = D / 16;           // k-steps over D
+  static constexpr int NO = D / 32;           // 32-row tiles over D
+  static constexpr int RLD = ROWB / 4096;     // 1 KB loads per wave for a row tile
+  static constexpr int TLD = TRB / 4096;      // and for a transposed tile
+};
+
+// Geometry of a chunk-relative block n and its token tau in the token layout.
+struct Tok {
+  int T, H, W, NH, D, nbx, nS;
+  __device__ size_t off(int b, int h, int n, int tau) const {
+    const int bt = n / nS, s = n - bt * nS, by = s / nbx, bx = s - by * nbx;
+    const int t = 2 * bt + (tau >> 6), y = 8 * by + ((tau >> 3) & 7), x = 8 * bx + (tau & 7);
+    return ((((size_t)b * T + t) * H + y) * W + x) * NH * D + (size_t)h * D;
+  }
+};
+
+__device__ inline Tok make_tok(const BwdArgs& a) {
+  Tok t;
+  t.T = a.T;
+  t.H = a.H;
+  t.W = a.W;
+  t.NH = a.NH;
+  t.D = a.D;
+  t.nbx = a.W / 8;
+  t.nS = (a.H / 8) * t.nbx;
+  return t;
+}
+
+// Direct loads of rows r0 .. r0+31 of block n (token layout) into a [32][D]
+// swizzled LDS tile; each wave instruction fills 1 KB, lane l at +16 l.
+template <int D>
+__device__ __forceinline__ void load_rows(const Tok& tk, const char* src, int b, int h, int n,
+                                          int r0, char* dst, int w, int lane) {
+  using G = Q4<D>;
+#pragma unroll
+  for (int it = 0; it < G::RLD; ++it) {
+    const int u = (it * 4 + w) * 64 + lane;
+    const int row = u / G::KCH, c = swz_row<D>(row, u % G::KCH);
+    const char* p = src + (tk.off(b, h, n, r0 + row) + c * 8) * 2;
+    __builtin_amdgcn_global_load_lds(p, LDS_PTR(dst + (it * 4 + w) * 1024), 16, 0, 0);
+  }
+}
+
+// Direct loads of columns c0 .. c0+31 of a [D][128] transposed block into a
+// [D][32] swizzled LDS tile.
+template <int D>
+__device__ __forceinline__ void load_cols(const char* blk, int c0, char* dst, int w, int lane) {
+  using G = Q4<D>;
+#pragma unroll
+  for (int it = 0; it < G::TLD; ++it) {
+    const int u = (it * 4 + w) * 64 + lane;
+    const int d = u >> 2, c = swz4(d, u & 3);
+    const char* p = blk + ((size_t)d * 128 + c0 + c * 8) * 2;
+    __builtin_amdgcn_global_load_lds(p, LDS_PTR(dst + (it * 4 + w) * 1024), 16, 0, 0);
+  }
+}
+
+// B fragments of 32 rows (this wave's rows 32w + l32) of block n: D values
+// per row, 8 per k-step, straight into registers.
+template <int D>
+__device__ __forceinline__ void row_frags(const Tok& tk, const void* src, int b, int h, int n,
+                                          int row, int g, bf16x8 (&f)[Q4<D>::NS]) {
+  const __bf16* p = (const __bf16*)src + tk.off(b, h, n, row);
+#pragma unroll
+  for (int s = 0; s < Q4<D>::NS; ++s) f[s] = *reinterpret_cast<const bf16x8*>(p + 16 * s + 8 * g);
+}
+
+// Write a D x 32 accumulator (rows d, column = this lane's row 32w + l32)
+// times `mul` to rows of block n in the token layout, through an LDS stage
+// of [128][D] bf16 so the stores are whole 16-byte chunks of a row.
+template <int D>
+__device__ __forceinline__ void store_rows(const Tok& tk, void* dst, int b, int h, int n,
+                                           const f32x16 (&acc)[Q4<D>::NO], float mul, char* st,
+                                           int w, int l32, int g, int tid) {
+  constexpr int NO = Q4<D>::NO, CH = D / 8;
+  const int tau = 32 * w + l32;
+#pragma unroll
+  for (int dt = 0; dt < NO; ++dt)
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      __bf16 v4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v4[j] = (__bf16)(acc[dt][4 * ii + j] * mul);
+      const int c = 4 * dt + ii;  // chunk of d = 32dt + 8ii .. +8; this lane's half at +8g
+      *reinterpret_cast<uint2*>(st + tau * (D * 2) + swz_row<D>(tau, c) * 16 + 8 * g) =
+          *reinterpret_cast<const uint2*>(v4);
+    }
+  __syncthreads();
+  uint16_t* o = (uint16_t*)dst;
+#pragma unroll
+  for (int e0 = 0; e0 < 128 * CH; e0 += 256) {
+    const int e = e0 + tid, row = e / CH, c = e % CH;
+    *reinterpret_cast<uint4*>(o + tk.off(b, h, n, row) + c * 8) =
+        *reinterpret_cast<const uint4*>(st + row * (D * 2) + swz_row<D>(row, c) * 16);
+  }
+}
+
+// ---------------------------------------------------------------- prep ----
+// One workgroup per (block, head), heads fastest. Transposes q, k and dO of
+// the block into [D][128] tiles through one LDS stage and computes delta.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
+  constexpr int CPT = D / 8, ITERS = 128 * CPT / 256, TPI = 256 / CPT, PITCH = D * 2 + 16;
+  __shared__ __attribute__((aligned(16))) char stage[128 * PITCH];
+  const Tok tk = make_tok(a);
+  const int nq = (a.T / 2) * tk.nS;
+  const int h = blockIdx.x % a.NH, n = (blockIdx.x / a.NH) % nq, b = blockIdx.x / (a.NH * nq);
+  const size_t blk = ((size_t)b * a.NH + h) * nq + n;
+  const int tid = threadIdx.x, c = tid % CPT, tsub = tid / CPT;
+
+  // delta: each token's CPT chunks sit on CPT consecutive lanes
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    const int tau = it * TPI + tsub;
+    const size_t o = tk.off(b, h, n, tau) + c * 8;
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>((const __bf16*)a.dout + o);
+    const bf16x8 y = *reinterpret_cast<const bf16x8*>((const __bf16*)a.out + o);
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s = fmaf((float)x[e], (float)y[e], s);
+#pragma unroll
+    for (int m = 1; m < CPT; m <<= 1) s += __shfl_xor(s, m, 64);
+    if (c == 0) a.delta[blk * 128 + tau] = s;
+  }
+
+  const void* srcs[3] = {a.q, a.k, a.dout};
+  void* dsts[3] = {a.qT, a.kT, a.doT};
+#pragma unroll
+  for (int tI = 0; tI < 3; ++tI) {
+    const char* src = (const char*)srcs[tI];
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      const int tau = it * TPI + tsub;
+      *reinterpret_cast<u32x4*>(stage + tau * PITCH + c * 16) =
+          *reinterpret_cast<const u32x4*>(src + (tk.off(b, h, n, tau) + c * 8) * 2);
+    }
+    __syncthreads();
+    char* dst = (char*)dsts[tI] + blk * (size_t)D * 128 * 2;
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {  // [D][128]: 16 chunks of 8 tokens per row d
+      const int e = it * 256 + tid, d = e / 16, kc = e % 16;
+      uint32_t wv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t lo = *reinterpret_cast<const uint16_t*>(stage + (kc * 8 + 2 * u) * PITCH + d * 2);
+        const uint32_t hi = *reinterpret_cast<const uint16_t*>(stage + (kc * 8 + 2 * u + 1) * PITCH + d * 2);
+        wv[u] = lo | (hi << 16);
+      }
+      *reinterpret_cast<u32x4*>(dst + ((size_t)d * 128 + kc * 8) * 2) = u32x4{wv[0], wv[1], wv[2], wv[3]};
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------- inverse lists ----
+// One wave per (b, h, key block j): scan the query rows in order, binary
+// search j in each row's ascending list, compact the hits with a ballot.
+__global__ __launch_bounds__(64) void inverse_lists_kernel(BwdArgs a) {
+  const int nq = (a.T / 2) * (a.H / 8) * (a.W / 8);
+  const int j = blockIdx.x % nq, bh = blockIdx.x / nq;
+  const int lane = threadIdx.x;
+  int base = 0;
+  int32_t* dst = a.inv_idx + ((size_t)bh * nq + j) * nq;
+  for (int i0 = 0; i0 < nq; i0 += 64) {
+    const int i = i0 + lane;
+    bool hit = false;
+    if (i < nq) {
+      const size_t row = (size_t)bh * nq + i;
+      const int32_t* list = a.sel_idx + row * a.kmax;
+      int lo = 0, hi = min(a.sel_cnt[row], a.kmax) - 1;
+      while (lo <= hi) {
+        const int mid = (lo + hi) >> 1;
+        const int v = list[mid];
+        if (v == j) {
+          hit = true;
+          break;
+        }
+        if ((unsigned)v < (unsigned)j) lo = mid + 1;  // -1 never sits before a valid id
+        else hi = mid - 1;
+      }
+    }
+    const uint64_t m = __ballot(hit);
+    if (hit) dst[base + __popcll(m & ((1ull << lane) - 1))] = i;
+    base += __popcll(m);
+  }
+  if (lane == 0) a.inv_cnt[(size_t)bh * nq + j] = base;
+}
+
+// ------------------------------------------------------------------ dQ ----
+template <int D>
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
+  using G = Q4<D>;
+  constexpr int NS = G::NS, NO = G::NO;
+  constexpr int BUF = 2 * G::ROWB + G::TRB;  // K rows, V rows, K^T columns
+  __shared__ __attribute__((aligned(16))) char lds[2 * BUF > 128 * D * 2 ? 2 * BUF : 128 * D * 2];
+
+  const Tok tk = make_tok(a);
+  const int nS = tk.nS, nq = (a.T / 2) * nS, n_tasks = a.B * a.NH * nq;
+  const int per = (n_tasks + 7) / 8;
+  const int task = (blockIdx.x & 7) * per + (blockIdx.x >> 3);  // XCD-contiguous
+  if (task >= n_tasks) return;
+  const int r = task % nq, n_tb = a.T / 2;
+  const int i = (n_tb - 1 - r / nS) * nS + r % nS;  // longest lists (latest TBs) first
+  const int bh = task / nq, h = bh % a.NH, b = bh / a.NH;
+  const size_t row = (size_t)bh * nq + i;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+  const int cnt = min(a.sel_cnt[row], a.kmax);
+  const int32_t* list = a.sel_idx + row * a.kmax;
+
+  f32x16 acc[NO];
+#pragma unroll
+  for (int t = 0; t < NO; ++t)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[t][e] = 0.f;
+
+  if (cnt > 0) {
+    bf16x8 qf[NS], of[NS];
+    row_frags<D>(tk, a.q, b, h, i, 32 * w + l32, g, qf);
+    row_frags<D>(tk, a.dout, b, h, i, 32 * w + l32, g, of);
+    const float sl2 = a.scale * kLog2e;
+    const float lse2 = a.lse[row * 128 + 32 * w + l32] * kLog2e;
+    const float dlt = a.delta[row * 128 + 32 * w + l32];
+    const int prow = perm32(l32);
+    const int total = 4 * cnt;  // quarters of 32 keys
+    auto issue = [&](int qi, char* buf) {
+      int j = list[qi >> 2];
+      j = (unsigned)j < (unsigned)nq ? j : 0;  // an invalid id loads block 0, then is skipped
+      const int k0 = 32 * (qi & 3);
+      load_rows<D>(tk, (const char*)a.k, b, h, j, k0, buf, w, lane);
+      load_rows<D>(tk, (const char*)a.v, b, h, j, k0, buf + G::ROWB, w, lane);
+      load_cols<D>((const char*)a.kT + ((size_t)bh * nq + j) * D * 128 * 2, k0,
+                   buf + 2 * G::ROWB, w, lane);
+    };
+    issue(0, lds);
+    for (int qi = 0; qi < total; ++qi) {
+      char* cur = lds + (qi & 1) * BUF;
+      wait_vm_all();
+      __syncthreads();
+      if (qi + 1 < total) issue(qi + 1, lds + ((qi + 1) & 1) * BUF);
+      if ((unsigned)list[qi >> 2] >= (unsigned)nq) continue;  // uniform: skipped id
+      const char* kr = cur;
+      const char* vr = cur + G::ROWB;
+      const char* kt = cur + 2 * G::ROWB;
+      f32x16 st, dp;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) st[e] = dp[e] = 0.f;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int off = prow * (D * 2) + swz_row<D>(prow, 2 * s + g) * 16;
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(kr + off),
+                                                     qf[s], st, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(vr + off),
+                                                     of[s], dp, 0, 0, 0);
+      }
+      bf16x8 ds[2];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(st[e], sl2, -lse2));
+        ds[e >> 3][e & 7] = (__bf16)(p * (dp[e] - dlt));
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int dt = 0; dt < NO; ++dt) {
+          const int d = 32 * dt + l32;
+          const bf16x8 af = *reinterpret_cast<const bf16x8*>(kt + d * 64 + swz4(d, 2 * ks + g) * 16);
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, ds[ks], acc[dt], 0, 0, 0);
+        }
+    }
+  }
+  __syncthreads();
+  store_rows<D>(tk, a.dq, b, h, i, acc, a.scale, lds, w, l32, g, tid);
+}
+
+// --------------------------------------------------------------- dK / dV ----
+template <int D>
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
+  using G = Q4<D>;
+  constexpr int NS = G::NS, NO = G::NO;
+  // Q rows, dO rows, Q^T columns, dO^T columns, then 1 KB for lse2 / delta
+  constexpr int BUF = 2 * G::ROWB + 2 * G::TRB + 1024;
+  __shared__ __attribute__((aligned(16))) char lds[2 * BUF > 128 * D * 2 ? 2 * BUF : 128 * D * 2];
+
+  const Tok tk = make_tok(a);
+  const int nS = tk.nS, nq = (a.T / 2) * nS, n_tasks = a.B * a.NH * nq;
+  const int per = (n_tasks + 7) / 8;
+  const int task = (blockIdx.x & 7) * per + (blockIdx.x >> 3);  // XCD-contiguous
+  if (task >= n_tasks) return;
+  const int j = task % nq;  // key TBs ascending: the earliest keys have the longest lists
+  const int bh = task / nq, h = bh % a.NH, b = bh / a.NH;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+  const size_t kj = (size_t)bh * nq + j;
+  const int cnt = min(a.inv_cnt[kj], nq);
+  const int32_t* inv = a.inv_idx + kj * nq;
+
+  f32x16 dk[NO], dv[NO];
+#pragma unroll
+  for (int t = 0; t < NO; ++t)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dk[t][e] = dv[t][e] = 0.f;
+
+  if (cnt > 0) {
+    bf16x8 kf[NS], vf[NS];
+    row_frags<D>(tk, a.k, b, h, j, 32 * w + l32, g, kf);
+    row_frags<D>(tk, a.v, b, h, j, 32 * w + l32, g, vf);
+    const float sl2 = a.scale * kLog2e;
+    const int prow = perm32(l32);
+    const int total = 4 * cnt;  // quarters of 32 queries
+    auto issue = [&](int qi, char* buf) {
+      const int i = inv[qi >> 2], q0 = 32 * (qi & 3);
+      const size_t qrow = (size_t)bh * nq + i;
+      load_rows<D>(tk, (const char*)a.q, b, h, i, q0, buf, w, lane);
+      load_rows<D>(tk, (const char*)a.dout, b, h, i, q0, buf + G::ROWB, w, lane);
+      load_cols<D>((const char*)a.qT + qrow * D * 128 * 2, q0, buf + 2 * G::ROWB, w, lane);
+      load_cols<D>((const char*)a.doT + qrow * D * 128 * 2, q0, buf + 2 * G::ROWB + G::TRB, w,
+                   lane);
+      if (w == 0) {  // lanes 0-7: lse of the 32 queries, 8-15: delta, the rest repeat them
+        const int u = lane & 15;
+        const char* p = u < 8 ? (const char*)(a.lse + qrow * 128 + q0) + 16 * u
+                              : (const char*)(a.delta + qrow * 128 + q0) + 16 * (u - 8);
+        __builtin_amdgcn_global_load_lds(p, LDS_PTR(buf + 2 * G::ROWB + 2 * G::TRB), 16, 0, 0);
+      }
+    };
+    issue(0, lds);
+    for (int qi = 0; qi < total; ++qi) {
+      char* cur = lds + (qi & 1) * BUF;
+      wait_vm_all();
+      __syncthreads();
+      if (qi + 1 < total) issue(qi + 1, lds + ((qi + 1) & 1) * BUF);
+      const char* qr = cur;
+      const char* orr = cur + G::ROWB;
+      const char* qt = cur + 2 * G::ROWB;
+      const char* ot = qt + G::TRB;
+      const float* ld = (const float*)(ot + G::TRB);  // [0, 32) lse, [32, 64) delta
+      f32x16 st, dp;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) st[e] = dp[e] = 0.f;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int off = prow * (D * 2) + swz_row<D>(prow, 2 * s + g) * 16;
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(qr + off),
+                                                     kf[s], st, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(orr + off),
+                                                     vf[s], dp, 0, 0, 0);
+      }
+      // element 8ks + e is query 16ks + 8g + e of the quarter
+      bf16x8 pb[2], dsb[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int q = 16 * ks + 8 * g;
+        const f32x4 l0 = *reinterpret_cast<const f32x4*>(ld + q);
+        const f32x4 l1 = *reinterpret_cast<const f32x4*>(ld + q + 4);
+        const f32x4 d0 = *reinterpret_cast<const f32x4*>(ld + 32 + q);
+        const f32x4 d1 = *reinterpret_cast<const f32x4*>(ld + 32 + q + 4);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float lse = e < 4 ? l0[e] : l1[e - 4];
+          const float dl = e < 4 ? d0[e] : d1[e - 4];
+          const float p = __builtin_amdgcn_exp2f(fmaf(st[8 * ks + e], sl2, -lse * kLog2e));
+          pb[ks][e] = (__bf16)p;
+          dsb[ks][e] = (__bf16)(p * (dp[8 * ks + e] - dl));
+        }
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int dt = 0; dt < NO; ++dt) {
+          const int d = 32 * dt + l32;
+          const int off = d * 64 + swz4(d, 2 * ks + g) * 16;
+          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(ot + off),
+                                                           pb[ks], dv[dt], 0, 0, 0);
+          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(qt + off),
+                                                           dsb[ks], dk[dt], 0, 0, 0);
+        }
+    }
+  }
+  __syncthreads();
+  store_rows<D>(tk, a.dk, b, h, j, dk, a.scale, lds, w, l32, g, tid);
+  __syncthreads();
+  store_rows<D>(tk, a.dv, b, h, j, dv, 1.f, lds, w, l32, g, tid);
+}
+
+template <int D>
+hipError_t launch(const BwdArgs& a, hipStream_t s) {
+  const long long nq = (long long)(a.T / 2) * (a.H / 8) * (a.W / 8);
+  const long long tasks = (long long)a.B * a.NH * nq;
+  const long long grid = 8 * ((tasks + 7) / 8);
+  hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)tasks), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(inverse_lists_kernel, dim3((unsigned)tasks), dim3(64), 0, s, a);
+  hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_bwd(const BwdArgs& a, hipStream_t s) {
+  return a.D == 64 ? launch<64>(a, s) : launch<128>(a, s);
+}
+
+}  // namespace lcsa

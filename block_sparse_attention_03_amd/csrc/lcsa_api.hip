@@ -109,6 +109,27 @@ lcsa_status attn_args(const lcsa_geom* gq, const void* q_blk, const lcsa_kv_cach
   return ok();
 }
 
+// Workspace sections of the backward, each rounded up to 256 bytes.
+struct BwdLayout {
+  size_t qT, kT, doT, delta, inv_cnt, inv_idx, total;
+};
+
+BwdLayout bwd_layout(const lcsa_geom& g) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t nq = (size_t)(g.frames / 2) * (g.height / 8) * (g.width / 8);
+  const size_t rows = (size_t)g.batch * g.heads * nq;
+  BwdLayout L{};
+  const size_t tile = up(rows * g.head_dim * 128 * 2);
+  L.qT = 0;
+  L.kT = L.qT + tile;
+  L.doT = L.kT + tile;
+  L.delta = L.doT + tile;
+  L.inv_cnt = L.delta + up(rows * 128 * 4);
+  L.inv_idx = L.inv_cnt + up(rows * 4);
+  L.total = L.inv_idx + up(rows * nq * 4);
+  return L;
+}
+
 }  // namespace
 
 extern "C" {
@@ -279,6 +300,70 @@ lcsa_status lcsa_local_lists(const lcsa_geom* gq, int64_t q_first_abs_tb,
   a.border = params->border;
   for (int32_t t = 0; t < ntb; ++t) a.n_vis[t] = visible_tbs(*cache, q_first_abs_tb + t);
   return device_status(launch_local_lists(a, (hipStream_t)stream), fn);
+}
+
+lcsa_status lcsa_attn_bwd_workspace_size(const lcsa_geom* g, size_t* bytes_out) {
+  lcsa_status st;
+  if ((st = check_geom(g, "lcsa_attn_bwd_workspace_size"))) return st;
+  if (!bytes_out) return fail(LCSA_ERR_NULL, "bytes_out is NULL");
+  *bytes_out = bwd_layout(*g).total;
+  return ok();
+}
+
+lcsa_status lcsa_block_sparse_attn_bwd(const lcsa_geom* g, const void* q, const void* k,
+                                       const void* v, const void* out, const void* dout,
+                                       const float* lse, const int32_t* sel_idx,
+                                       const int32_t* sel_cnt, int32_t kmax, float scale,
+                                       void* dq, void* dk, void* dv, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  const char* fn = "lcsa_block_sparse_attn_bwd";
+  lcsa_status st;
+  if ((st = check_geom(g, fn)) || (st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) ||
+      (st = check_ptr(v, "v")) || (st = check_ptr(out, "out")) ||
+      (st = check_ptr(dout, "dout")) || (st = check_ptr(lse, "lse")) ||
+      (st = check_ptr(sel_idx, "sel_idx")) || (st = check_ptr(sel_cnt, "sel_cnt")) ||
+      (st = check_ptr(dq, "dq")) || (st = check_ptr(dk, "dk")) || (st = check_ptr(dv, "dv")) ||
+      (st = check_ptr(workspace, "workspace")))
+    return st;
+  if (g->dtype != LCSA_BF16) return fail(LCSA_ERR_DTYPE, "%s: bf16 only", fn);
+  if (kmax < 1) return fail(LCSA_ERR_CAPACITY, "kmax %d < 1", kmax);
+  if (!std::isfinite(scale) || scale < 0.f)
+    return fail(LCSA_ERR_PARAM, "scale must be finite and >= 0 (0 = 1/sqrt(D))");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(LCSA_ERR_ALIGN, "%s: workspace is not 256-byte aligned", fn);
+  const BwdLayout lay = bwd_layout(*g);
+  if (workspace_bytes < lay.total)
+    return fail(LCSA_ERR_CAPACITY, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes,
+                lay.total);
+  if (g->frames == 0) return ok();
+  char* ws = (char*)workspace;
+  BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.dout = dout;
+  a.lse = lse;
+  a.sel_idx = sel_idx;
+  a.sel_cnt = sel_cnt;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.qT = ws + lay.qT;
+  a.kT = ws + lay.kT;
+  a.doT = ws + lay.doT;
+  a.delta = (float*)(ws + lay.delta);
+  a.inv_cnt = (int32_t*)(ws + lay.inv_cnt);
+  a.inv_idx = (int32_t*)(ws + lay.inv_idx);
+  a.B = g->batch;
+  a.NH = g->heads;
+  a.D = g->head_dim;
+  a.T = g->frames;
+  a.H = g->height;
+  a.W = g->width;
+  a.kmax = kmax;
+  a.scale = scale == 0.f ? 1.f / std::sqrt((float)g->head_dim) : scale;
+  return device_status(launch_attn_bwd(a, (hipStream_t)stream), fn);
 }
 
 lcsa_status lcsa_segment_max_list(const lcsa_geom* gq, const int32_t* frame_seg,

@@ -80,10 +80,35 @@ struct LocalListArgs {
   int32_t n_vis[LCSA_MAX_SLOTS];  // view positions visible to query TB a (a prefix)
 };
 
+// Backward of the block-sparse attention on the training shape: the keys
+// are the chunk's own blocks (logical id = block index in the chunk).
+struct BwdArgs {
+  const void* q;            // token layout [B][T][H][W][NH][D], bf16
+  const void* k;
+  const void* v;
+  const void* out;          // forward output O
+  const void* dout;         // dL/dO
+  const float* lse;         // [B][NH][nq][128] natural log-sum-exp of the forward
+  const int32_t* sel_idx;   // [B][NH][nq][kmax], ascending ids < nq, -1 padded
+  const int32_t* sel_cnt;   // [B][NH][nq]
+  void* dq;                 // token layout, bf16
+  void* dk;
+  void* dv;
+  void* qT;                 // workspace [B][NH][nq][D][128] bf16 (transposed tiles)
+  void* kT;
+  void* doT;
+  float* delta;             // workspace [B][NH][nq][128]: rowsum(dO * O)
+  int32_t* inv_cnt;         // workspace [B][NH][nq]: query blocks selecting key block j
+  int32_t* inv_idx;         // workspace [B][NH][nq][nq]: those query blocks, ascending
+  int32_t B, NH, D, T, H, W, kmax;
+  float scale;
+};
+
 hipError_t launch_partition_pool(const PartitionArgs& a, hipStream_t s);
 hipError_t launch_draft_mask(const DraftArgs& a, hipStream_t s);
 hipError_t launch_block_sparse_attn(const AttnArgs& a, int32_t dtype, bool segment, hipStream_t s);
 hipError_t launch_segment_lists(const SegListArgs& a, hipStream_t s);
 hipError_t launch_local_lists(const LocalListArgs& a, hipStream_t s);
+hipError_t launch_attn_bwd(const BwdArgs& a, hipStream_t s);
 
 }  // namespace lcsa

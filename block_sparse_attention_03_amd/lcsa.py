@@ -85,6 +85,10 @@ def load_library(path: str = LIB_PATH):
                             c_void_p],
         "lcsa_block_sparse_attn": [G, c_void_p, C, c_void_p, c_void_p, c_int32, c_float,
                                    c_void_p, c_void_p, c_void_p],
+        "lcsa_attn_bwd_workspace_size": [G, POINTER(ctypes.c_size_t)],
+        "lcsa_block_sparse_attn_bwd": [G, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                       c_void_p, c_void_p, c_void_p, c_int32, c_float, c_void_p,
+                                       c_void_p, c_void_p, c_void_p, ctypes.c_size_t, c_void_p],
         "lcsa_max_candidates": [G, c_int64, C, P, POINTER(c_int32)],
         "lcsa_local_lists": [G, c_int64, C, P, c_int32, c_void_p, c_void_p, c_void_p],
         "lcsa_segment_max_list": [G, POINTER(c_int32), POINTER(c_int32)],
@@ -229,6 +233,23 @@ def lcsa_local_lists(geom: Geom, q_first_abs_tb: int, cache: KvCacheStruct, para
     _check(lib.lcsa_local_lists(ctypes.byref(geom), q_first_abs_tb, ctypes.byref(cache),
                                 ctypes.byref(params), kmax, _ptr(sel_idx), _ptr(sel_cnt),
                                 _stream(stream)))
+
+
+def lcsa_attn_bwd_workspace_size(geom: Geom) -> int:
+    lib = load_library()
+    n = ctypes.c_size_t(0)
+    _check(lib.lcsa_attn_bwd_workspace_size(ctypes.byref(geom), ctypes.byref(n)))
+    return n.value
+
+
+def lcsa_block_sparse_attn_bwd(geom: Geom, q, k, v, out, dout, lse, sel_idx, sel_cnt, kmax: int,
+                               dq, dk, dv, workspace, scale: float = 0.0, stream=None):
+    lib = load_library()
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib.lcsa_block_sparse_attn_bwd(ctypes.byref(geom), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                          _ptr(dout), _ptr(lse), _ptr(sel_idx), _ptr(sel_cnt),
+                                          kmax, c_float(scale), _ptr(dq), _ptr(dk), _ptr(dv),
+                                          _ptr(workspace), nbytes, _stream(stream)))
 
 
 def _frame_seg(frame_seg):

@@ -33,6 +33,7 @@ import os
 import numpy as np
 
 TENSOR_IDS = {"q": 0, "k": 1, "v": 2}
+FIELD_IDS = {**TENSOR_IDS, "dout": 3}  # dout: the upstream gradient of a backward test
 
 
 def field_params(seed: int, tensor_id: int, heads: int, head_dim: int):
@@ -112,7 +113,7 @@ def make_qkv(seed: int, heads: int, head_dim: int, height: int, width: int,
     """
     res = {}
     for name in which:
-        f = field_frames(seed, TENSOR_IDS[name], heads, head_dim, height, width,
+        f = field_frames(seed, FIELD_IDS[name], heads, head_dim, height, width,
                          t0, t1, batch=batch, noise_std=noise_std)
         if dtype == "bf16":
             bits = round_bf16_bits(f)
@@ -152,3 +153,28 @@ def field_frames_device(seed: int, tensor_id: int, heads: int, head_dim: int,
                                                  device=device, dtype=torch.float32)
             out[b, ti] = frame.to(dtype)
     return out
+
+
+def random_lists(seed: int, batch: int, heads: int, n_tb: int, n_s: int, k_of_tb, kmax: int):
+    """Seeded block index lists for tests of the list consumers.
+
+    Row (b, h, i) of temporal block t = i // n_s holds min(k_of_tb(t),
+    (t + 1) * n_s) distinct ids drawn uniformly from [0, (t + 1) * n_s),
+    ascending and padded with -1 up to kmax (the shape of causal lists,
+    whose length grows with t). Returns (sel_idx int32 [B][NH][nq][kmax],
+    sel_cnt int32 [B][NH][nq], nested lists [B][NH][nq])."""
+    nq = n_tb * n_s
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 0x115]))
+    idx = np.full((batch, heads, nq, kmax), -1, dtype=np.int32)
+    cnt = np.zeros((batch, heads, nq), dtype=np.int32)
+    nested = [[[None] * nq for _ in range(heads)] for _ in range(batch)]
+    for b in range(batch):
+        for h in range(heads):
+            for i in range(nq):
+                t = i // n_s
+                k = min(int(k_of_tb(t)), (t + 1) * n_s, kmax)
+                ids = np.sort(rng.choice((t + 1) * n_s, size=k, replace=False)).astype(np.int32)
+                idx[b, h, i, :k] = ids
+                cnt[b, h, i] = k
+                nested[b][h][i] = ids.tolist()
+    return idx, cnt, nested

@@ -41,6 +41,7 @@ class Workload:
     frame_seg: tuple | None = None  # Stage-1 segment id per latent frame (segment-masked path)
     lists: str = "draft"           # "draft": top-k selection; "local": every allowed key block
     layers: tuple = ()             # a stack of workloads run one after another per step
+    backward: bool = False         # also run dq, dk, dv over the same lists (training shape)
 
     @property
     def n_slots(self) -> int:
@@ -73,6 +74,10 @@ WORKLOADS = {
     "longT_768x1280": Workload("long-T parallel forward 768x1280 (24 latent frames x 48x80 "
                                "tokens, block-causal over 12 temporal blocks)", 12, 128, "bf16",
                                48, 80, frames=24, cache_frames=0, cap_tb=12, steps=10, seed=1006),
+    "train_longT_768x1280": Workload("training step 768x1280: long-T forward + backward (24 "
+                                     "latent frames, 12 TBs, dq/dk/dv over the same lists)", 12,
+                                     128, "bf16", 48, 80, frames=24, cache_frames=0, cap_tb=12,
+                                     steps=10, seed=1006, backward=True),
     # Stage-1 joint video-image training shape: an 89-frame 768x1280 clip
     # (23 latent frames) and one image as a one-frame segment, 24 frames
     "stage1_768x1280": Workload("Stage-1 segment-masked attention 768x1280 (23-frame video "
@@ -102,7 +107,8 @@ WORKLOADS = {
 }
 
 ORDER = ["tiny", "cold_768x1408", "step_768x1408", "step_1536x2688", "step_4k", "longT_768x1280",
-         "stage1_768x1280", "hybrid_local_4k", "hybrid_global_4k", "hybrid_4k"]
+         "stage1_768x1280", "hybrid_local_4k", "hybrid_global_4k", "hybrid_4k",
+         "train_longT_768x1280"]
 
 
 def segment_pair_quarters(frame_seg) -> dict:
@@ -123,3 +129,9 @@ def segment_pair_quarters(frame_seg) -> dict:
 def attention_flops_per_pair(head_dim: int) -> int:
     """QK^T and PV of one 128 x 128 block pair: 2 * 2 * 128 * 128 * D."""
     return 4 * 128 * 128 * head_dim
+
+
+def backward_flops_per_pair(head_dim: int) -> int:
+    """The five products of the backward of one block pair (S recomputed,
+    dP, dV, dQ, dK): 5 * 2 * 128 * 128 * D."""
+    return 10 * 128 * 128 * head_dim

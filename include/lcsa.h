@@ -283,6 +283,36 @@ lcsa_status lcsa_segment_attn(const lcsa_geom* gq, const void* q_blk, int64_t q_
                               const int32_t* sel_idx, const int32_t* sel_cnt, int32_t kmax,
                               float scale, void* out, float* lse, void* stream);
 
+/* ---- Backward of the block-sparse attention ------------------------------ */
+
+/* [FN] Key design 1 trains the student on all frames of a clip in parallel
+ * under the block-sparse causal mask, and Key design 2 gives the attention
+ * on the selected block pairs. The backward takes the training shape: the
+ * keys are the chunk's own blocks (logical id = block index in the chunk,
+ * (t, by, bx) order), the selection is held fixed, and q, k, v, out (the
+ * forward output), dout (dL/dout) and the gradients dq, dk, dv are bf16 in
+ * the token layout [B][T][H][W][NH][D]. lse is the forward's natural
+ * log-sum-exp ([B][NH][nq][128] float32, from lcsa_block_sparse_attn).
+ * sel_idx rows must be ascending (as every list builder here writes them),
+ * with ids < nq; larger ids are skipped, as in the forward. scale 0 means
+ * 1/sqrt(D). bf16 only (LCSA_ERR_DTYPE otherwise). */
+
+/* Bytes of device workspace lcsa_block_sparse_attn_bwd needs for g:
+ * transposed q, k, dout tiles, rowsum(dout * out) and the inverse lists
+ * (B*NH*nq*nq int32). Host only. */
+lcsa_status lcsa_attn_bwd_workspace_size(const lcsa_geom* g, size_t* bytes_out);
+
+/* dq, dk, dv of the attention over the listed blocks (all three written in
+ * full; key blocks no row selects get dk = dv = 0). workspace: a device
+ * buffer of at least lcsa_attn_bwd_workspace_size() bytes, 256-byte
+ * aligned, owned by the caller and overwritten. Deterministic: no atomics. */
+lcsa_status lcsa_block_sparse_attn_bwd(const lcsa_geom* g, const void* q, const void* k,
+                                       const void* v, const void* out, const void* dout,
+                                       const float* lse, const int32_t* sel_idx,
+                                       const int32_t* sel_cnt, int32_t kmax, float scale,
+                                       void* dq, void* dk, void* dv, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
 /* Text of the last error on this thread ("" after success). */
 const char* lcsa_last_error(void);
 
