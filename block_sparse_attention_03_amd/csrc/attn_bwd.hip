@@ -14,8 +14,8 @@
 //
 // Four kernels, all bf16 on the gfx950 matrix cores (v_mfma_f32_32x32x16_bf16,
 // float32 accumulation):
-//  * prep:  per (block, head) the transposed tiles Q^T, K^T, dO^T ([D][128])
-//           and delta, into the workspace;
+//  * prep:  per (block, head) the transposed tiles Q^T, K^T, dO^T ([D][128]),
+//           lse * log2(e) and delta, into the workspace;
 //  * inverse lists: for each key block, the query blocks whose list holds
 //           it, ascending (binary search in the sorted lists, wave ballot),
 //           so dK / dV need no atomics and are deterministic;
@@ -69,6 +69,8 @@ __device__ inline int perm32(int r) {
 
 __device__ inline void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
+
+
 template <int D>
 struct Q4 {                                   // one 32-row quarter of a block
   static constexpr int ROWB = 32 * D * 2;     // [32][D] row tile bytes
@@ -83,6 +85,11 @@ struct Q4 {                                   // one 32-row quarter of a block
 // Geometry of a chunk-relative block n and its token tau in the token layout.
 struct Tok {
   int T, H, W, NH, D, nbx, nS;
+  // bytes from a block's first token to the first token of its quarter qq
+  // (rows 32qq .. 32qq + 31: frame qq / 2, token rows 4 (qq % 2) ..)
+  __device__ size_t quarter_bytes(int qq) const {
+    return ((size_t)(qq >> 1) * H * W + (size_t)(qq & 1) * 4 * W) * NH * D * 2;
+  }
   __device__ size_t off(int b, int h, int n, int tau) const {
     const int bt = n / nS, s = n - bt * nS, by = s / nbx, bx = s - by * nbx;
     const int t = 2 * bt + (tau >> 6), y = 8 * by + ((tau >> 3) & 7), x = 8 * bx + (tau & 7);
@@ -102,33 +109,87 @@ __device__ inline Tok make_tok(const BwdArgs& a) {
   return t;
 }
 
-// Direct loads of rows r0 .. r0+31 of block n (token layout) into a [32][D]
-// swizzled LDS tile; each wave instruction fills 1 KB, lane l at +16 l.
+// Offsets, in bytes from its block's first token, of this lane's 16-byte
+// units of quarter 0 of a [32][D] row tile (token layout source, swizzled
+// LDS destination: unit u of wave instruction it lands at +16 u). Quarter qq
+// adds (qq / 2) frames and 4 (qq % 2) token rows: Tok::quarter_bytes.
 template <int D>
-__device__ __forceinline__ void load_rows(const Tok& tk, const char* src, int b, int h, int n,
-                                          int r0, char* dst, int w, int lane) {
+__device__ inline void row_unit_offsets(const Tok& tk, int w, int lane,
+                                        uint32_t (&off)[Q4<D>::RLD]) {
   using G = Q4<D>;
 #pragma unroll
   for (int it = 0; it < G::RLD; ++it) {
     const int u = (it * 4 + w) * 64 + lane;
     const int row = u / G::KCH, c = swz_row<D>(row, u % G::KCH);
-    const char* p = src + (tk.off(b, h, n, r0 + row) + c * 8) * 2;
-    __builtin_amdgcn_global_load_lds(p, LDS_PTR(dst + (it * 4 + w) * 1024), 16, 0, 0);
+    const size_t tok = ((size_t)((row >> 3) & 7) * tk.W + (row & 7)) * tk.NH * tk.D;
+    off[it] = (uint32_t)((tok + c * 8) * 2);
   }
 }
 
-// Direct loads of columns c0 .. c0+31 of a [D][128] transposed block into a
-// [D][32] swizzled LDS tile.
+// Offsets of this lane's units of a [D][32] column tile inside a [D][128]
+// transposed block (add 64 qq bytes for quarter qq).
 template <int D>
-__device__ __forceinline__ void load_cols(const char* blk, int c0, char* dst, int w, int lane) {
-  using G = Q4<D>;
+__device__ inline void col_unit_offsets(int w, int lane, uint32_t (&off)[Q4<D>::TLD]) {
 #pragma unroll
-  for (int it = 0; it < G::TLD; ++it) {
+  for (int it = 0; it < Q4<D>::TLD; ++it) {
     const int u = (it * 4 + w) * 64 + lane;
     const int d = u >> 2, c = swz4(d, u & 3);
-    const char* p = blk + ((size_t)d * 128 + c0 + c * 8) * 2;
-    __builtin_amdgcn_global_load_lds(p, LDS_PTR(dst + (it * 4 + w) * 1024), 16, 0, 0);
+    off[it] = (uint32_t)((d * 128 + c * 8) * 2);
   }
+}
+
+// Issue the direct loads of one quarter: a row tile (block base + per-lane
+// offsets) and / or a column tile.
+template <int D>
+__device__ __forceinline__ void load_rows(const char* qblk, const uint32_t* off,
+                                          char* dst, int w) {  // qblk: the quarter's first token
+#pragma unroll
+  for (int it = 0; it < Q4<D>::RLD; ++it)
+    __builtin_amdgcn_global_load_lds(qblk + off[it], LDS_PTR(dst + (it * 4 + w) * 1024), 16, 0,
+                                     0);
+}
+
+template <int D>
+__device__ __forceinline__ void load_cols(const char* blk, const uint32_t* off,
+                                          int qq, char* dst, int w) {
+#pragma unroll
+  for (int it = 0; it < Q4<D>::TLD; ++it)
+    __builtin_amdgcn_global_load_lds(blk + off[it] + 64 * qq, LDS_PTR(dst + (it * 4 + w) * 1024),
+                                     16, 0, 0);
+}
+
+// Issue the loads of quarter qq of one key block for the dQ kernel: K rows,
+// V rows and K^T columns.
+template <int D>
+__device__ __forceinline__ void issue_dq(const Tok& tk, const char* kb, const char* vb,
+                                         const char* ktb, const uint32_t* roff,
+                                         const uint32_t* coff, int qq, char* buf,
+                                         int w) {
+  using G = Q4<D>;
+  const size_t qo = tk.quarter_bytes(qq);
+  load_rows<D>(kb + qo, roff, buf, w);
+  load_rows<D>(vb + qo, roff, buf + G::ROWB, w);
+  load_cols<D>(ktb, coff, qq, buf + 2 * G::ROWB, w);
+}
+
+// Issue the loads of quarter qq of one query block for the dK/dV kernel: Q
+// rows, dO rows, Q^T and dO^T columns, and (wave 0) the quarter's lse2 and
+// delta values: lanes 0-7 fetch 32 lse2 values, lanes 8-15 the 32 delta
+// values, the other lanes repeat them into the rest of a 1 KB region.
+template <int D>
+__device__ __forceinline__ void issue_dkdv(const Tok& tk, const char* qb, const char* ob,
+                                           const char* qtb, const char* otb, const char* lb,
+                                           const uint32_t* roff, const uint32_t* coff, uint32_t loff,
+                                           int qq, char* buf, int w) {
+  using G = Q4<D>;
+  const size_t qo = tk.quarter_bytes(qq);
+  load_rows<D>(qb + qo, roff, buf, w);
+  load_rows<D>(ob + qo, roff, buf + G::ROWB, w);
+  load_cols<D>(qtb, coff, qq, buf + 2 * G::ROWB, w);
+  load_cols<D>(otb, coff, qq, buf + 2 * G::ROWB + G::TRB, w);
+  if (w == 0)
+    __builtin_amdgcn_global_load_lds(lb + 128 * qq + loff, LDS_PTR(buf + 2 * G::ROWB + 2 * G::TRB),
+                                     16, 0, 0);
 }
 
 // B fragments of 32 rows (this wave's rows 32w + l32) of block n: D values
@@ -196,7 +257,10 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
     for (int e = 0; e < 8; ++e) s = fmaf((float)x[e], (float)y[e], s);
 #pragma unroll
     for (int m = 1; m < CPT; m <<= 1) s += __shfl_xor(s, m, 64);
-    if (c == 0) a.delta[blk * 128 + tau] = s;
+    if (c == 0) {
+      a.ld2[blk * 256 + tau] = a.lse[blk * 128 + tau] * kLog2e;
+      a.ld2[blk * 256 + 128 + tau] = s;
+    }
   }
 
   const void* srcs[3] = {a.q, a.k, a.dout};
@@ -279,7 +343,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   const int i = (n_tb - 1 - r / nS) * nS + r % nS;  // longest lists (latest TBs) first
   const int bh = task / nq, h = bh % a.NH, b = bh / a.NH;
   const size_t row = (size_t)bh * nq + i;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int cnt = min(a.sel_cnt[row], a.kmax);
   const int32_t* list = a.sel_idx + row * a.kmax;
 
@@ -294,26 +359,22 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     row_frags<D>(tk, a.q, b, h, i, 32 * w + l32, g, qf);
     row_frags<D>(tk, a.dout, b, h, i, 32 * w + l32, g, of);
     const float sl2 = a.scale * kLog2e;
-    const float lse2 = a.lse[row * 128 + 32 * w + l32] * kLog2e;
-    const float dlt = a.delta[row * 128 + 32 * w + l32];
+    const float lse2 = a.ld2[row * 256 + 32 * w + l32];
+    const float dlt = a.ld2[row * 256 + 128 + 32 * w + l32];
     const int prow = perm32(l32);
-    const int total = 4 * cnt;  // quarters of 32 keys
-    auto issue = [&](int qi, char* buf) {
-      int j = list[qi >> 2];
-      j = (unsigned)j < (unsigned)nq ? j : 0;  // an invalid id loads block 0, then is skipped
-      const int k0 = 32 * (qi & 3);
-      load_rows<D>(tk, (const char*)a.k, b, h, j, k0, buf, w, lane);
-      load_rows<D>(tk, (const char*)a.v, b, h, j, k0, buf + G::ROWB, w, lane);
-      load_cols<D>((const char*)a.kT + ((size_t)bh * nq + j) * D * 128 * 2, k0,
-                   buf + 2 * G::ROWB, w, lane);
+    uint32_t roff[G::RLD], coff[G::TLD];
+    row_unit_offsets<D>(tk, w, lane, roff);
+    col_unit_offsets<D>(w, lane, coff);
+    const char *kb = nullptr, *vb = nullptr, *ktb = nullptr;
+    auto block = [&](int j) {  // an invalid id loads block 0 and is skipped
+      j = (unsigned)j < (unsigned)nq ? j : 0;
+      const size_t base = tk.off(b, h, j, 0) * 2;
+      kb = (const char*)a.k + base;
+      vb = (const char*)a.v + base;
+      ktb = (const char*)a.kT + ((size_t)bh * nq + j) * D * 128 * 2;
     };
-    issue(0, lds);
-    for (int qi = 0; qi < total; ++qi) {
-      char* cur = lds + (qi & 1) * BUF;
-      wait_vm_all();
-      __syncthreads();
-      if (qi + 1 < total) issue(qi + 1, lds + ((qi + 1) & 1) * BUF);
-      if ((unsigned)list[qi >> 2] >= (unsigned)nq) continue;  // uniform: skipped id
+    auto issue = [&](int qq, char* buf) { issue_dq<D>(tk, kb, vb, ktb, roff, coff, qq, buf, w); };
+    auto compute = [&](const char* cur) {
       const char* kr = cur;
       const char* vr = cur + G::ROWB;
       const char* kt = cur + 2 * G::ROWB;
@@ -342,6 +403,33 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
           const bf16x8 af = *reinterpret_cast<const bf16x8*>(kt + d * 64 + swz4(d, 2 * ks + g) * 16);
           acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, ds[ks], acc[dt], 0, 0, 0);
         }
+    };
+    char* buf0 = lds;
+    char* buf1 = lds + BUF;
+    block(list[0]);
+    issue(0, buf0);
+    for (int n = 0; n < cnt; ++n) {
+      const bool ok = (unsigned)list[n] < (unsigned)nq;  // uniform: skipped id
+      // quarter qq of block n sits in buffer qq & 1; the next quarter is in flight
+      wait_vm_all();
+      __syncthreads();
+      issue(1, buf1);
+      if (ok) compute(buf0);
+      wait_vm_all();
+      __syncthreads();
+      issue(2, buf0);
+      if (ok) compute(buf1);
+      wait_vm_all();
+      __syncthreads();
+      issue(3, buf1);
+      if (ok) compute(buf0);
+      wait_vm_all();
+      __syncthreads();
+      if (n + 1 < cnt) {
+        block(list[n + 1]);
+        issue(0, buf0);
+      }
+      if (ok) compute(buf1);
     }
   }
   __syncthreads();
@@ -349,8 +437,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 }
 
 // --------------------------------------------------------------- dK / dV ----
+// One workgroup per CU: the K / V fragments and both accumulators take about
+// 320 registers per lane, more than two workgroups per CU leave. Quarter
+// buffers are double-buffered in LDS (a deeper prefetch measured no faster).
 template <int D>
-__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   using G = Q4<D>;
   constexpr int NS = G::NS, NO = G::NO;
   // Q rows, dO rows, Q^T columns, dO^T columns, then 1 KB for lse2 / delta
@@ -364,10 +455,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   if (task >= n_tasks) return;
   const int j = task % nq;  // key TBs ascending: the earliest keys have the longest lists
   const int bh = task / nq, h = bh % a.NH, b = bh / a.NH;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const size_t kj = (size_t)bh * nq + j;
   const int cnt = min(a.inv_cnt[kj], nq);
-  const int32_t* inv = a.inv_idx + kj * nq;
+  // read through the constant address space: scalar loads, counted by
+  // lgkmcnt, so fetching the next entry never waits for the tile prefetches
+  const __attribute__((address_space(4))) int32_t* inv =
+      (const __attribute__((address_space(4))) int32_t*)(a.inv_idx + kj * nq);
 
   f32x16 dk[NO], dv[NO];
 #pragma unroll
@@ -381,33 +476,29 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
     row_frags<D>(tk, a.v, b, h, j, 32 * w + l32, g, vf);
     const float sl2 = a.scale * kLog2e;
     const int prow = perm32(l32);
-    const int total = 4 * cnt;  // quarters of 32 queries
-    auto issue = [&](int qi, char* buf) {
-      const int i = inv[qi >> 2], q0 = 32 * (qi & 3);
-      const size_t qrow = (size_t)bh * nq + i;
-      load_rows<D>(tk, (const char*)a.q, b, h, i, q0, buf, w, lane);
-      load_rows<D>(tk, (const char*)a.dout, b, h, i, q0, buf + G::ROWB, w, lane);
-      load_cols<D>((const char*)a.qT + qrow * D * 128 * 2, q0, buf + 2 * G::ROWB, w, lane);
-      load_cols<D>((const char*)a.doT + qrow * D * 128 * 2, q0, buf + 2 * G::ROWB + G::TRB, w,
-                   lane);
-      if (w == 0) {  // lanes 0-7: lse of the 32 queries, 8-15: delta, the rest repeat them
-        const int u = lane & 15;
-        const char* p = u < 8 ? (const char*)(a.lse + qrow * 128 + q0) + 16 * u
-                              : (const char*)(a.delta + qrow * 128 + q0) + 16 * (u - 8);
-        __builtin_amdgcn_global_load_lds(p, LDS_PTR(buf + 2 * G::ROWB + 2 * G::TRB), 16, 0, 0);
-      }
+    uint32_t roff[G::RLD], coff[G::TLD];
+    row_unit_offsets<D>(tk, w, lane, roff);
+    col_unit_offsets<D>(w, lane, coff);
+    const uint32_t loff = 16 * (lane & 7) + ((lane & 8) ? 512 : 0);
+    struct Src {
+      const char *q, *o, *qt, *ot, *l;
     };
-    issue(0, lds);
-    for (int qi = 0; qi < total; ++qi) {
-      char* cur = lds + (qi & 1) * BUF;
-      wait_vm_all();
-      __syncthreads();
-      if (qi + 1 < total) issue(qi + 1, lds + ((qi + 1) & 1) * BUF);
+    auto source = [&](int i) {
+      const size_t base = tk.off(b, h, i, 0) * 2;
+      const size_t qrow = (size_t)bh * nq + i;
+      return Src{(const char*)a.q + base, (const char*)a.dout + base,
+                 (const char*)a.qT + qrow * D * 128 * 2, (const char*)a.doT + qrow * D * 128 * 2,
+                 (const char*)(a.ld2 + qrow * 256)};
+    };
+    auto issue = [&](const Src& p, int qq, char* buf) {
+      issue_dkdv<D>(tk, p.q, p.o, p.qt, p.ot, p.l, roff, coff, loff, qq, buf, w);
+    };
+    auto compute = [&](const char* cur) {
       const char* qr = cur;
       const char* orr = cur + G::ROWB;
       const char* qt = cur + 2 * G::ROWB;
       const char* ot = qt + G::TRB;
-      const float* ld = (const float*)(ot + G::TRB);  // [0, 32) lse, [32, 64) delta
+      const float* ld = (const float*)(ot + G::TRB);  // [0, 32) lse2, [32, 64) delta
       f32x16 st, dp;
 #pragma unroll
       for (int e = 0; e < 16; ++e) st[e] = dp[e] = 0.f;
@@ -420,34 +511,52 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
                                                      vf[s], dp, 0, 0, 0);
       }
       // element 8ks + e is query 16ks + 8g + e of the quarter
-      bf16x8 pb[2], dsb[2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const int q = 16 * ks + 8 * g;
-        const f32x4 l0 = *reinterpret_cast<const f32x4*>(ld + q);
-        const f32x4 l1 = *reinterpret_cast<const f32x4*>(ld + q + 4);
-        const f32x4 d0 = *reinterpret_cast<const f32x4*>(ld + 32 + q);
-        const f32x4 d1 = *reinterpret_cast<const f32x4*>(ld + 32 + q + 4);
+        bf16x8 pb, dsb;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float lse = e < 4 ? l0[e] : l1[e - 4];
-          const float dl = e < 4 ? d0[e] : d1[e - 4];
-          const float p = __builtin_amdgcn_exp2f(fmaf(st[8 * ks + e], sl2, -lse * kLog2e));
-          pb[ks][e] = (__bf16)p;
-          dsb[ks][e] = (__bf16)(p * (dp[8 * ks + e] - dl));
+          const float p = __builtin_amdgcn_exp2f(fmaf(st[8 * ks + e], sl2, -ld[q + e]));
+          pb[e] = (__bf16)p;
+          dsb[e] = (__bf16)(p * (dp[8 * ks + e] - ld[32 + q + e]));
         }
-      }
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int dt = 0; dt < NO; ++dt) {
           const int d = 32 * dt + l32;
           const int off = d * 64 + swz4(d, 2 * ks + g) * 16;
           dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(ot + off),
-                                                           pb[ks], dv[dt], 0, 0, 0);
+                                                           pb, dv[dt], 0, 0, 0);
           dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(qt + off),
-                                                           dsb[ks], dk[dt], 0, 0, 0);
+                                                           dsb, dk[dt], 0, 0, 0);
         }
+      }
+    };
+    // quarter qq of query block n sits in buffer qq & 1; the next is in flight
+    char* buf0 = lds;
+    char* buf1 = lds + BUF;
+    Src cur = source(inv[0]);
+    issue(cur, 0, buf0);
+    for (int n = 0; n < cnt; ++n) {
+      wait_vm_all();
+      __syncthreads();
+      issue(cur, 1, buf1);
+      compute(buf0);
+      wait_vm_all();
+      __syncthreads();
+      issue(cur, 2, buf0);
+      compute(buf1);
+      wait_vm_all();
+      __syncthreads();
+      issue(cur, 3, buf1);
+      compute(buf0);
+      wait_vm_all();
+      __syncthreads();
+      if (n + 1 < cnt) {
+        cur = source(inv[n + 1]);
+        issue(cur, 0, buf0);
+      }
+      compute(buf1);
     }
   }
   __syncthreads();

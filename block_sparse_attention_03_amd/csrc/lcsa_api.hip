@@ -124,7 +124,7 @@ BwdLayout bwd_layout(const lcsa_geom& g) {
   L.kT = L.qT + tile;
   L.doT = L.kT + tile;
   L.delta = L.doT + tile;
-  L.inv_cnt = L.delta + up(rows * 128 * 4);
+  L.inv_cnt = L.delta + up(rows * 256 * 4);
   L.inv_idx = L.inv_cnt + up(rows * 4);
   L.total = L.inv_idx + up(rows * nq * 4);
   return L;
@@ -352,7 +352,7 @@ lcsa_status lcsa_block_sparse_attn_bwd(const lcsa_geom* g, const void* q, const 
   a.qT = ws + lay.qT;
   a.kT = ws + lay.kT;
   a.doT = ws + lay.doT;
-  a.delta = (float*)(ws + lay.delta);
+  a.ld2 = (float*)(ws + lay.delta);
   a.inv_cnt = (int32_t*)(ws + lay.inv_cnt);
   a.inv_idx = (int32_t*)(ws + lay.inv_idx);
   a.B = g->batch;

@@ -97,7 +97,8 @@ struct BwdArgs {
   void* qT;                 // workspace [B][NH][nq][D][128] bf16 (transposed tiles)
   void* kT;
   void* doT;
-  float* delta;             // workspace [B][NH][nq][128]: rowsum(dO * O)
+  float* ld2;               // workspace [B][NH][nq][256]: lse * log2(e) of the 128 queries,
+                            // then rowsum(dO * O) of the same queries
   int32_t* inv_cnt;         // workspace [B][NH][nq]: query blocks selecting key block j
   int32_t* inv_idx;         // workspace [B][NH][nq][nq]: those query blocks, ascending
   int32_t B, NH, D, T, H, W, kmax;
