@@ -362,17 +362,28 @@ def summarize_profiles(args):
         raise SystemExit("--summarize-profiles needs --copy-probe-mib (the calibration size)")
     trace_dir, fetch_dir, write_dir = args.summarize_profiles
     probe_bytes = args.copy_probe_mib * (1 << 20)
-    fc, fa, nf = _counter_per_dispatch(fetch_dir, "FETCH_SIZE")
-    wc, wa, nw = _counter_per_dispatch(write_dir, "WRITE_SIZE")
-    f_factor = probe_bytes / (fc * 1024.0)
-    w_factor = probe_bytes / (wc * 1024.0)
-    fetch_b = fa * 1024.0 * f_factor
-    write_b = wa * 1024.0 * w_factor
+    counters = fetch_dir != "-" and write_dir != "-"  # "-": kernel trace only
+    cnt = None
+    if counters:
+        fc, fa, nf = _counter_per_dispatch(fetch_dir, "FETCH_SIZE")
+        wc, wa, nw = _counter_per_dispatch(write_dir, "WRITE_SIZE")
+        f_factor = probe_bytes / (fc * 1024.0)
+        w_factor = probe_bytes / (wc * 1024.0)
+        fetch_b = fa * 1024.0 * f_factor
+        write_b = wa * 1024.0 * w_factor
+        cnt = (fetch_b, write_b, fa, wa, fc, wc, f_factor, w_factor, nf, nw)
     stats = [r for r in _csv_rows(trace_dir, "kernel_stats.csv") if _short(r["Name"])]
     bench = None
     if args.bench_log:
         with open(args.bench_log) as f:
             bench = json.loads([ln for ln in f if ln.startswith("{")][-1])
+    if cnt:
+        _write_traffic(args, *cnt)
+    _write_summary(args, stats, bench, cnt)
+
+
+def _write_traffic(args, fetch_b, write_b, fa, wa, fc, wc, f_factor, w_factor, nf, nw):
+    probe_bytes = args.copy_probe_mib * (1 << 20)
     entry = {"kernel": ATTN_KERNEL, "bytes_per_launch": round(fetch_b + write_b),
              "fetch_bytes_per_launch": round(fetch_b), "write_bytes_per_launch": round(write_b),
              "fetch_kib_raw": round(fa, 1), "write_kib_raw": round(wa, 1),
@@ -390,9 +401,12 @@ def summarize_profiles(args):
         json.dump(tj, f, indent=1, sort_keys=True)
         f.write("\n")
 
+
+def _write_summary(args, stats, bench, cnt):
     sw = (f"--steps {bench['steps']} --warmup {bench['warmup']}" if bench else "--steps S --warmup W")
     kernels = sorted({_short(r["Name"]) for r in stats})
-    tag = "_".join(k.split("<")[0].replace("_kernel", "") for k in kernels)
+    names = sorted({k.split("<")[0].replace("_kernel", "") for k in kernels})
+    tag = "_".join(names) if len(names) <= 3 else "lcsa_kernels"
     out = os.path.join(ROOT, "profiles", f"{tag}_{args.workload}.md")
     cmd_b = (f"python3 bench.py --workload {args.workload} {sw} "
              f"--no-cpu-baseline --copy-probe-mib {args.copy_probe_mib}")
@@ -400,20 +414,34 @@ def summarize_profiles(args):
              "Commands (from the repository root, with `TMPDIR=/tmp` exported for the profiler's "
              "scratch files):", "",
              f"    rocprofv3 --kernel-trace --stats --output-format csv -d TRACE_DIR -o tr -- {cmd_b}",
-             f"    rocprofv3 --pmc FETCH_SIZE --output-format csv -d FETCH_DIR -o pmc -- {cmd_b}",
-             f"    rocprofv3 --pmc WRITE_SIZE --output-format csv -d WRITE_DIR -o pmc -- {cmd_b}",
+             *([f"    rocprofv3 --pmc FETCH_SIZE --output-format csv -d FETCH_DIR -o pmc -- {cmd_b}",
+                f"    rocprofv3 --pmc WRITE_SIZE --output-format csv -d WRITE_DIR -o pmc -- {cmd_b}"]
+               if cnt else []),
              f"    python3 bench.py --workload {args.workload} --copy-probe-mib {args.copy_probe_mib} "
-             "--summarize-profiles TRACE_DIR FETCH_DIR WRITE_DIR --bench-log BENCH_LOG", "",
+             f"--summarize-profiles TRACE_DIR {'FETCH_DIR WRITE_DIR' if cnt else '- -'} "
+             "--bench-log BENCH_LOG", "",
              "## Kernel durations (rocprofv3 --stats)", "",
              "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
     for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
         lines.append(f"| {_short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
-    if bench:
+    if bench and "bwd_ms" in bench:
+        lines += ["", f"bench.py, same workload, HIP events on the launch stream: attention "
+                  f"forward + backward {bench['attn_ms'] * 1e3:.1f} us per step (backward "
+                  f"{bench['bwd_ms'] * 1e3:.1f} us), step {bench['ms_per_step'] * 1e3:.1f} us, "
+                  f"{bench['config']['selected_pairs_per_step']} block pairs per step "
+                  f"(steps={bench['steps']}, warmup={bench['warmup']})."]
+    elif bench:
         lines += ["", f"bench.py, same workload, HIP events on the launch stream: attention "
                   f"{bench['attn_ms'] * 1e3:.1f} us per launch, step {bench['ms_per_step'] * 1e3:.1f} us, "
                   f"{bench['config']['selected_pairs_per_step']} block pairs per step "
                   f"(steps={bench['steps']}, warmup={bench['warmup']})."]
+    if not cnt:
+        with open(out, "w") as f:
+            f.write("\n".join(lines) + "\n")
+        print(json.dumps({"wrote": out}))
+        return
+    fetch_b, write_b, fa, wa, fc, wc, f_factor, w_factor, nf, nw = cnt
     lines += ["", "## HBM traffic of the attention kernel (rocprofv3 --pmc)", "",
               f"Calibration: the plain {args.copy_probe_mib} MiB device copy ({COPY_KERNEL}) reads "
               f"FETCH_SIZE {fc:.0f} KiB and WRITE_SIZE {wc:.0f} KiB, so one counted KiB is "
@@ -423,7 +451,7 @@ def summarize_profiles(args):
               f"| WRITE_SIZE | {wa:.0f} | {write_b / 1e6:.1f} | {nw} |", ""]
     with open(out, "w") as f:
         f.write("\n".join(lines))
-    print(json.dumps({"wrote": [out, args.traffic_json], args.workload: entry}))
+    print(json.dumps({"wrote": out}))
 
 
 if __name__ == "__main__":
