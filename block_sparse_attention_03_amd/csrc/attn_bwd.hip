@@ -33,43 +33,10 @@
 // in 32-row quarters, double-buffered in LDS with direct global->LDS loads,
 // and rows are XOR-swizzled in 16-byte chunks (conflict-free fragment reads).
 #include "lcsa_kernels.h"
+#include "mfma_tiles.h"
 
 namespace lcsa {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
-
-constexpr float kLog2e = 1.4426950408889634f;
-
-// XOR swizzles of 16-byte chunk c in LDS rows of 256, 128 and 64 bytes: 16
-// consecutive rows read at one logical chunk hit 16 different bank groups.
-// Involutions: the same map goes logical -> physical and back.
-__device__ inline int swz16(int row, int c) { return c ^ (row & 15); }
-__device__ inline int swz8(int row, int c) { return c ^ ((row >> 1) & 7); }
-__device__ inline int swz4(int row, int c) { return c ^ ((row >> 2) & 3); }
-template <int D>
-__device__ inline int swz_row(int row, int c) {  // rows of D bf16
-  if constexpr (D == 128) return swz16(row, c);
-  else return swz8(row, c);
-}
-
-// Row order of a 32-row A operand whose product feeds the next MFMA as B:
-// lane (l, g) of a 32x32 accumulator holds rows 8i + 4g + j; reading source
-// row perm(r) into A row r makes them the source rows 16*(i/2) + 8g +
-// 4*(i%2) + j, so accumulator elements 8ks .. 8ks+7 are source rows
-// 16ks + 8g .. 16ks + 8g + 7: one B fragment of k-step ks.
-__device__ inline int perm32(int r) {
-  const int i = r >> 3, gg = (r >> 2) & 1, j = r & 3;
-  return 16 * (i >> 1) + 8 * gg + 4 * (i & 1) + j;
-}
-
-__device__ inline void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
-
-
 
 template <int D>
 struct Q4 {                                   // one 32-row quarter of a block

@@ -30,16 +30,10 @@
 #include <type_traits>
 
 #include "lcsa_kernels.h"
+#include "mfma_tiles.h"
 
 namespace lcsa {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // native vector: stays in VGPRs
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ inline size_t out_offset(const AttnArgs& a, int b, int h, int i, int tau, int d) {
   const int nbx = a.W / 8, nS = (a.H / 8) * nbx;
@@ -48,32 +42,6 @@ __device__ inline size_t out_offset(const AttnArgs& a, int b, int h, int i, int 
   const int y = 8 * by + ((tau >> 3) & 7);
   const int x = 8 * bx + (tau & 7);
   return ((((size_t)b * a.T + t) * a.H + y) * a.W + x) * a.NH * a.D + (size_t)h * a.D + d;
-}
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
-
-// XOR swizzles of 16-byte chunk c in an LDS row: rows of 256 bytes (16
-// chunks) and rows of 128 bytes (8 chunks). Both are involutions, so the
-// same function maps logical -> physical and back. Sixteen consecutive
-// rows read at the same logical chunk hit sixteen different bank groups.
-__device__ inline int swz16(int row, int c) { return c ^ (row & 15); }
-__device__ inline int swz8(int row, int c) { return c ^ ((row >> 1) & 7); }
-
-template <int D>
-__device__ inline int swz_k(int row, int c) {
-  if constexpr (D == 128) return swz16(row, c);
-  else return swz8(row, c);
-}
-
-// Key order inside a 32-key S^T tile. Lane (q, g) of an MFMA 32x32 output
-// holds rows 8i + 4g + j (i, j = 0..3); loading K row perm(r) into A row r
-// makes those rows the keys 16*(i/2) + 8g + 4*(i%2) + j, i.e. for the PV
-// k-step ks the lane holds exactly the 8 contiguous keys 16ks + 8g + e that
-// a plain V^T row chunk supplies as the A operand.
-__device__ inline int perm_key(int r) {
-  const int i = r >> 3, gg = (r >> 2) & 1, j = r & 3;
-  return 16 * (i >> 1) + 8 * gg + 4 * (i & 1) + j;
 }
 
 template <int D>
@@ -100,7 +68,7 @@ __device__ __forceinline__ void load_subtile(const char* kblk, const char* vblk,
 #pragma unroll
   for (int it = 0; it < T::KLD; ++it) {
     const int unit = (it * 4 + w) * 64 + lane;
-    const int row = unit / T::KCH, c = swz_k<D>(row, unit % T::KCH);
+    const int row = unit / T::KCH, c = swz_row<D>(row, unit % T::KCH);
     const char* src = kblk + ((size_t)(64 * hf + row) * D + c * 8) * 2;
     __builtin_amdgcn_global_load_lds(src, LDS_PTR(buf + (it * 4 + w) * 1024), 16, 0, 0);
   }
@@ -113,8 +81,6 @@ __device__ __forceinline__ void load_subtile(const char* kblk, const char* vblk,
     __builtin_amdgcn_global_load_lds(src, LDS_PTR(vb + (it * 4 + w) * 1024), 16, 0, 0);
   }
 }
-
-__device__ inline void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
 __device__ inline float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
@@ -198,10 +164,12 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   // Lane-invariant LDS fragment offsets. K rows prow and prow + 32 share
   // the swizzle (it depends on row & 15), V^T rows 32dt + l32 share it for
   // every dt, so tile and buffer selection are immediate offsets.
-  const int prow = perm_key(l32);
+  // K rows are read in perm32 order, so S^T's accumulators are P's B
+  // fragments in V^T's natural key order
+  const int prow = perm32(l32);
   int koff[NS], voff[4];
 #pragma unroll
-  for (int s2 = 0; s2 < NS; ++s2) koff[s2] = prow * (D * 2) + swz_k<D>(prow, 2 * s2 + g) * 16;
+  for (int s2 = 0; s2 < NS; ++s2) koff[s2] = prow * (D * 2) + swz_row<D>(prow, 2 * s2 + g) * 16;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) voff[ks] = l32 * 128 + swz8(l32, 2 * ks + g) * 16;
 
@@ -316,7 +284,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) v4[j] = (__bf16)(o[dt][4 * ii + j] * inv);
       const int c = 4 * dt + ii;  // 16-byte chunk of d = 32dt + 8ii .. +8
-      *reinterpret_cast<uint2*>(st + tau * (D * 2) + swz_k<D>(tau, c) * 16 + 8 * g) =
+      *reinterpret_cast<uint2*>(st + tau * (D * 2) + swz_row<D>(tau, c) * 16 + 8 * g) =
           *reinterpret_cast<const uint2*>(v4);
     }
   __syncthreads();
@@ -325,7 +293,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   for (int e0 = 0; e0 < 128 * CH; e0 += 256) {
     const int e = e0 + tid, trow = e / CH, c = e % CH;
     *reinterpret_cast<uint4*>(out + out_offset(a, b, h, i, trow, c * 8)) =
-        *reinterpret_cast<const uint4*>(st + trow * (D * 2) + swz_k<D>(trow, c) * 16);
+        *reinterpret_cast<const uint4*>(st + trow * (D * 2) + swz_row<D>(trow, c) * 16);
   }
   if (a.lse && g == 0)
     a.lse[row * 128 + tau] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
