@@ -271,6 +271,7 @@ def main():
                    "kmax": kmax, "parallelism": "single GPU"},
         "attn_ms": round(attn_avg, 4),
         **({"bwd_ms": round(float(np.mean(bwd_ms)), 4)} if has_bwd else {}),
+        "attn_ms_median": round(float(np.median(attn_ms)), 4),
         "attn_ms_p10_p90": [round(float(np.percentile(attn_ms, 10)), 4),
                             round(float(np.percentile(attn_ms, 90)), 4)],
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
@@ -318,8 +319,15 @@ def cpu_baseline(w, sample_heads, sample_steps, flops_pair):
         res = O.lcsa_step(d["q"][1], d["k"][1], d["v"][1], cache, t0 // 2, p)
         sec += time.perf_counter() - tic
         pairs += int(sum(len(r) for bh in res.sel for hh in bh for r in hh))
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")),
+                         None)
+    except OSError:
+        pass
     return {"value": round(pairs * flops_pair / sec / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
-            "kind": "oracle", "seconds": round(sec, 3),
+            "kind": "oracle", "seconds": round(sec, 3), "cpu_model": model,
             "sample": f"{steps} consecutive full LCSA steps (partition, pool, draft, top-k, "
                       f"attention, cache update) of the same workload's stream, heads 0..{nh - 1} "
                       f"of {w.heads}, float64 NumPy"}
