@@ -222,3 +222,47 @@ def test_segment_validation_before_any_device_call(lib):
     big = L.make_geom(1, 2, 128, 34, 48, 80, L.LCSA_BF16)
     with pytest.raises(L.LcsaError, match="LCSA_ERR_CAPACITY"):
         L.lcsa_segment_max_list(big, [0] * 34)
+
+
+# ------------------------------------------------------------------ backward
+
+def test_backward_workspace_size_and_validation(lib):
+    g = L.make_geom(1, 2, 128, 4, 16, 24, L.LCSA_BF16)
+    nq, rows = 2 * 6, 2 * 2 * 6
+    need = L.lcsa_attn_bwd_workspace_size(g)
+    up = lambda x: (x + 255) // 256 * 256
+    assert need == 3 * up(rows * 128 * 128 * 2) + up(rows * 256 * 4) + up(rows * 4) + up(rows * nq * 4)
+
+    class Buf:  # an aligned fake device buffer: validation fails before any device call
+        def __init__(self, addr, n=0):
+            self.addr, self.n = addr, n
+
+        def data_ptr(self):
+            return self.addr
+
+        def numel(self):
+            return self.n
+
+        def element_size(self):
+            return 1
+
+    P = Buf(FAKE)
+
+    def call(geom=g, ws=Buf(FAKE, need), kmax=4, scale=0.0):
+        L.lcsa_block_sparse_attn_bwd(geom, P, P, P, P, P, P, P, P, kmax, P, P, P, ws, scale=scale,
+                                     stream=0)
+
+    with pytest.raises(L.LcsaError, match="LCSA_ERR_CAPACITY"):   # workspace one byte short
+        call(ws=Buf(FAKE, need - 1))
+    with pytest.raises(L.LcsaError, match="LCSA_ERR_ALIGN"):      # workspace not 256-aligned
+        call(ws=Buf(FAKE + 16, need))
+    with pytest.raises(L.LcsaError, match="LCSA_ERR_DTYPE"):      # bf16 only
+        call(geom=L.make_geom(1, 2, 128, 4, 16, 24, L.LCSA_F32))
+    with pytest.raises(L.LcsaError, match="LCSA_ERR_CAPACITY"):
+        call(kmax=0)
+    with pytest.raises(L.LcsaError, match="LCSA_ERR_PARAM"):
+        call(scale=-1.0)
+    lib_ = L.load_library()
+    assert lib_.lcsa_block_sparse_attn_bwd(ctypes.byref(g), None, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                           FAKE, FAKE, 4, ctypes.c_float(0), FAKE, FAKE, FAKE,
+                                           FAKE, need, None) == 1  # LCSA_ERR_NULL
