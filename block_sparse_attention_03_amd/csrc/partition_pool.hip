@@ -63,7 +63,10 @@ __device__ inline size_t token_offset(const PartitionArgs& a, int b, int h, int 
   return ((((size_t)b * a.T + t) * a.H + y) * a.W + x) * a.NH * a.D + (size_t)h * a.D;
 }
 
-// Load this thread's chunks of one 128 x D block (token layout source).
+// Load this thread's chunks of one 128 x D block (token layout source). The
+// token-layout inputs are read exactly once, so the loads are non-temporal
+// (4K step: 234 -> 212 us). The outputs are stored normally: the attention
+// kernel reads them next, and non-temporal stores measured slower.
 template <int ESZ, int D>
 __device__ inline void load_block(const PartitionArgs& a, const char* src, int b, int h, int bt,
                                   int by, int bx, u32x4 (&v)[Geo<ESZ, D>::ITERS]) {
@@ -72,8 +75,8 @@ __device__ inline void load_block(const PartitionArgs& a, const char* src, int b
 #pragma unroll
   for (int it = 0; it < G::ITERS; ++it) {
     const int tau = it * G::TPI + tsub;
-    v[it] = *reinterpret_cast<const u32x4*>(
-        src + (token_offset(a, b, h, bt, by, bx, tau) + c * G::EPC) * ESZ);
+    v[it] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+        src + (token_offset(a, b, h, bt, by, bx, tau) + c * G::EPC) * ESZ));
   }
 }
 
