@@ -292,8 +292,11 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
   for (int e0 = 0; e0 < 128 * CH; e0 += 256) {
     const int e = e0 + tid, trow = e / CH, c = e % CH;
-    *reinterpret_cast<uint4*>(out + out_offset(a, b, h, i, trow, c * 8)) =
-        *reinterpret_cast<const uint4*>(st + trow * (D * 2) + swz_row<D>(trow, c) * 16);
+    // O is written once and not read back here: non-temporal, so it does not
+    // evict the K / V tiles other query blocks still reuse from L2
+    __builtin_nontemporal_store(
+        *reinterpret_cast<const u32x4*>(st + trow * (D * 2) + swz_row<D>(trow, c) * 16),
+        reinterpret_cast<u32x4*>(out + out_offset(a, b, h, i, trow, c * 8)));
   }
   if (a.lse && g == 0)
     a.lse[row * 128 + tau] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
