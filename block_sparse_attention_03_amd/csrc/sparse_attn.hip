@@ -57,29 +57,44 @@ struct Tile {
   static constexpr int NO = D / 32;                // O^T tiles
 };
 
-// Issue the direct global -> LDS loads of half `hf` (keys 64hf..64hf+63) of
-// a key block into one buffer. Each wave instruction fills 1 KB of LDS, lane
-// l landing at +16l; the lane fetches whichever global chunk belongs there
-// under the swizzle.
+// Direct global -> LDS loads of one 64-key half of a key block. Each wave
+// instruction fills 1 KB of LDS, lane l landing at +16l; the lane fetches
+// whichever global chunk belongs there under the swizzle. The per-lane byte
+// offsets (relative to the half's first K row and first V^T column) do not
+// depend on the block, so they are computed once (subtile_offsets) and the
+// per-block part of each address is a scalar base plus a 32-bit lane offset.
 template <int D>
-__device__ __forceinline__ void load_subtile(const char* kblk, const char* vblk, int hf, char* buf,
-                                             int w, int lane) {
+__device__ __forceinline__ void subtile_offsets(int w, int lane, uint32_t* koff, uint32_t* voff) {
   using T = Tile<D>;
 #pragma unroll
   for (int it = 0; it < T::KLD; ++it) {
     const int unit = (it * 4 + w) * 64 + lane;
     const int row = unit / T::KCH, c = swz_row<D>(row, unit % T::KCH);
-    const char* src = kblk + ((size_t)(64 * hf + row) * D + c * 8) * 2;
-    __builtin_amdgcn_global_load_lds(src, LDS_PTR(buf + (it * 4 + w) * 1024), 16, 0, 0);
+    koff[it] = (uint32_t)((row * D + c * 8) * 2);
   }
-  char* vb = buf + T::KBYTES;
 #pragma unroll
   for (int it = 0; it < T::VLD; ++it) {
     const int unit = (it * 4 + w) * 64 + lane;
     const int d = unit >> 3, c = swz8(d, unit & 7);
-    const char* src = vblk + ((size_t)d * 128 + 64 * hf + c * 8) * 2;
-    __builtin_amdgcn_global_load_lds(src, LDS_PTR(vb + (it * 4 + w) * 1024), 16, 0, 0);
+    voff[it] = (uint32_t)((d * 128 + c * 8) * 2);
   }
+}
+
+// Issue the loads of half hf (keys 64hf..64hf+63) into one LDS buffer; w is
+// the (uniform) wave index.
+template <int D>
+__device__ __forceinline__ void load_subtile(const char* kblk, const char* vblk, int hf, char* buf,
+                                             int w, const uint32_t* koff, const uint32_t* voff) {
+  using T = Tile<D>;
+  const char* kh = kblk + (size_t)64 * hf * D * 2;
+  const char* vh = vblk + 64 * hf * 2;
+#pragma unroll
+  for (int it = 0; it < T::KLD; ++it)
+    __builtin_amdgcn_global_load_lds(kh + koff[it], LDS_PTR(buf + (it * 4 + w) * 1024), 16, 0, 0);
+  char* vb = buf + T::KBYTES;
+#pragma unroll
+  for (int it = 0; it < T::VLD; ++it)
+    __builtin_amdgcn_global_load_lds(vh + voff[it], LDS_PTR(vb + (it * 4 + w) * 1024), 16, 0, 0);
 }
 
 __device__ inline float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
@@ -119,7 +134,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   const int bh = task / nq;
   const int h = bh % a.NH, b = bh / a.NH;
   const size_t row = (size_t)bh * nq + i;  // flat query-block row of the lists and q_blk
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int cnt = min(a.sel_cnt[row], a.kmax);
   const int32_t* list = a.sel_idx + row * a.kmax;
   const int tau = 32 * w + l32;          // this lane's query row in the block
@@ -142,11 +158,19 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     qf[s] = *reinterpret_cast<const bf16x8*>(qb + tau * D + 16 * s + 8 * g);
 
   const size_t bh_slots = (size_t)bh * a.n_slots;
-  const float inv_ns = 1.f / (float)nS;
+  // View position of a uniform key block id j in [0, n_keys): j / nS by a
+  // binary search on the scalar unit (positions are below LCSA_MAX_SLOTS)
+  auto view_pos = [&](int j) {
+    int p = 0;
+#pragma unroll
+    for (int step = LCSA_MAX_SLOTS / 2; step > 0; step >>= 1)
+      if (j >= (p + step) * nS) p += step;
+    return p;
+  };
+  const int qtb = i / nS;  // query TB (segment mask)
   auto block_base = [&](int j, const char*& kp, const char*& vp) {
     j = (unsigned)j < (unsigned)n_keys ? j : 0;
-    // p = j / nS exactly: (j + 0.5) / nS lies strictly inside (p, p + 1)
-    const int p = (int)(((float)j + 0.5f) * inv_ns);
+    const int p = view_pos(j);
     const int s = j - p * nS;
     const size_t blk = (bh_slots + a.view.slot[p]) * nS + s;
     kp = (const char*)a.k_ring + blk * (128 * D * 2);
@@ -241,34 +265,55 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[dt][ks], pf[ks >> 1][ks & 1], o[dt], 0, 0, 0);
   };
 
-  const int qtb = i / nS;                                   // query TB (segment mask)
   const int dq = __builtin_amdgcn_readfirstlane(w) >> 1;   // this wave's query frame
   const char *kp, *vp;
-  block_base(list[0], kp, vp);
-  load_subtile<D>(kp, vp, 0, lds, w, lane);
-  for (int it = 0; it < cnt; ++it) {
-    const int j = list[it];
+  uint32_t gkoff[T::KLD], gvoff[T::VLD];
+  subtile_offsets<D>(w, lane, gkoff, gvoff);
+  // Which halves of key block j this wave computes: none for a skipped id;
+  // under the segment mask, the halves whose frame shares this wave's segment
+  auto block_flags = [&](int j, bool& ok0, bool& ok1) {
     const bool ok = (unsigned)j < (unsigned)n_keys;  // uniform: skipped id
-    bool ok0 = ok, ok1 = ok;
+    ok0 = ok1 = ok;
     if constexpr (SEG) {
-      const int p = ok ? (int)(((float)j + 0.5f) * inv_ns) : 0;
-      const uint32_t m = (uint32_t)a.qmask[qtb][p] >> (2 * dq);
+      const int p = ok ? view_pos(j) : 0;
+      // the dword of qmask[qtb] holding byte p, as a scalar load
+      const uint32_t m = ((const uint32_t*)a.qmask[qtb])[p >> 2] >> (8 * (p & 3) + 2 * dq);
       ok0 = ok && (m & 1u);
       ok1 = ok && (m & 2u);
     }
+  };
+  // List entries are read with scalar loads one block iteration before they
+  // are needed (entry it + 2 at the end of iteration it, consumed after the
+  // next iteration's first barrier), so no wave waits on a list load.
+  const __attribute__((address_space(4))) int32_t* slist =
+      (const __attribute__((address_space(4))) int32_t*)list;
+  int j_nxt = slist[min(1, cnt - 1)];
+  bool ok0, ok1;
+  {
+    const int j0 = slist[0];
+    block_flags(j0, ok0, ok1);
+    block_base(j0, kp, vp);
+  }
+  load_subtile<D>(kp, vp, 0, lds, w, gkoff, gvoff);
+  for (int it = 0; it < cnt; ++it) {
     // half 0 of block it is in buffer 0; fetch half 1 into buffer 1
     wait_vm_all();
     __syncthreads();
-    load_subtile<D>(kp, vp, 1, lds + T::BUF, w, lane);
+    load_subtile<D>(kp, vp, 1, lds + T::BUF, w, gkoff, gvoff);
     if (ok0) compute_half(std::integral_constant<int, 0>{});
     // half 1 is in buffer 1; fetch half 0 of the next block into buffer 0
     wait_vm_all();
     __syncthreads();
+    bool nok0 = false, nok1 = false;
     if (it + 1 < cnt) {
-      block_base(list[it + 1], kp, vp);
-      load_subtile<D>(kp, vp, 0, lds, w, lane);
+      block_flags(j_nxt, nok0, nok1);
+      block_base(j_nxt, kp, vp);
+      load_subtile<D>(kp, vp, 0, lds, w, gkoff, gvoff);
     }
     if (ok1) compute_half(std::integral_constant<int, 1>{});
+    ok0 = nok0;
+    ok1 = nok1;
+    j_nxt = slist[min(it + 2, cnt - 1)];
   }
 
   // epilogue: normalise, stage the 128 x D tile in LDS, write whole rows
