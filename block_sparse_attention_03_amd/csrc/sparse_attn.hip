@@ -62,7 +62,7 @@ struct Tile {
 // whichever global chunk belongs there under the swizzle. The per-lane byte
 // offsets (relative to the half's first K row and first V^T column) do not
 // depend on the block, so they are computed once (subtile_offsets) and the
-// per-block part of each address is a scalar base plus a 32-bit lane offset.
+// per-block part of each address is scalar.
 template <int D>
 __device__ __forceinline__ void subtile_offsets(int w, int lane, uint32_t* koff, uint32_t* voff) {
   using T = Tile<D>;
@@ -80,21 +80,32 @@ __device__ __forceinline__ void subtile_offsets(int w, int lane, uint32_t* koff,
   }
 }
 
+// Raw buffer resource word 3 for untyped dword loads (32-bit data format).
+constexpr int kRawBufferWord3 = 0x00020000;
+
 // Issue the loads of half hf (keys 64hf..64hf+63) into one LDS buffer; w is
-// the (uniform) wave index.
+// the (uniform) wave index. Buffer loads: the resource holds the block base
+// and its size (an offset past it would read zeros, never another block),
+// the half offset is the scalar offset, so a load needs no vector address
+// arithmetic at all.
 template <int D>
 __device__ __forceinline__ void load_subtile(const char* kblk, const char* vblk, int hf, char* buf,
                                              int w, const uint32_t* koff, const uint32_t* voff) {
   using T = Tile<D>;
-  const char* kh = kblk + (size_t)64 * hf * D * 2;
-  const char* vh = vblk + 64 * hf * 2;
+  constexpr int kBlockBytes = 128 * D * 2;
+  const __amdgpu_buffer_rsrc_t kr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)kblk, (short)0, kBlockBytes, kRawBufferWord3);
+  const __amdgpu_buffer_rsrc_t vr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)vblk, (short)0, kBlockBytes, kRawBufferWord3);
 #pragma unroll
   for (int it = 0; it < T::KLD; ++it)
-    __builtin_amdgcn_global_load_lds(kh + koff[it], LDS_PTR(buf + (it * 4 + w) * 1024), 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, LDS_PTR(buf + (it * 4 + w) * 1024), 16, koff[it],
+                                             64 * hf * D * 2, 0, 0);
   char* vb = buf + T::KBYTES;
 #pragma unroll
   for (int it = 0; it < T::VLD; ++it)
-    __builtin_amdgcn_global_load_lds(vh + voff[it], LDS_PTR(vb + (it * 4 + w) * 1024), 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, LDS_PTR(vb + (it * 4 + w) * 1024), 16, voff[it],
+                                             64 * hf * 2, 0, 0);
 }
 
 __device__ inline float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
@@ -208,6 +219,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
       kf[0][s2] = *reinterpret_cast<const bf16x8*>(kb + koff[s2]);
       kf[1][s2] = *reinterpret_cast<const bf16x8*>(kb + koff[s2] + 32 * D * 2);
     }
+    __builtin_amdgcn_sched_barrier(0);  // all K fragment reads issue before the first MFMA
     f32x16 sacc[2];
 #pragma unroll
     for (int r = 0; r < 16; ++r) sacc[0][r] = sacc[1][r] = 0.f;
