@@ -52,6 +52,7 @@ struct Q4 {                                   // one 32-row quarter of a block
 // Geometry of a chunk-relative block n and its token tau in the token layout.
 struct Tok {
   int T, H, W, NH, D, nbx, nS;
+  uint32_t qspan;  // bytes from a quarter's first token past its last unit
   // bytes from a block's first token to the first token of its quarter qq
   // (rows 32qq .. 32qq + 31: frame qq / 2, token rows 4 (qq % 2) ..)
   __device__ size_t quarter_bytes(int qq) const {
@@ -73,6 +74,9 @@ __device__ inline Tok make_tok(const BwdArgs& a) {
   t.D = a.D;
   t.nbx = a.W / 8;
   t.nS = (a.H / 8) * t.nbx;
+  // a quarter's rows lie in 4 token rows of one frame: its last 16-byte unit
+  // ends before token 3W + 8 (offsets checked against 32 bits on the host)
+  t.qspan = (uint32_t)((size_t)(3 * a.W + 8) * a.NH * a.D * 2);
   return t;
 }
 
@@ -106,23 +110,27 @@ __device__ inline void col_unit_offsets(int w, int lane, uint32_t (&off)[Q4<D>::
 }
 
 // Issue the direct loads of one quarter: a row tile (block base + per-lane
-// offsets) and / or a column tile.
+// offsets) and / or a column tile. Buffer loads: the scalar resource holds
+// the tile's base and extent, the lane offset is the vector offset, so the
+// loads need no vector address arithmetic.
 template <int D>
-__device__ __forceinline__ void load_rows(const char* qblk, const uint32_t* off,
+__device__ __forceinline__ void load_rows(const char* qblk, uint32_t span, const uint32_t* off,
                                           char* dst, int w) {  // qblk: the quarter's first token
+  const __amdgpu_buffer_rsrc_t r = raw_rsrc(qblk, span);
 #pragma unroll
   for (int it = 0; it < Q4<D>::RLD; ++it)
-    __builtin_amdgcn_global_load_lds(qblk + off[it], LDS_PTR(dst + (it * 4 + w) * 1024), 16, 0,
-                                     0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, LDS_PTR(dst + (it * 4 + w) * 1024), 16, off[it], 0,
+                                             0, 0);
 }
 
 template <int D>
 __device__ __forceinline__ void load_cols(const char* blk, const uint32_t* off,
                                           int qq, char* dst, int w) {
+  const __amdgpu_buffer_rsrc_t r = raw_rsrc(blk, D * 128 * 2);
 #pragma unroll
   for (int it = 0; it < Q4<D>::TLD; ++it)
-    __builtin_amdgcn_global_load_lds(blk + off[it] + 64 * qq, LDS_PTR(dst + (it * 4 + w) * 1024),
-                                     16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, LDS_PTR(dst + (it * 4 + w) * 1024), 16, off[it],
+                                             64 * qq, 0, 0);
 }
 
 // Issue the loads of quarter qq of one key block for the dQ kernel: K rows,
@@ -134,8 +142,8 @@ __device__ __forceinline__ void issue_dq(const Tok& tk, const char* kb, const ch
                                          int w) {
   using G = Q4<D>;
   const size_t qo = tk.quarter_bytes(qq);
-  load_rows<D>(kb + qo, roff, buf, w);
-  load_rows<D>(vb + qo, roff, buf + G::ROWB, w);
+  load_rows<D>(kb + qo, tk.qspan, roff, buf, w);
+  load_rows<D>(vb + qo, tk.qspan, roff, buf + G::ROWB, w);
   load_cols<D>(ktb, coff, qq, buf + 2 * G::ROWB, w);
 }
 
@@ -150,13 +158,14 @@ __device__ __forceinline__ void issue_dkdv(const Tok& tk, const char* qb, const 
                                            int qq, char* buf, int w) {
   using G = Q4<D>;
   const size_t qo = tk.quarter_bytes(qq);
-  load_rows<D>(qb + qo, roff, buf, w);
-  load_rows<D>(ob + qo, roff, buf + G::ROWB, w);
+  load_rows<D>(qb + qo, tk.qspan, roff, buf, w);
+  load_rows<D>(ob + qo, tk.qspan, roff, buf + G::ROWB, w);
   load_cols<D>(qtb, coff, qq, buf + 2 * G::ROWB, w);
   load_cols<D>(otb, coff, qq, buf + 2 * G::ROWB + G::TRB, w);
-  if (w == 0)
-    __builtin_amdgcn_global_load_lds(lb + 128 * qq + loff, LDS_PTR(buf + 2 * G::ROWB + 2 * G::TRB),
-                                     16, 0, 0);
+  if (w == 0)  // lb: the block's 256 floats (1 KB) of lse2 then delta
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(raw_rsrc(lb, 1024),
+                                             LDS_PTR(buf + 2 * G::ROWB + 2 * G::TRB), 16, loff,
+                                             128 * qq, 0, 0);
 }
 
 // B fragments of 32 rows (this wave's rows 32w + l32) of block n: D values

@@ -329,6 +329,11 @@ lcsa_status lcsa_block_sparse_attn_bwd(const lcsa_geom* g, const void* q, const 
   if (kmax < 1) return fail(LCSA_ERR_CAPACITY, "kmax %d < 1", kmax);
   if (!std::isfinite(scale) || scale < 0.f)
     return fail(LCSA_ERR_PARAM, "scale must be finite and >= 0 (0 = 1/sqrt(D))");
+  // a 32-row quarter of a block spans 4 token rows; its tiles are read with
+  // 32-bit offsets from the quarter's first token
+  if ((int64_t)(3 * (int64_t)g->width + 8) * g->heads * g->head_dim * 2 >= ((int64_t)1 << 31))
+    return fail(LCSA_ERR_CAPACITY, "%s: token rows of %d x %d x %d are too wide", fn, g->width,
+                g->heads, g->head_dim);
   if (reinterpret_cast<uintptr_t>(workspace) % 256)
     return fail(LCSA_ERR_ALIGN, "%s: workspace is not 256-byte aligned", fn);
   const BwdLayout lay = bwd_layout(*g);

@@ -45,6 +45,15 @@ __device__ inline int perm32(int r) {
   return 16 * (i >> 1) + 8 * gg + 4 * (i & 1) + j;
 }
 
+// Raw buffer resource over [base, base + bytes) for untyped dword loads
+// (word 3: 32-bit data format). A buffer load's address is this base plus a
+// 32-bit lane offset plus a scalar offset, and an offset at or past `bytes`
+// reads zeros instead of memory outside the range.
+__device__ inline __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
 // Wait for all of this wave's outstanding vector memory operations
 // (s_waitcnt vmcnt(0); expcnt and lgkmcnt left at their no-wait maxima).
 __device__ inline void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }

@@ -16,7 +16,7 @@
 // with an online softmax in base 2 (exp2 of a log2e-prescaled logit).
 // A key block is consumed in two 64-key halves. Each half (K [64][D] plus
 // V^T [D][64], 32 KB at D = 128) goes straight from global memory into one
-// of two LDS buffers (global_load_lds, no register staging): while one
+// of two LDS buffers (buffer loads into LDS, no register staging): while one
 // half is computed the next one is in flight, so 64 KB of LDS per
 // workgroup and two workgroups per CU. LDS rows are XOR-swizzled in
 // 16-byte chunks so the fragment reads are bank-conflict free, and K rows
@@ -80,9 +80,6 @@ __device__ __forceinline__ void subtile_offsets(int w, int lane, uint32_t* koff,
   }
 }
 
-// Raw buffer resource word 3 for untyped dword loads (32-bit data format).
-constexpr int kRawBufferWord3 = 0x00020000;
-
 // Issue the loads of half hf (keys 64hf..64hf+63) into one LDS buffer; w is
 // the (uniform) wave index. Buffer loads: the resource holds the block base
 // and its size (an offset past it would read zeros, never another block),
@@ -93,10 +90,8 @@ __device__ __forceinline__ void load_subtile(const char* kblk, const char* vblk,
                                              int w, const uint32_t* koff, const uint32_t* voff) {
   using T = Tile<D>;
   constexpr int kBlockBytes = 128 * D * 2;
-  const __amdgpu_buffer_rsrc_t kr =
-      __builtin_amdgcn_make_buffer_rsrc((void*)kblk, (short)0, kBlockBytes, kRawBufferWord3);
-  const __amdgpu_buffer_rsrc_t vr =
-      __builtin_amdgcn_make_buffer_rsrc((void*)vblk, (short)0, kBlockBytes, kRawBufferWord3);
+  const __amdgpu_buffer_rsrc_t kr = raw_rsrc(kblk, kBlockBytes);
+  const __amdgpu_buffer_rsrc_t vr = raw_rsrc(vblk, kBlockBytes);
 #pragma unroll
   for (int it = 0; it < T::KLD; ++it)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, LDS_PTR(buf + (it * 4 + w) * 1024), 16, koff[it],
