@@ -262,6 +262,12 @@ def test_backward_workspace_size_and_validation(lib):
         call(kmax=0)
     with pytest.raises(L.LcsaError, match="LCSA_ERR_PARAM"):
         call(scale=-1.0)
+    # a block quarter spans 4 token rows read with 32-bit offsets: (3W + 8) NH D 2 bytes
+    # must stay below 2^31 (W = 43688 is the first multiple of 8 past it at NH 64, D 128)
+    wide = L.make_geom(1, 64, 128, 4, 16, 43688, L.LCSA_BF16)
+    assert (3 * 43688 + 8) * 64 * 128 * 2 >= 2 ** 31 > (3 * 43680 + 8) * 64 * 128 * 2
+    with pytest.raises(L.LcsaError, match="LCSA_ERR_CAPACITY.*too wide"):
+        call(geom=wide, ws=Buf(FAKE, L.lcsa_attn_bwd_workspace_size(wide)))
     lib_ = L.load_library()
     assert lib_.lcsa_block_sparse_attn_bwd(ctypes.byref(g), None, FAKE, FAKE, FAKE, FAKE, FAKE,
                                            FAKE, FAKE, 4, ctypes.c_float(0), FAKE, FAKE, FAKE,
