@@ -6,12 +6,14 @@
 // its mean ([FN] "FlashVSR" note, Key design 2: block-mean pooling before
 // the coarse block map).
 //
-// One workgroup moves one (batch, head, block) for q, k and v. The token
-// layout keeps a token's D channels contiguous (D*esize = 128..512 bytes),
-// so every read is a run of whole 16-byte chunks; every write is a fully
-// contiguous 128 x D tile. V is written transposed ([D][128]) because the
-// attention kernel feeds V^T to the matrix cores as the A operand. Block
-// means are accumulated in float64 (exact for bf16 inputs) and written as
+// One workgroup moves one tile: one of q, k or v for one (batch, head,
+// block), so reads and writes of different workgroups overlap and a small
+// grid still spreads over the chip. The token layout keeps a token's D
+// channels contiguous (D*esize = 128..512 bytes), so every read is a run of
+// whole 16-byte chunks; every write is a fully contiguous 128 x D tile. V is
+// written transposed ([D][128]) because the attention kernel feeds V^T to
+// the matrix cores as the A operand. Block means of q and k are accumulated
+// in float64 (exact for bf16 inputs of moderate range) and written as
 // float64, so the draft selection downstream takes its decision on exact
 // pooled values. HBM-bound: the algorithmic traffic of one (block, head) is
 // 3 tiles read + 3 tiles written + 2 pooled rows.
@@ -80,14 +82,13 @@ __device__ inline void load_block(const PartitionArgs& a, const char* src, int b
   }
 }
 
-// Store the chunks as a contiguous [128][D] tile and return the thread's
-// float64 partial column sums in red[tid][0 .. EPC).
+// Store the chunks as a contiguous [128][D] tile; acc gets the thread's
+// float64 column sums of its EPC channels over its ITERS tokens.
 template <int ESZ, int D>
 __device__ inline void store_tile_sum(char* dst, const u32x4 (&v)[Geo<ESZ, D>::ITERS],
-                                      double* red_row) {
+                                      double (&acc)[Geo<ESZ, D>::EPC]) {
   using G = Geo<ESZ, D>;
   const int c = threadIdx.x % G::CPT, tsub = threadIdx.x / G::CPT;
-  double acc[G::EPC];
 #pragma unroll
   for (int e = 0; e < G::EPC; ++e) acc[e] = 0.0;
 #pragma unroll
@@ -99,98 +100,111 @@ __device__ inline void store_tile_sum(char* dst, const u32x4 (&v)[Geo<ESZ, D>::I
 #pragma unroll
     for (int e = 0; e < G::EPC; ++e) acc[e] += w[e];
   }
-#pragma unroll
-  for (int e = 0; e < G::EPC; ++e) red_row[e] = acc[e];
-}
-
-// Column d's block mean from the partial sums (fixed summation order).
-template <int ESZ, int D>
-__device__ inline double block_mean(const double* red, int d) {
-  using G = Geo<ESZ, D>;
-  const int cc = d / G::EPC, e = d % G::EPC;
-  double s = 0.0;
-  for (int ts = 0; ts < G::TPI; ++ts) s += red[(ts * G::CPT + cc) * G::EPC + e];
-  return s / 128.0;
 }
 
 template <int ESZ, int D>
 __global__ __launch_bounds__(kThreads) void partition_pool_kernel(PartitionArgs a) {
   using G = Geo<ESZ, D>;
-  __shared__ double red_q[kThreads * G::EPC];
-  __shared__ double red_k[kThreads * G::EPC];
-  __shared__ __attribute__((aligned(16))) char vstage[128 * G::PITCH];
+  static_assert(64 % G::CPT == 0, "a wave holds whole groups of column chunks");
+  constexpr int kWaves = kThreads / 64;
+  // one LDS buffer for either role: the V stage, or the per-wave column sums
+  __shared__ __attribute__((aligned(16))) char smem[128 * G::PITCH];
+  static_assert(kWaves * D * sizeof(double) <= sizeof(smem), "column sums fit the stage");
 
   // heads vary fastest across workgroups: the heads of one block read the
-  // same 128 token rows ([NH][D] contiguous per token) at about the same time
+  // same 128 token rows ([NH][D] contiguous per token) at about the same
+  // time; then the tensor (k, v, q), then the block
   const int nby = a.H / 8, nbx = a.W / 8, nS = nby * nbx;
   const int nblk = (a.T / 2) * nS;
-  const int h = blockIdx.x % a.NH;
-  const int n = (blockIdx.x / a.NH) % nblk;
-  const int b = blockIdx.x / (a.NH * nblk);
+  const bool has_q = a.q != nullptr;
+  const int roles = has_q ? 3 : 2;
+  int idx = blockIdx.x;
+  const int h = idx % a.NH;
+  idx /= a.NH;
+  const int role = idx % roles;  // 0: k, 1: v, 2: q (uniform per workgroup)
+  idx /= roles;
+  const int n = idx % nblk;
+  const int b = idx / nblk;
   const int bt = n / nS, s = n % nS, by = s / nbx, bx = s % nbx;
-  const int nq = nblk;
   const size_t tile = (size_t)128 * D;
   const int slot = (a.first_slot + bt) % a.n_slots;
   const size_t ring_blk = (((size_t)b * a.NH + h) * a.n_slots + slot) * nS + s;
   const int tid = threadIdx.x;
-  const bool has_q = a.q != nullptr;
 
-  // all global loads first: up to 3 x 128 bytes per thread in flight
-  u32x4 vq[G::ITERS], vk[G::ITERS], vv[G::ITERS];
-  if (has_q) load_block<ESZ, D>(a, (const char*)a.q, b, h, bt, by, bx, vq);
-  load_block<ESZ, D>(a, (const char*)a.k, b, h, bt, by, bx, vk);
-  load_block<ESZ, D>(a, (const char*)a.v, b, h, bt, by, bx, vv);
+  u32x4 v[G::ITERS];
+  const void* src = role == 0 ? a.k : role == 1 ? a.v : a.q;
+  load_block<ESZ, D>(a, (const char*)src, b, h, bt, by, bx, v);
 
-  const size_t qb = ((size_t)b * a.NH + h) * nq + n;
-  if (has_q) store_tile_sum<ESZ, D>((char*)a.q_blk + qb * tile * ESZ, vq, red_q + tid * G::EPC);
-  store_tile_sum<ESZ, D>((char*)a.k_ring + ring_blk * tile * ESZ, vk, red_k + tid * G::EPC);
-  {
+  if (role == 1) {
+    // v: stage the block, then write it transposed ([D][128])
     const int c = tid % G::CPT, tsub = tid / G::CPT;
 #pragma unroll
     for (int it = 0; it < G::ITERS; ++it) {
       const int tau = it * G::TPI + tsub;
-      *reinterpret_cast<u32x4*>(vstage + tau * G::PITCH + c * 16) = vv[it];
+      *reinterpret_cast<u32x4*>(smem + tau * G::PITCH + c * 16) = v[it];
     }
-  }
-  __syncthreads();
-
-  if (tid < D) {
-    if (has_q) a.q_pool[qb * D + tid] = block_mean<ESZ, D>(red_q, tid);
-    // k means go d-major into the pooled ring
-    a.kpool_ring[((((size_t)b * a.NH + h) * a.n_slots + slot) * D + tid) * nS + s] =
-        block_mean<ESZ, D>(red_k, tid);
-  }
-  // v: write the staged block transposed ([D][128])
-  char* vdst = (char*)a.v_ring + ring_blk * tile * ESZ;
-  constexpr int KC = 128 / G::EPC;  // 16-byte chunks per transposed row
+    __syncthreads();
+    char* vdst = (char*)a.v_ring + ring_blk * tile * ESZ;
+    constexpr int KC = 128 / G::EPC;  // 16-byte chunks per transposed row
 #pragma unroll
-  for (int it = 0; it < G::ITERS; ++it) {
-    const int e = it * kThreads + tid;
-    const int d = e / KC, kc = e % KC;
-    uint32_t w[4];
-    if constexpr (ESZ == 2) {
+    for (int it = 0; it < G::ITERS; ++it) {
+      const int e = it * kThreads + tid;
+      const int d = e / KC, kc = e % KC;
+      uint32_t w[4];
+      if constexpr (ESZ == 2) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t lo =
-            *reinterpret_cast<const uint16_t*>(vstage + (kc * 8 + 2 * u) * G::PITCH + d * 2);
-        const uint32_t hi =
-            *reinterpret_cast<const uint16_t*>(vstage + (kc * 8 + 2 * u + 1) * G::PITCH + d * 2);
-        w[u] = lo | (hi << 16);
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t lo =
+              *reinterpret_cast<const uint16_t*>(smem + (kc * 8 + 2 * u) * G::PITCH + d * 2);
+          const uint32_t hi =
+              *reinterpret_cast<const uint16_t*>(smem + (kc * 8 + 2 * u + 1) * G::PITCH + d * 2);
+          w[u] = lo | (hi << 16);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          w[u] = *reinterpret_cast<const uint32_t*>(smem + (kc * 4 + u) * G::PITCH + d * 4);
       }
-    } else {
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        w[u] = *reinterpret_cast<const uint32_t*>(vstage + (kc * 4 + u) * G::PITCH + d * 4);
+      *reinterpret_cast<u32x4*>(vdst + ((size_t)d * 128 + kc * G::EPC) * ESZ) =
+          u32x4{w[0], w[1], w[2], w[3]};
     }
-    *reinterpret_cast<u32x4*>(vdst + ((size_t)d * 128 + kc * G::EPC) * ESZ) =
-        u32x4{w[0], w[1], w[2], w[3]};
+    return;
+  }
+
+  // q or k: the row-major tile, then the block mean of each channel
+  const size_t qb = ((size_t)b * a.NH + h) * nblk + n;
+  char* dst = role == 0 ? (char*)a.k_ring + ring_blk * tile * ESZ
+                        : (char*)a.q_blk + qb * tile * ESZ;
+  double acc[G::EPC];
+  store_tile_sum<ESZ, D>(dst, v, acc);
+  // the lanes of a wave holding the same column chunk (lane % CPT) add up,
+  // in a fixed xor order; then the waves' sums in order
+  const int lane = tid & 63, w = tid >> 6;
+#pragma unroll
+  for (int m = G::CPT; m < 64; m <<= 1)
+#pragma unroll
+    for (int e = 0; e < G::EPC; ++e) acc[e] += __shfl_xor(acc[e], m);
+  double* red = reinterpret_cast<double*>(smem);  // [kWaves][D]
+  if (lane < G::CPT)
+#pragma unroll
+    for (int e = 0; e < G::EPC; ++e) red[w * D + lane * G::EPC + e] = acc[e];
+  __syncthreads();
+  if (tid < D) {
+    double sum = 0.0;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) sum += red[ww * D + tid];
+    const double mean = sum / 128.0;
+    if (role == 2)
+      a.q_pool[qb * D + tid] = mean;
+    else  // k means go d-major into the pooled ring
+      a.kpool_ring[((((size_t)b * a.NH + h) * a.n_slots + slot) * D + tid) * nS + s] = mean;
   }
 }
 
 template <int ESZ, int D>
 hipError_t launch(const PartitionArgs& a, hipStream_t s) {
   const long long nblk = (long long)(a.T / 2) * (a.H / 8) * (a.W / 8);
-  const long long wgs = nblk * a.NH * a.B;
+  const long long wgs = nblk * a.NH * a.B * (a.q ? 3 : 2);
   hipLaunchKernelGGL((partition_pool_kernel<ESZ, D>), dim3((unsigned)wgs), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
