@@ -47,8 +47,9 @@ __device__ inline int perm32(int r) {
 
 // Raw buffer resource over [base, base + bytes) for untyped dword loads
 // (word 3: 32-bit data format). A buffer load's address is this base plus a
-// 32-bit lane offset plus a scalar offset, and an offset at or past `bytes`
-// reads zeros instead of memory outside the range.
+// 32-bit lane offset plus a scalar offset; the lane offset is range-checked
+// against `bytes` (one at or past it reads zeros), the scalar offset is not,
+// so callers keep scalar offset + lane offset inside the range themselves.
 __device__ inline __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                            0x00020000);

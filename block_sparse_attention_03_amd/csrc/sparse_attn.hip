@@ -82,8 +82,8 @@ __device__ __forceinline__ void subtile_offsets(int w, int lane, uint32_t* koff,
 
 // Issue the loads of half hf (keys 64hf..64hf+63) into one LDS buffer; w is
 // the (uniform) wave index. Buffer loads: the resource holds the block base
-// and its size (an offset past it would read zeros, never another block),
-// the half offset is the scalar offset, so a load needs no vector address
+// and its size, the half offset is the scalar offset (half offset + lane
+// offset stay inside the block), so a load needs no vector address
 // arithmetic at all.
 template <int D>
 __device__ __forceinline__ void load_subtile(const char* kblk, const char* vblk, int hf, char* buf,
