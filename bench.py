@@ -1,5 +1,7 @@
 """LCSA benchmark: one streaming step = partition+pool -> draft mask ->
-block-sparse attention -> cache evict, through the C-ABI, on one GPU.
+block-sparse attention -> cache evict, through the C-ABI, on one GPU, on one
+stream (--overlap-v moves the transposed-v part of the partition to a second
+stream; measured slower).
 
 Default workload: the steady-state streaming step at 768x1408 (2 new latent
 frames of 48x88 tokens, 12 heads, head_dim 128, bf16, a 6-frame KV cache,
@@ -39,6 +41,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="step_768x1408")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--overlap-v", action="store_true",
+                    help="run the transposed-v part of the partition on a second stream, under "
+                         "the q/k part and the lists (measured slower: the cross-stream "
+                         "fork and join cost more than the overlap saves)")
     ap.add_argument("--cpu-sample-heads", type=int, default=12)
     ap.add_argument("--cpu-sample-steps", type=int, default=4)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -108,6 +114,8 @@ def main():
     torch.cuda.synchronize()
     geom = L.make_geom(w.batch, w.heads, w.head_dim, w.frames, w.height, w.width, code)
     stream = torch.cuda.current_stream()
+    # --overlap-v: a second stream (default priority) for the transposed-v part
+    side = torch.cuda.Stream() if args.overlap_v else None
     tb_first = t_first // 2
 
     import ctypes
@@ -144,6 +152,7 @@ def main():
             else:
                 self.kmax = L.lcsa_max_topk(geom, tb_first, probe, self.params)
             self.bufs = L.StepBuffers(geom, self.kmax, device=dev, with_lse=sp.backward)
+            self.fork_join = (torch.cuda.Event(), torch.cuda.Event())
             self.keep = sp.cap_tb if sp.cache_frames else 0  # cold chunks: empty after each step
             if sp.backward:  # training shape: the keys are the chunk's own blocks
                 assert sp.cache_frames == 0 and not self.seg
@@ -157,7 +166,13 @@ def main():
         def run(self, tb, q, k, v, ev=None, evb=None):
             c, b = self.cache, self.bufs
             slot = c.append(w.frames // 2, tb)
-            L.lcsa_partition_pool(geom, q, k, v, b.q_blk, b.q_pool, c.c, slot, stream)
+            join = None
+            if side is not None:  # the transposed v tiles under the q/k part and the lists
+                join = L.fork_v_part(geom, v, c.c, slot, stream, side, self.fork_join)
+                L.lcsa_partition_pool_parts(geom, q, k, None, b.q_blk, b.q_pool, c.c, slot,
+                                            L.PART_QK, stream)
+            else:
+                L.lcsa_partition_pool(geom, q, k, v, b.q_blk, b.q_pool, c.c, slot, stream)
             if self.seg:
                 L.lcsa_segment_lists(geom, tb, c.c, self.seg, self.kmax, b.sel_idx, b.sel_cnt,
                                      stream)
@@ -167,6 +182,8 @@ def main():
             else:
                 L.lcsa_draft_mask(geom, b.q_pool, tb, c.c, self.params, self.kmax, b.sel_idx,
                                   b.sel_cnt, None, stream)
+            if join is not None:
+                stream.wait_event(join)
             if ev is not None:
                 ev[0].record(stream)
             if self.seg:

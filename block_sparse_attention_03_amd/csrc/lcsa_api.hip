@@ -134,17 +134,24 @@ BwdLayout bwd_layout(const lcsa_geom& g) {
 
 extern "C" {
 
-lcsa_status lcsa_partition_pool(const lcsa_geom* g, const void* q, const void* k, const void* v,
-                                void* q_blk, double* q_pool, lcsa_kv_cache* cache,
-                                int32_t first_slot, void* stream) {
+// lcsa_partition_pool and lcsa_partition_pool_parts: `parts` selects the
+// q/k tiles with their means and / or the transposed v tiles.
+static lcsa_status partition_parts(const lcsa_geom* g, const void* q, const void* k,
+                                   const void* v, void* q_blk, double* q_pool,
+                                   lcsa_kv_cache* cache, int32_t first_slot, int32_t parts,
+                                   void* stream, const char* fn) {
   lcsa_status st;
-  if ((st = check_geom(g, "lcsa_partition_pool")) || (st = check_cache(cache)) ||
+  if ((st = check_geom(g, fn)) || (st = check_cache(cache)) ||
       (st = check_matches_cache(g, cache)))
     return st;
-  const bool has_q = q || q_blk || q_pool;
+  if (parts < 1 || parts > (LCSA_PART_QK | LCSA_PART_V))
+    return fail(LCSA_ERR_PARAM, "%s: parts %d is not LCSA_PART_QK, LCSA_PART_V or both", fn,
+                parts);
+  const bool do_qk = parts & LCSA_PART_QK, do_v = parts & LCSA_PART_V;
+  const bool has_q = do_qk && (q || q_blk || q_pool);
   if (has_q && !(q && q_blk && q_pool))
     return fail(LCSA_ERR_NULL, "q, q_blk and q_pool must be all NULL or all non-NULL");
-  if ((st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
+  if ((do_qk && (st = check_ptr(k, "k"))) || (do_v && (st = check_ptr(v, "v"))) ||
       (has_q && ((st = check_ptr(q, "q")) || (st = check_ptr(q_blk, "q_blk")) ||
                  (st = check_ptr(q_pool, "q_pool")))))
     return st;
@@ -161,8 +168,9 @@ lcsa_status lcsa_partition_pool(const lcsa_geom* g, const void* q, const void* k
   }
   PartitionArgs a{};
   a.q = has_q ? q : nullptr;
-  a.k = k;
-  a.v = v;
+  a.k = do_qk ? k : nullptr;
+  a.v = do_v ? v : nullptr;
+  a.parts = parts;
   a.q_blk = q_blk;
   a.q_pool = q_pool;
   a.k_ring = cache->k_ring;
@@ -177,7 +185,22 @@ lcsa_status lcsa_partition_pool(const lcsa_geom* g, const void* q, const void* k
   a.n_slots = cache->n_slots;
   a.first_slot = first_slot;
   a.dtype = g->dtype;
-  return device_status(launch_partition_pool(a, (hipStream_t)stream), "lcsa_partition_pool");
+  return device_status(launch_partition_pool(a, (hipStream_t)stream), fn);
+}
+
+lcsa_status lcsa_partition_pool(const lcsa_geom* g, const void* q, const void* k, const void* v,
+                                void* q_blk, double* q_pool, lcsa_kv_cache* cache,
+                                int32_t first_slot, void* stream) {
+  return partition_parts(g, q, k, v, q_blk, q_pool, cache, first_slot,
+                         LCSA_PART_QK | LCSA_PART_V, stream, "lcsa_partition_pool");
+}
+
+lcsa_status lcsa_partition_pool_parts(const lcsa_geom* g, const void* q, const void* k,
+                                      const void* v, void* q_blk, double* q_pool,
+                                      lcsa_kv_cache* cache, int32_t first_slot, int32_t parts,
+                                      void* stream) {
+  return partition_parts(g, q, k, v, q_blk, q_pool, cache, first_slot, parts, stream,
+                         "lcsa_partition_pool_parts");
 }
 
 lcsa_status lcsa_draft_mask(const lcsa_geom* gq, const double* q_pool, int64_t q_first_abs_tb,

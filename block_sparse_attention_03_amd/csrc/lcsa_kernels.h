@@ -30,6 +30,7 @@ struct PartitionArgs {
   int32_t B, NH, D, T, H, W;
   int32_t n_slots, first_slot;
   int32_t dtype;
+  int32_t parts;            // LCSA_PART_QK | LCSA_PART_V: which tiles this launch moves
 };
 
 struct DraftArgs {

@@ -117,11 +117,20 @@ __global__ __launch_bounds__(kThreads) void partition_pool_kernel(PartitionArgs 
   const int nby = a.H / 8, nbx = a.W / 8, nS = nby * nbx;
   const int nblk = (a.T / 2) * nS;
   const bool has_q = a.q != nullptr;
-  const int roles = has_q ? 3 : 2;
+  const bool do_qk = a.parts & LCSA_PART_QK, do_v = a.parts & LCSA_PART_V;
+  const int roles = (do_qk ? (has_q ? 2 : 1) : 0) + (do_v ? 1 : 0);
   int idx = blockIdx.x;
   const int h = idx % a.NH;
   idx /= a.NH;
-  const int role = idx % roles;  // 0: k, 1: v, 2: q (uniform per workgroup)
+  // 0: k, 1: v, 2: q (uniform per workgroup), in that order among the
+  // requested parts
+  int role, rr = idx % roles;
+  if (do_qk && rr == 0) {
+    role = 0;
+  } else {
+    rr -= do_qk ? 1 : 0;
+    role = (do_v && rr == 0) ? 1 : 2;
+  }
   idx /= roles;
   const int n = idx % nblk;
   const int b = idx / nblk;
@@ -204,7 +213,9 @@ __global__ __launch_bounds__(kThreads) void partition_pool_kernel(PartitionArgs 
 template <int ESZ, int D>
 hipError_t launch(const PartitionArgs& a, hipStream_t s) {
   const long long nblk = (long long)(a.T / 2) * (a.H / 8) * (a.W / 8);
-  const long long wgs = nblk * a.NH * a.B * (a.q ? 3 : 2);
+  const bool do_qk = a.parts & LCSA_PART_QK, do_v = a.parts & LCSA_PART_V;
+  const long long roles = (do_qk ? (a.q ? 2 : 1) : 0) + (do_v ? 1 : 0);
+  const long long wgs = nblk * a.NH * a.B * roles;
   hipLaunchKernelGGL((partition_pool_kernel<ESZ, D>), dim3((unsigned)wgs), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }

@@ -81,6 +81,8 @@ def load_library(path: str = LIB_PATH):
         "lcsa_max_topk": [G, c_int64, C, P, POINTER(c_int32)],
         "lcsa_partition_pool": [G, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, C,
                                 c_int32, c_void_p],
+        "lcsa_partition_pool_parts": [G, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, C,
+                                      c_int32, c_int32, c_void_p],
         "lcsa_draft_mask": [G, c_void_p, c_int64, C, P, c_int32, c_void_p, c_void_p, c_void_p,
                             c_void_p],
         "lcsa_block_sparse_attn": [G, c_void_p, C, c_void_p, c_void_p, c_int32, c_float,
@@ -200,6 +202,35 @@ def lcsa_partition_pool(geom: Geom, q, k, v, q_blk, q_pool, cache: KvCacheStruct
     _check(lib.lcsa_partition_pool(ctypes.byref(geom), _ptr(q), _ptr(k), _ptr(v), _ptr(q_blk),
                                    _ptr(q_pool), ctypes.byref(cache), first_slot,
                                    _stream(stream)))
+
+
+PART_QK, PART_V = 1, 2  # LCSA_PART_QK, LCSA_PART_V
+
+
+def lcsa_partition_pool_parts(geom: Geom, q, k, v, q_blk, q_pool, cache: KvCacheStruct,
+                              first_slot: int, parts: int, stream=None):
+    lib = load_library()
+    _check(lib.lcsa_partition_pool_parts(ctypes.byref(geom), _ptr(q), _ptr(k), _ptr(v),
+                                         _ptr(q_blk), _ptr(q_pool), ctypes.byref(cache),
+                                         first_slot, parts, _stream(stream)))
+
+
+def fork_v_part(geom: Geom, v, cache: KvCacheStruct, first_slot: int, stream, side_stream,
+                events=None):
+    """Start the transposed-v part of the partition on side_stream (a torch
+    stream) once the work already queued on `stream` is done: the ring slot
+    it fills may have been read by that work. Returns the event the attention
+    launch on `stream` must wait for. `events` may pass a reusable (fork,
+    join) pair of torch events."""
+    import torch
+    main = stream if stream is not None else torch.cuda.current_stream()
+    fork, join = events if events is not None else (torch.cuda.Event(), torch.cuda.Event())
+    fork.record(main)
+    side_stream.wait_event(fork)
+    lcsa_partition_pool_parts(geom, None, None, v, None, None, cache, first_slot, PART_V,
+                              side_stream)
+    join.record(side_stream)
+    return join
 
 
 def lcsa_draft_mask(geom: Geom, q_pool, q_first_abs_tb: int, cache: KvCacheStruct,
@@ -345,10 +376,13 @@ class StepBuffers:
 
 def run_step(geom: Geom, q, k, v, cache: KVCache, first_abs_tb: int, params: SelectParams,
              bufs: StepBuffers | None = None, keep_tb: int | None = None, stream=None,
-             want_probs=False, want_lse=False, scale: float = 0.0, local: bool = False):
+             want_probs=False, want_lse=False, scale: float = 0.0, local: bool = False,
+             side_stream=None):
     """One LCSA invocation through the C-ABI: append, partition+pool, draft
     (or, with local=True, the FlashVSR+ local lists: every allowed key
-    block), attention, evict. Returns the StepBuffers holding the results."""
+    block), attention, evict. With a side_stream, the transposed-v part of
+    the partition runs there, under the q/k part and the draft, and the
+    attention waits for it. Returns the StepBuffers holding the results."""
     n_tb = geom.frames // 2
     first_slot = cache.append(n_tb, first_abs_tb)
     if local:
@@ -360,13 +394,22 @@ def run_step(geom: Geom, q, k, v, cache: KVCache, first_abs_tb: int, params: Sel
         bufs = StepBuffers(geom, kmax, device=q.device,
                            with_probs_keys=n_keys if want_probs and not local else 0,
                            with_lse=want_lse)
-    lcsa_partition_pool(geom, q, k, v, bufs.q_blk, bufs.q_pool, cache.c, first_slot, stream)
+    join = None
+    if side_stream is not None:
+        join = fork_v_part(geom, v, cache.c, first_slot, stream, side_stream)
+        lcsa_partition_pool_parts(geom, q, k, None, bufs.q_blk, bufs.q_pool, cache.c, first_slot,
+                                  PART_QK, stream)
+    else:
+        lcsa_partition_pool(geom, q, k, v, bufs.q_blk, bufs.q_pool, cache.c, first_slot, stream)
     if local:
         lcsa_local_lists(geom, first_abs_tb, cache.c, params, bufs.kmax, bufs.sel_idx,
                          bufs.sel_cnt, stream)
     else:
         lcsa_draft_mask(geom, bufs.q_pool, first_abs_tb, cache.c, params, bufs.kmax,
                         bufs.sel_idx, bufs.sel_cnt, bufs.probs, stream)
+    if join is not None:
+        import torch
+        (stream if stream is not None else torch.cuda.current_stream()).wait_event(join)
     lcsa_block_sparse_attn(geom, bufs.q_blk, cache.c, bufs.sel_idx, bufs.sel_cnt, bufs.kmax,
                            bufs.out, bufs.lse, scale, stream)
     if keep_tb is not None:

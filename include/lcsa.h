@@ -187,6 +187,23 @@ lcsa_status lcsa_partition_pool(const lcsa_geom* g, const void* q, const void* k
                                 lcsa_kv_cache* cache, int32_t first_slot,
                                 void* stream);
 
+/* One part of lcsa_partition_pool, for callers that overlap the two parts
+ * on two streams ([HW] 2.2 step 1 and step 3's pooling, as above).
+ * parts = LCSA_PART_QK moves q (when given) and k into their blocks with
+ * the block means: everything lcsa_draft_mask reads. parts = LCSA_PART_V
+ * writes the transposed v blocks into the ring, which only
+ * lcsa_block_sparse_attn reads. Both bits together equal
+ * lcsa_partition_pool. A pointer the requested parts do not touch may be
+ * NULL (v for LCSA_PART_QK alone; q, k, q_blk, q_pool for LCSA_PART_V
+ * alone); the rules of lcsa_partition_pool hold for the others. The two
+ * parts write disjoint memory. Any other value of parts is LCSA_ERR_PARAM. */
+#define LCSA_PART_QK 1
+#define LCSA_PART_V 2
+lcsa_status lcsa_partition_pool_parts(const lcsa_geom* g, const void* q, const void* k,
+                                      const void* v, void* q_blk, double* q_pool,
+                                      lcsa_kv_cache* cache, int32_t first_slot, int32_t parts,
+                                      void* stream);
+
 /* Steps 3-4 ([HW] 2.2 steps 2-3; [FN] Key designs 1-3). For each query
  * block of the chunk (geometry gq, first temporal block q_first_abs_tb) and
  * every key block held by the cache: candidate iff the key's TB is not
@@ -316,7 +333,7 @@ lcsa_status lcsa_block_sparse_attn_bwd(const lcsa_geom* g, const void* q, const 
 /* Text of the last error on this thread ("" after success). */
 const char* lcsa_last_error(void);
 
-/* Interface version of this header: 2. */
+/* Interface version of this header: 3. */
 int32_t lcsa_abi_version(void);
 
 #ifdef __cplusplus

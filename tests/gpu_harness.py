@@ -47,9 +47,10 @@ def lib_params(w) -> L.SelectParams:
 class Stream:
     """Runs the same stream of chunks on the GPU and in the oracle."""
 
-    def __init__(self, w, device, seed=None, zero_q=False):
+    def __init__(self, w, device, seed=None, zero_q=False, side_stream=None):
         import torch
         self.w = w
+        self.side = side_stream  # run the transposed-v partition part there
         self.dev = device
         self.seed = w.seed if seed is None else seed
         self.zero_q = zero_q
@@ -89,7 +90,8 @@ class Stream:
             f"D {w.head_dim}, {w.dtype})")
         local = w.lists == "local"
         bufs = L.run_step(self.geom, q, k, v, self.gcache, tb0, self.lp, keep_tb=w.cap_tb,
-                          want_probs=want_probs and not local, want_lse=True, local=local)
+                          want_probs=want_probs and not local, want_lse=True, local=local,
+                          side_stream=self.side)
         torch.cuda.synchronize()
         g = {"sel_idx": bufs.sel_idx.cpu().numpy(), "sel_cnt": bufs.sel_cnt.cpu().numpy(),
              "out": bufs.out, "lse": bufs.lse.cpu().numpy(),

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(lib):
     assert len(names) >= 10
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.lcsa_abi_version() == 2
+    assert lib.lcsa_abi_version() == 3
 
 
 FAKE = 0x10000  # aligned, never dereferenced: validation fails first
@@ -145,6 +145,18 @@ def test_validation_rejects_bad_input_before_any_device_call(lib):
     # slot not held
     expect(6, L.lcsa_partition_pool, geom, ok, ok, ok, ok, ok, c, 2, s)
     expect(4, L.lcsa_partition_pool, geom, ok, ok, ok, ok, ok, c, 9, s)
+    # the partition's parts: only LCSA_PART_QK, LCSA_PART_V or both; the pointers a part
+    # touches are checked, the others may be NULL
+    P = L.lcsa_partition_pool_parts
+    expect(4, P, geom, ok, ok, ok, ok, ok, c, 0, 0, s)
+    expect(4, P, geom, ok, ok, ok, ok, ok, c, 0, 4, s)
+    expect(1, P, geom, None, None, None, None, None, c, 0, L.PART_V, s)      # v missing
+    expect(1, P, geom, ok, None, None, ok, ok, c, 0, L.PART_QK, s)           # k missing
+    expect(1, P, geom, ok, ok, None, None, ok, c, 0, L.PART_QK, s)           # q without q_blk
+    expect(5, P, geom, None, None, _P(FAKE + 8), None, None, c, 0, L.PART_V, s)
+    expect(6, P, geom, None, None, ok, None, None, c, 2, L.PART_V, s)        # slot not held
+    expect(2, P, L.make_geom(1, 12, 128, 3, 48, 88, 0), None, ok, None, None, None, c, 0,
+           L.PART_QK, s)
     # selection parameters
     expect(4, L.lcsa_draft_mask, geom, ok, 0, c, L.make_params(local_range=10), 64, ok, ok, None, s)
     expect(4, L.lcsa_draft_mask, geom, ok, 0, c, L.make_params(local_range=0), 64, ok, ok, None, s)

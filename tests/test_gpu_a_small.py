@@ -94,6 +94,32 @@ def test_small_streaming_with_cache(dev):
     say(f"small stream: {stats}")
 
 
+def test_two_stream_partition_matches_one_stream(dev):
+    """The transposed-v part of the partition on a second stream (forked after
+    the previous step, joined before the attention) gives bitwise the same
+    lists, outputs, q blocks and ring contents as the one-stream step, step
+    after step while ring slots are reused, and matches the oracle."""
+    w = small(frames=2, cache_frames=6, cap_tb=3, local_range=5, ratio=(1, 4))
+    one = Stream(w, dev)
+    two = Stream(w, dev, side_stream=torch.cuda.Stream())
+    for n in range(5):
+        g1, _ = one.step(want_probs=False)
+        g2, ref = two.step(want_probs=False)
+        for key in ("sel_idx", "sel_cnt", "lse"):
+            assert np.array_equal(g1[key], g2[key]), key
+        for key in ("out", "q_blk"):
+            assert torch.equal(g1[key], g2[key]), key
+        slots, _ = two.gcache.view()
+        assert slots == one.gcache.view()[0]
+        for sl in slots:  # the blocks the caches hold (other slots were never written)
+            for ring in ("k_ring", "v_ring", "kpool_ring"):
+                assert torch.equal(getattr(one.gcache, ring)[:, :, sl],
+                                   getattr(two.gcache, ring)[:, :, sl]), (ring, sl)
+        check_layouts(two, g2, ref)
+        stats = compare_step(w, g2, ref)
+    say(f"two-stream partition: {stats}")
+
+
 def test_equal_scores_take_lowest_ids(dev):
     """q = 0: every draft score is exactly 0, so the selection is the k lowest
     logical ids on both sides (ties broken by index), and the output is the
