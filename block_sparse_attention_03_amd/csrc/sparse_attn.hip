@@ -60,47 +60,45 @@ struct Tile {
 // Direct global -> LDS loads of one 64-key half of a key block. Each wave
 // instruction fills 1 KB of LDS, lane l landing at +16l; the lane fetches
 // whichever global chunk belongs there under the swizzle. The per-lane byte
-// offsets (relative to the half's first K row and first V^T column) do not
-// depend on the block, so they are computed once (subtile_offsets) and the
-// per-block part of each address is scalar.
+// offset (relative to the half's first K row, resp. first V^T column) does
+// not depend on the block, so it is computed once, and the per-block part of
+// each address is scalar. Instruction it covers K rows 16 it (at D = 128;
+// 32 it at D = 64) and V^T rows 32 it on from what instruction 0 covers:
+// 4 KB, resp. 8 KB, further, under the same swizzle (the swizzles depend on
+// the row modulo 16), so one lane offset per tile serves every instruction.
 template <int D>
-__device__ __forceinline__ void subtile_offsets(int w, int lane, uint32_t* koff, uint32_t* voff) {
+__device__ __forceinline__ void subtile_offsets(int w, int lane, uint32_t& koff, uint32_t& voff) {
   using T = Tile<D>;
-#pragma unroll
-  for (int it = 0; it < T::KLD; ++it) {
-    const int unit = (it * 4 + w) * 64 + lane;
-    const int row = unit / T::KCH, c = swz_row<D>(row, unit % T::KCH);
-    koff[it] = (uint32_t)((row * D + c * 8) * 2);
-  }
-#pragma unroll
-  for (int it = 0; it < T::VLD; ++it) {
-    const int unit = (it * 4 + w) * 64 + lane;
-    const int d = unit >> 3, c = swz8(d, unit & 7);
-    voff[it] = (uint32_t)((d * 128 + c * 8) * 2);
-  }
+  const int ku = w * 64 + lane;  // unit of instruction 0
+  const int row = ku / T::KCH;
+  koff = (uint32_t)((row * D + swz_row<D>(row, ku % T::KCH) * 8) * 2);
+  const int d = ku >> 3;
+  voff = (uint32_t)((d * 128 + swz8(d, ku & 7) * 8) * 2);
 }
 
 // Issue the loads of half hf (keys 64hf..64hf+63) into one LDS buffer; w is
 // the (uniform) wave index. Buffer loads: the resource holds the block base
-// and its size, the half offset is the scalar offset (half offset + lane
-// offset stay inside the block), so a load needs no vector address
-// arithmetic at all.
+// and its size, the half and instruction offsets are the scalar offset
+// (with the lane offset they stay inside the block), so a load needs no
+// vector address arithmetic at all.
 template <int D>
 __device__ __forceinline__ void load_subtile(const char* kblk, const char* vblk, int hf, char* buf,
-                                             int w, const uint32_t* koff, const uint32_t* voff) {
+                                             int w, uint32_t koff, uint32_t voff) {
   using T = Tile<D>;
+  static_assert(T::KBYTES / T::KLD == 4096 && T::VBYTES / T::VLD == 4096,
+                "four waves fill 4 KB of LDS per instruction");
   constexpr int kBlockBytes = 128 * D * 2;
   const __amdgpu_buffer_rsrc_t kr = raw_rsrc(kblk, kBlockBytes);
   const __amdgpu_buffer_rsrc_t vr = raw_rsrc(vblk, kBlockBytes);
 #pragma unroll
   for (int it = 0; it < T::KLD; ++it)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, LDS_PTR(buf + (it * 4 + w) * 1024), 16, koff[it],
-                                             64 * hf * D * 2, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, LDS_PTR(buf + (it * 4 + w) * 1024), 16, koff,
+                                             64 * hf * D * 2 + 4096 * it, 0, 0);
   char* vb = buf + T::KBYTES;
 #pragma unroll
   for (int it = 0; it < T::VLD; ++it)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, LDS_PTR(vb + (it * 4 + w) * 1024), 16, voff[it],
-                                             64 * hf * 2, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, LDS_PTR(vb + (it * 4 + w) * 1024), 16, voff,
+                                             64 * hf * 2 + 8192 * it, 0, 0);
 }
 
 __device__ inline float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
@@ -274,7 +272,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
 
   const int dq = __builtin_amdgcn_readfirstlane(w) >> 1;   // this wave's query frame
   const char *kp, *vp;
-  uint32_t gkoff[T::KLD], gvoff[T::VLD];
+  uint32_t gkoff, gvoff;
   subtile_offsets<D>(w, lane, gkoff, gvoff);
   // Which halves of key block j this wave computes: none for a skipped id;
   // under the segment mask, the halves whose frame shares this wave's segment
