@@ -94,15 +94,17 @@ def test_small_streaming_with_cache(dev):
     say(f"small stream: {stats}")
 
 
-def test_two_stream_partition_matches_one_stream(dev):
+@pytest.mark.parametrize("kw", [dict(), dict(head_dim=64), dict(dtype="f32")],
+                         ids=["bf16-d128", "bf16-d64", "f32-d128"])
+def test_two_stream_partition_matches_one_stream(dev, kw):
     """The transposed-v part of the partition on a second stream (forked after
     the previous step, joined before the attention) gives bitwise the same
     lists, outputs, q blocks and ring contents as the one-stream step, step
     after step while ring slots are reused, and matches the oracle."""
-    w = small(frames=2, cache_frames=6, cap_tb=3, local_range=5, ratio=(1, 4))
+    w = small(frames=2, cache_frames=6, cap_tb=3, local_range=5, ratio=(1, 4), **kw)
     one = Stream(w, dev)
     two = Stream(w, dev, side_stream=torch.cuda.Stream())
-    for n in range(5):
+    for n in range(4):
         g1, _ = one.step(want_probs=False)
         g2, ref = two.step(want_probs=False)
         for key in ("sel_idx", "sel_cnt", "lse"):
