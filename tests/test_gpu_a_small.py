@@ -122,6 +122,21 @@ def test_two_stream_partition_matches_one_stream(dev, kw):
     say(f"two-stream partition: {stats}")
 
 
+@pytest.mark.parametrize("q_scale", [16.0, 64.0])
+def test_large_logits(dev, q_scale):
+    """q scaled by a power of two (exact in bf16): logits of tens to hundreds,
+    so the running row max jumps by far more than the lazy-rescale threshold,
+    most probabilities underflow to zero and the softmax is sharply peaked;
+    outputs and lse still match the oracle."""
+    w = small(frames=2, cache_frames=6, cap_tb=3, local_range=5, ratio=(1, 4))
+    st = Stream(w, dev, q_scale=q_scale)
+    for n in range(2):
+        g, ref = st.step(want_probs=False)
+        assert np.isfinite(g["lse"]).all()
+        stats = compare_step(w, g, ref)
+    say(f"large logits x{q_scale}: {stats}")
+
+
 def test_equal_scores_take_lowest_ids(dev):
     """q = 0: every draft score is exactly 0, so the selection is the k lowest
     logical ids on both sides (ties broken by index), and the output is the
