@@ -168,11 +168,13 @@ def compare_step(w, g, ref, rows="all", check_probs=True):
         # lse bound: rounding each probability (bf16 on the matrix-core path)
         # moves ln(sum) by at most that unit roundoff; a float32 logit of D
         # exact products is within gamma_D * |q| |k| * scale of the exact one
-        # (u = 2^-23: the bound for truncating as well as round-to-nearest
-        # accumulation) and lse is 1-Lipschitz in the logits; float32
-        # rounding of the result adds a few ulps of |lse|.
+        # (u = 2^-23 on the matrix cores: the bound for truncating as well as
+        # round-to-nearest accumulation; 2^-24 for the fp32 path's IEEE fma)
+        # and lse is 1-Lipschitz in the logits; float32 rounding of the
+        # result adds a few ulps of |lse|.
         D = w.head_dim
-        gamma = D * 2.0 ** -23 / (1 - D * 2.0 ** -23)
+        u = 2.0 ** -23 if w.dtype == "bf16" else 2.0 ** -24
+        gamma = D * u / (1 - D * u)
         qn = np.sqrt((ref.q_blocks ** 2).sum(-1)).max()
         kn = np.sqrt((kb ** 2).sum(-1)).max()
         tol = ((2.0 ** -9 if w.dtype == "bf16" else 1e-5) + gamma * qn * kn / math.sqrt(D)
