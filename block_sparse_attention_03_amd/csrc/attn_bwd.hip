@@ -357,14 +357,31 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       f32x16 st, dp;
 #pragma unroll
       for (int e = 0; e < 16; ++e) st[e] = dp[e] = 0.f;
+      // every A fragment of the S^T and dP^T products is read before the
+      // first product, so the wave waits for LDS once, not per product
+      bf16x8 ka[NS], va[NS];
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const int off = prow * (D * 2) + swz_row<D>(prow, 2 * s + g) * 16;
-        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(kr + off),
-                                                     qf[s], st, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(vr + off),
-                                                     of[s], dp, 0, 0, 0);
+        ka[s] = *reinterpret_cast<const bf16x8*>(kr + off);
+        va[s] = *reinterpret_cast<const bf16x8*>(vr + off);
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s], qf[s], st, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[s], of[s], dp, 0, 0, 0);
+      }
+      // the K^T fragments of the dQ^T products, read while the products run
+      bf16x8 kta[2][NO];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int dt = 0; dt < NO; ++dt) {
+          const int d = 32 * dt + l32;
+          kta[ks][dt] = *reinterpret_cast<const bf16x8*>(kt + d * 64 + swz4(d, 2 * ks + g) * 16);
+        }
+      __builtin_amdgcn_sched_barrier(0);
       bf16x8 ds[2];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -374,11 +391,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int dt = 0; dt < NO; ++dt) {
-          const int d = 32 * dt + l32;
-          const bf16x8 af = *reinterpret_cast<const bf16x8*>(kt + d * 64 + swz4(d, 2 * ks + g) * 16);
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, ds[ks], acc[dt], 0, 0, 0);
-        }
+        for (int dt = 0; dt < NO; ++dt)
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kta[ks][dt], ds[ks], acc[dt], 0, 0, 0);
     };
     char* buf0 = lds;
     char* buf1 = lds + BUF;
@@ -478,14 +492,34 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
       f32x16 st, dp;
 #pragma unroll
       for (int e = 0; e < 16; ++e) st[e] = dp[e] = 0.f;
+      // every A fragment of the S and dP products is read before the first
+      // product (one LDS wait per quarter, not one per product)
+      bf16x8 qa[NS], oa[NS];
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const int off = prow * (D * 2) + swz_row<D>(prow, 2 * s + g) * 16;
-        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(qr + off),
-                                                     kf[s], st, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(orr + off),
-                                                     vf[s], dp, 0, 0, 0);
+        qa[s] = *reinterpret_cast<const bf16x8*>(qr + off);
+        oa[s] = *reinterpret_cast<const bf16x8*>(orr + off);
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], kf[s], st, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[s], vf[s], dp, 0, 0, 0);
+      }
+      // the dO^T and Q^T fragments of the dV^T and dK^T products, read while
+      // the products above run
+      bf16x8 ota[2][NO], qta[2][NO];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int dt = 0; dt < NO; ++dt) {
+          const int d = 32 * dt + l32;
+          const int off = d * 64 + swz4(d, 2 * ks + g) * 16;
+          ota[ks][dt] = *reinterpret_cast<const bf16x8*>(ot + off);
+          qta[ks][dt] = *reinterpret_cast<const bf16x8*>(qt + off);
+        }
+      __builtin_amdgcn_sched_barrier(0);
       // element 8ks + e is query 16ks + 8g + e of the quarter
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
@@ -499,12 +533,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
         }
 #pragma unroll
         for (int dt = 0; dt < NO; ++dt) {
-          const int d = 32 * dt + l32;
-          const int off = d * 64 + swz4(d, 2 * ks + g) * 16;
-          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(ot + off),
-                                                           pb, dv[dt], 0, 0, 0);
-          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(qt + off),
-                                                           dsb, dk[dt], 0, 0, 0);
+          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ota[ks][dt], pb, dv[dt], 0, 0, 0);
+          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qta[ks][dt], dsb, dk[dt], 0, 0, 0);
         }
       }
     };
