@@ -537,6 +537,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
           dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qta[ks][dt], dsb, dk[dt], 0, 0, 0);
         }
       }
+      // issue order: the lse / delta reads and the first k-step's softmax,
+      // then the first k-step's products each followed by a share of the
+      // second k-step's softmax, then the second k-step's products
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 36, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * NO; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * NO, 0);
     };
     // quarter qq of query block n sits in buffer qq & 1; the next is in flight
     char* buf0 = lds;
