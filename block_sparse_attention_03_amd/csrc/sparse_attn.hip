@@ -133,8 +133,13 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   if (task >= n_tasks) return;
   // longest lists first: query TBs in descending order (a later TB sees more
   // key blocks), so the short lists of the first TBs fill the tail
+  // Inside a TB the blocks go column by column: the workgroups an XCD holds
+  // at once then cover a few whole columns, so a block's left, right, upper
+  // and lower neighbours (whose lists share about half their keys) run
+  // together, where a row-major order kept only two or three rows in flight.
   const int r = task % nq, n_tb = a.T / 2;
-  const int i = (n_tb - 1 - r / nS) * nS + r % nS;
+  const int nby = a.H / 8, rs = r % nS;
+  const int i = (n_tb - 1 - r / nS) * nS + (rs % nby) * (a.W / 8) + rs / nby;
   const int bh = task / nq;
   const int h = bh % a.NH, b = bh / a.NH;
   const size_t row = (size_t)bh * nq + i;  // flat query-block row of the lists and q_blk
