@@ -45,6 +45,10 @@ def parse():
                     help="run the transposed-v part of the partition on a second stream, under "
                          "the q/k part and the lists (measured slower: the cross-stream "
                          "fork and join cost more than the overlap saves)")
+    ap.add_argument("--q-blocks", action="store_true",
+                    help="have the partition write the query blocks (q_blk) and the attention "
+                         "read q from them, instead of reading q in token layout (measured "
+                         "slower: q_blk is an extra write and read of the whole of q)")
     ap.add_argument("--cpu-sample-heads", type=int, default=12)
     ap.add_argument("--cpu-sample-steps", type=int, default=4)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -151,7 +155,8 @@ def main():
                 self.kmax = L.lcsa_max_candidates(geom, tb_first, probe, self.params)
             else:
                 self.kmax = L.lcsa_max_topk(geom, tb_first, probe, self.params)
-            self.bufs = L.StepBuffers(geom, self.kmax, device=dev, with_lse=sp.backward)
+            self.bufs = L.StepBuffers(geom, self.kmax, device=dev, with_lse=sp.backward,
+                                      with_q_blk=args.q_blocks)
             self.fork_join = (torch.cuda.Event(), torch.cuda.Event())
             self.keep = sp.cap_tb if sp.cache_frames else 0  # cold chunks: empty after each step
             if sp.backward:  # training shape: the keys are the chunk's own blocks
@@ -186,12 +191,18 @@ def main():
                 stream.wait_event(join)
             if ev is not None:
                 ev[0].record(stream)
-            if self.seg:
+            if self.seg and b.q_blk is not None:
                 L.lcsa_segment_attn(geom, b.q_blk, tb, c.c, self.seg, b.sel_idx, b.sel_cnt,
                                     self.kmax, b.out, None, 0.0, stream)
-            else:
+            elif self.seg:
+                L.lcsa_segment_attn_tok(geom, q, tb, c.c, self.seg, b.sel_idx, b.sel_cnt,
+                                        self.kmax, b.out, None, 0.0, stream)
+            elif b.q_blk is not None:
                 L.lcsa_block_sparse_attn(geom, b.q_blk, c.c, b.sel_idx, b.sel_cnt, self.kmax,
                                          b.out, b.lse, 0.0, stream)
+            else:
+                L.lcsa_block_sparse_attn_tok(geom, q, c.c, b.sel_idx, b.sel_cnt, self.kmax,
+                                             b.out, b.lse, 0.0, stream)
             if ev is not None:
                 ev[1].record(stream)
             if self.sp.backward:
@@ -258,14 +269,7 @@ def main():
     value = flops_step / (ms_step * 1e-3) / 1e12
     achieved = flops_step / (attn_avg * 1e-3) / 1e12
 
-    traffic = None
-    try:
-        with open(args.traffic_json) as f:
-            tj = json.load(f)
-        entry = tj.get(args.workload) or {}
-        traffic = entry.get("bytes_per_launch")
-    except (OSError, ValueError):
-        pass
+    traffic = traffic_for(args.traffic_json, args.workload)
 
     result = {
         "metric": "block-sparse attn effective TFLOP/s + ms per streaming step at 768x1408",
@@ -285,7 +289,8 @@ def main():
                    "local_range": w.local_range, "selected_pairs_per_step": pairs,
                    **({"frame_segments": seg} if seg else {}),
                    **({"layers": list(w.layers)} if w.layers else {}),
-                   "kmax": kmax, "parallelism": "single GPU"},
+                   "kmax": kmax, "q_read_from": "q_blk" if args.q_blocks else "token layout",
+                   "streams": 2 if args.overlap_v else 1, "parallelism": "single GPU"},
         "attn_ms": round(attn_avg, 4),
         **({"bwd_ms": round(float(np.mean(bwd_ms)), 4)} if has_bwd else {}),
         "attn_ms_median": round(float(np.median(attn_ms)), 4),
@@ -351,6 +356,34 @@ def cpu_baseline(w, sample_heads, sample_steps, flops_pair):
 
 
 ATTN_KERNEL = "attn_bf16"
+# The files whose text makes up the attention kernel. traffic.json keeps a
+# digest of them from when its counters were summarized; a run on other
+# sources reports traffic as null instead of figures taken on older code.
+ATTN_SOURCES = ("block_sparse_attention_03_amd/csrc/sparse_attn.hip",
+                "block_sparse_attention_03_amd/csrc/mfma_tiles.h",
+                "block_sparse_attention_03_amd/csrc/lcsa_kernels.h")
+
+
+def attn_source_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in ATTN_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(path: str, workload: str):
+    """Counter-derived HBM bytes per attention launch of `workload`, or None
+    when none were taken or they were taken on other kernel sources."""
+    try:
+        with open(path) as f:
+            entry = json.load(f).get(workload) or {}
+    except (OSError, ValueError):
+        return None
+    if entry.get("source_digest") != attn_source_digest():
+        return None
+    return entry.get("bytes_per_launch")
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
@@ -415,7 +448,7 @@ def _write_traffic(args, fetch_b, write_b, fa, wa, fc, wc, f_factor, w_factor, n
              "calibration": {"copy_bytes": probe_bytes, "fetch_kib": round(fc, 1),
                              "write_kib": round(wc, 1), "fetch_factor": round(f_factor, 4),
                              "write_factor": round(w_factor, 4)},
-             "dispatches": [nf, nw]}
+             "dispatches": [nf, nw], "source_digest": attn_source_digest()}
     try:
         with open(args.traffic_json) as f:
             tj = json.load(f)

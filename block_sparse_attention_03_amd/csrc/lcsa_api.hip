@@ -73,13 +73,15 @@ lcsa_status check_cold_view(const lcsa_geom* gq, int64_t q_first_abs_tb,
   return ok();
 }
 
-// Validation and argument setup shared by the two attention entry points.
-lcsa_status attn_args(const lcsa_geom* gq, const void* q_blk, const lcsa_kv_cache* cache,
-                      const int32_t* sel_idx, const int32_t* sel_cnt, int32_t kmax, float scale,
-                      void* out, float* lse, const char* fn, AttnArgs* a) {
+// Validation and argument setup shared by the attention entry points; q is
+// q_blk (block layout) or, with tokens set, q in token layout.
+lcsa_status attn_args(const lcsa_geom* gq, const void* q, bool tokens,
+                      const lcsa_kv_cache* cache, const int32_t* sel_idx,
+                      const int32_t* sel_cnt, int32_t kmax, float scale, void* out, float* lse,
+                      const char* fn, AttnArgs* a) {
   lcsa_status st;
   if ((st = check_geom(gq, fn)) || (st = check_cache(cache)) ||
-      (st = check_matches_cache(gq, cache)) || (st = check_ptr(q_blk, "q_blk")) ||
+      (st = check_matches_cache(gq, cache)) || (st = check_ptr(q, tokens ? "q" : "q_blk")) ||
       (st = check_ptr(sel_idx, "sel_idx")) || (st = check_ptr(sel_cnt, "sel_cnt")) ||
       (st = check_ptr(out, "out")) || (st = check_ptr(lse, "lse", true)))
     return st;
@@ -89,7 +91,7 @@ lcsa_status attn_args(const lcsa_geom* gq, const void* q_blk, const lcsa_kv_cach
   if (gq->frames > 0 && cache->count == 0)
     return fail(LCSA_ERR_CAPACITY, "the cache holds no key blocks");
   *a = AttnArgs{};
-  a->q_blk = q_blk;
+  (tokens ? a->q_tok : a->q_blk) = q;
   a->k_ring = cache->k_ring;
   a->v_ring = cache->v_ring;
   a->sel_idx = sel_idx;
@@ -149,10 +151,10 @@ static lcsa_status partition_parts(const lcsa_geom* g, const void* q, const void
                 parts);
   const bool do_qk = parts & LCSA_PART_QK, do_v = parts & LCSA_PART_V;
   const bool has_q = do_qk && (q || q_blk || q_pool);
-  if (has_q && !(q && q_blk && q_pool))
-    return fail(LCSA_ERR_NULL, "q, q_blk and q_pool must be all NULL or all non-NULL");
+  if (has_q && !(q && q_pool))
+    return fail(LCSA_ERR_NULL, "q and q_pool must be both NULL or both non-NULL (q_blk needs q)");
   if ((do_qk && (st = check_ptr(k, "k"))) || (do_v && (st = check_ptr(v, "v"))) ||
-      (has_q && ((st = check_ptr(q, "q")) || (st = check_ptr(q_blk, "q_blk")) ||
+      (has_q && ((st = check_ptr(q, "q")) || (st = check_ptr(q_blk, "q_blk", true)) ||
                  (st = check_ptr(q_pool, "q_pool")))))
     return st;
   const int32_t ntb = g->frames / 2;
@@ -171,7 +173,7 @@ static lcsa_status partition_parts(const lcsa_geom* g, const void* q, const void
   a.k = do_qk ? k : nullptr;
   a.v = do_v ? v : nullptr;
   a.parts = parts;
-  a.q_blk = q_blk;
+  a.q_blk = has_q ? q_blk : nullptr;
   a.q_pool = q_pool;
   a.k_ring = cache->k_ring;
   a.v_ring = cache->v_ring;
@@ -280,16 +282,30 @@ lcsa_status lcsa_draft_mask(const lcsa_geom* gq, const double* q_pool, int64_t q
   return device_status(launch_draft_mask(a, (hipStream_t)stream), "lcsa_draft_mask");
 }
 
+static lcsa_status sparse_attn(const lcsa_geom* gq, const void* q, bool tokens,
+                               const lcsa_kv_cache* cache, const int32_t* sel_idx,
+                               const int32_t* sel_cnt, int32_t kmax, float scale, void* out,
+                               float* lse, void* stream, const char* fn) {
+  AttnArgs a;
+  lcsa_status st = attn_args(gq, q, tokens, cache, sel_idx, sel_cnt, kmax, scale, out, lse, fn, &a);
+  if (st || gq->frames == 0) return st;
+  return device_status(launch_block_sparse_attn(a, gq->dtype, false, (hipStream_t)stream), fn);
+}
+
 lcsa_status lcsa_block_sparse_attn(const lcsa_geom* gq, const void* q_blk,
                                    const lcsa_kv_cache* cache, const int32_t* sel_idx,
                                    const int32_t* sel_cnt, int32_t kmax, float scale, void* out,
                                    float* lse, void* stream) {
-  AttnArgs a;
-  lcsa_status st = attn_args(gq, q_blk, cache, sel_idx, sel_cnt, kmax, scale, out, lse,
-                             "lcsa_block_sparse_attn", &a);
-  if (st || gq->frames == 0) return st;
-  return device_status(launch_block_sparse_attn(a, gq->dtype, false, (hipStream_t)stream),
-                       "lcsa_block_sparse_attn");
+  return sparse_attn(gq, q_blk, false, cache, sel_idx, sel_cnt, kmax, scale, out, lse, stream,
+                     "lcsa_block_sparse_attn");
+}
+
+lcsa_status lcsa_block_sparse_attn_tok(const lcsa_geom* gq, const void* q,
+                                       const lcsa_kv_cache* cache, const int32_t* sel_idx,
+                                       const int32_t* sel_cnt, int32_t kmax, float scale,
+                                       void* out, float* lse, void* stream) {
+  return sparse_attn(gq, q, true, cache, sel_idx, sel_cnt, kmax, scale, out, lse, stream,
+                     "lcsa_block_sparse_attn_tok");
 }
 
 lcsa_status lcsa_local_lists(const lcsa_geom* gq, int64_t q_first_abs_tb,
@@ -437,13 +453,13 @@ lcsa_status lcsa_segment_lists(const lcsa_geom* gq, int64_t q_first_abs_tb,
   return device_status(launch_segment_lists(a, (hipStream_t)stream), fn);
 }
 
-lcsa_status lcsa_segment_attn(const lcsa_geom* gq, const void* q_blk, int64_t q_first_abs_tb,
-                              const lcsa_kv_cache* cache, const int32_t* frame_seg,
-                              const int32_t* sel_idx, const int32_t* sel_cnt, int32_t kmax,
-                              float scale, void* out, float* lse, void* stream) {
-  const char* fn = "lcsa_segment_attn";
+static lcsa_status segment_attn(const lcsa_geom* gq, const void* q, bool tokens,
+                                int64_t q_first_abs_tb, const lcsa_kv_cache* cache,
+                                const int32_t* frame_seg, const int32_t* sel_idx,
+                                const int32_t* sel_cnt, int32_t kmax, float scale, void* out,
+                                float* lse, void* stream, const char* fn) {
   AttnArgs a;
-  lcsa_status st = attn_args(gq, q_blk, cache, sel_idx, sel_cnt, kmax, scale, out, lse, fn, &a);
+  lcsa_status st = attn_args(gq, q, tokens, cache, sel_idx, sel_cnt, kmax, scale, out, lse, fn, &a);
   if (st || gq->frames == 0) return st;
   int32_t n_tb[LCSA_MAX_SLOTS];
   int8_t tb[LCSA_MAX_SLOTS][LCSA_MAX_SLOTS];
@@ -452,6 +468,22 @@ lcsa_status lcsa_segment_attn(const lcsa_geom* gq, const void* q_blk, int64_t q_
       (st = check_cold_view(gq, q_first_abs_tb, cache, fn)))
     return st;
   return device_status(launch_block_sparse_attn(a, gq->dtype, true, (hipStream_t)stream), fn);
+}
+
+lcsa_status lcsa_segment_attn(const lcsa_geom* gq, const void* q_blk, int64_t q_first_abs_tb,
+                              const lcsa_kv_cache* cache, const int32_t* frame_seg,
+                              const int32_t* sel_idx, const int32_t* sel_cnt, int32_t kmax,
+                              float scale, void* out, float* lse, void* stream) {
+  return segment_attn(gq, q_blk, false, q_first_abs_tb, cache, frame_seg, sel_idx, sel_cnt, kmax,
+                      scale, out, lse, stream, "lcsa_segment_attn");
+}
+
+lcsa_status lcsa_segment_attn_tok(const lcsa_geom* gq, const void* q, int64_t q_first_abs_tb,
+                                  const lcsa_kv_cache* cache, const int32_t* frame_seg,
+                                  const int32_t* sel_idx, const int32_t* sel_cnt, int32_t kmax,
+                                  float scale, void* out, float* lse, void* stream) {
+  return segment_attn(gq, q, true, q_first_abs_tb, cache, frame_seg, sel_idx, sel_cnt, kmax,
+                      scale, out, lse, stream, "lcsa_segment_attn_tok");
 }
 
 }  // extern "C"

@@ -270,6 +270,6 @@ lcsa_status lcsa_max_candidates(const lcsa_geom* gq, int64_t q_first_abs_tb,
   return ok();
 }
 
-int32_t lcsa_abi_version(void) { return 3; }
+int32_t lcsa_abi_version(void) { return 4; }
 
 }  // extern "C"

@@ -49,7 +49,8 @@ struct DraftArgs {
 };
 
 struct AttnArgs {
-  const void* q_blk;        // [B][NH][nq][128][D]
+  const void* q_blk;        // [B][NH][nq][128][D], read when q_tok is null
+  const void* q_tok;        // q in token layout [B][T][H][W][NH][D], or null
   const void* k_ring;       // [B][NH][n_slots][nS][128][D]
   const void* v_ring;       // [B][NH][n_slots][nS][D][128]
   const int32_t* sel_idx;   // [B][NH][nq][kmax]

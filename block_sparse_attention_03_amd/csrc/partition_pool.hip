@@ -82,8 +82,9 @@ __device__ inline void load_block(const PartitionArgs& a, const char* src, int b
   }
 }
 
-// Store the chunks as a contiguous [128][D] tile; acc gets the thread's
-// float64 column sums of its EPC channels over its ITERS tokens.
+// Store the chunks as a contiguous [128][D] tile (no store when dst is
+// null: uniform per workgroup); acc gets the thread's float64 column sums
+// of its EPC channels over its ITERS tokens.
 template <int ESZ, int D>
 __device__ inline void store_tile_sum(char* dst, const u32x4 (&v)[Geo<ESZ, D>::ITERS],
                                       double (&acc)[Geo<ESZ, D>::EPC]) {
@@ -94,7 +95,7 @@ __device__ inline void store_tile_sum(char* dst, const u32x4 (&v)[Geo<ESZ, D>::I
 #pragma unroll
   for (int it = 0; it < G::ITERS; ++it) {
     const int tau = it * G::TPI + tsub;
-    *reinterpret_cast<u32x4*>(dst + ((size_t)tau * D + c * G::EPC) * ESZ) = v[it];
+    if (dst) *reinterpret_cast<u32x4*>(dst + ((size_t)tau * D + c * G::EPC) * ESZ) = v[it];
     double w[G::EPC];
     widen_chunk<ESZ>(v[it], w);
 #pragma unroll
@@ -180,10 +181,12 @@ __global__ __launch_bounds__(kThreads) void partition_pool_kernel(PartitionArgs 
     return;
   }
 
-  // q or k: the row-major tile, then the block mean of each channel
+  // q or k: the row-major tile (none for q without q_blk), then the block
+  // mean of each channel
   const size_t qb = ((size_t)b * a.NH + h) * nblk + n;
   char* dst = role == 0 ? (char*)a.k_ring + ring_blk * tile * ESZ
-                        : (char*)a.q_blk + qb * tile * ESZ;
+            : a.q_blk   ? (char*)a.q_blk + qb * tile * ESZ
+                        : nullptr;
   double acc[G::EPC];
   store_tile_sum<ESZ, D>(dst, v, acc);
   // the lanes of a wave holding the same column chunk (lane % CPT) add up,

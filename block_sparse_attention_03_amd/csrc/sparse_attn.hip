@@ -160,11 +160,13 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     return;
   }
 
-  const uint16_t* qb = (const uint16_t*)a.q_blk + row * 128 * D;
+  // this lane's query row: D contiguous values in either layout
+  const uint16_t* qb = a.q_tok ? (const uint16_t*)a.q_tok + out_offset(a, b, h, i, tau, 0)
+                               : (const uint16_t*)a.q_blk + (row * 128 + tau) * D;
   bf16x8 qf[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s)
-    qf[s] = *reinterpret_cast<const bf16x8*>(qb + tau * D + 16 * s + 8 * g);
+    qf[s] = *reinterpret_cast<const bf16x8*>(qb + 16 * s + 8 * g);
 
   const size_t bh_slots = (size_t)bh * a.n_slots;
   // View position of a uniform key block id j in [0, n_keys): j / nS by a
@@ -378,7 +380,8 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(AttnArgs a) {
     return;
   }
   float q[D], o[D];
-  const float* qb = (const float*)a.q_blk + ((size_t)task * 128 + tau) * D;
+  const float* qb = a.q_tok ? (const float*)a.q_tok + out_offset(a, b, h, i, tau, 0)
+                            : (const float*)a.q_blk + ((size_t)task * 128 + tau) * D;
 #pragma unroll
   for (int d = 0; d < D; ++d) {
     q[d] = qb[d];

@@ -87,6 +87,8 @@ def load_library(path: str = LIB_PATH):
                             c_void_p],
         "lcsa_block_sparse_attn": [G, c_void_p, C, c_void_p, c_void_p, c_int32, c_float,
                                    c_void_p, c_void_p, c_void_p],
+        "lcsa_block_sparse_attn_tok": [G, c_void_p, C, c_void_p, c_void_p, c_int32, c_float,
+                                       c_void_p, c_void_p, c_void_p],
         "lcsa_attn_bwd_workspace_size": [G, POINTER(ctypes.c_size_t)],
         "lcsa_block_sparse_attn_bwd": [G, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                        c_void_p, c_void_p, c_void_p, c_int32, c_float, c_void_p,
@@ -98,6 +100,8 @@ def load_library(path: str = LIB_PATH):
                                c_void_p],
         "lcsa_segment_attn": [G, c_void_p, c_int64, C, POINTER(c_int32), c_void_p, c_void_p,
                               c_int32, c_float, c_void_p, c_void_p, c_void_p],
+        "lcsa_segment_attn_tok": [G, c_void_p, c_int64, C, POINTER(c_int32), c_void_p,
+                                  c_void_p, c_int32, c_float, c_void_p, c_void_p, c_void_p],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -249,6 +253,14 @@ def lcsa_block_sparse_attn(geom: Geom, q_blk, cache: KvCacheStruct, sel_idx, sel
                                       _ptr(out), _ptr(lse), _stream(stream)))
 
 
+def lcsa_block_sparse_attn_tok(geom: Geom, q, cache: KvCacheStruct, sel_idx, sel_cnt, kmax: int,
+                               out, lse=None, scale: float = 0.0, stream=None):
+    lib = load_library()
+    _check(lib.lcsa_block_sparse_attn_tok(ctypes.byref(geom), _ptr(q), ctypes.byref(cache),
+                                          _ptr(sel_idx), _ptr(sel_cnt), kmax, c_float(scale),
+                                          _ptr(out), _ptr(lse), _stream(stream)))
+
+
 def lcsa_max_candidates(geom: Geom, q_first_abs_tb: int, cache: KvCacheStruct,
                         params: SelectParams) -> int:
     lib = load_library()
@@ -313,6 +325,16 @@ def lcsa_segment_attn(geom: Geom, q_blk, q_first_abs_tb: int, cache: KvCacheStru
                                  _stream(stream)))
 
 
+def lcsa_segment_attn_tok(geom: Geom, q, q_first_abs_tb: int, cache: KvCacheStruct, frame_seg,
+                          sel_idx, sel_cnt, kmax: int, out, lse=None, scale: float = 0.0,
+                          stream=None):
+    lib = load_library()
+    _check(lib.lcsa_segment_attn_tok(ctypes.byref(geom), _ptr(q), q_first_abs_tb,
+                                     ctypes.byref(cache), _frame_seg(frame_seg), _ptr(sel_idx),
+                                     _ptr(sel_cnt), kmax, c_float(scale), _ptr(out), _ptr(lse),
+                                     _stream(stream)))
+
+
 def lcsa_last_error() -> str:
     return load_library().lcsa_last_error().decode()
 
@@ -355,14 +377,16 @@ class StepBuffers:
     """Per-chunk outputs of the pipeline for a query geometry."""
 
     def __init__(self, geom: Geom, kmax: int, device="cuda", with_probs_keys: int = 0,
-                 with_lse: bool = False):
+                 with_lse: bool = False, with_q_blk: bool = False):
         import torch
         nS = (geom.height // 8) * (geom.width // 8)
         nq = (geom.frames // 2) * nS
         dt = torch.bfloat16 if geom.dtype == LCSA_BF16 else torch.float32
         B, NH, D = geom.batch, geom.heads, geom.head_dim
         self.kmax = kmax
-        self.q_blk = torch.empty((B, NH, nq, 128, D), dtype=dt, device=device)
+        # the query blocks are only materialised for the block-layout path
+        self.q_blk = (torch.empty((B, NH, nq, 128, D), dtype=dt, device=device)
+                      if with_q_blk else None)
         self.q_pool = torch.empty((B, NH, nq, D), dtype=torch.float64, device=device)
         self.sel_idx = torch.empty((B, NH, nq, max(kmax, 1)), dtype=torch.int32, device=device)
         self.sel_cnt = torch.empty((B, NH, nq), dtype=torch.int32, device=device)
@@ -377,12 +401,15 @@ class StepBuffers:
 def run_step(geom: Geom, q, k, v, cache: KVCache, first_abs_tb: int, params: SelectParams,
              bufs: StepBuffers | None = None, keep_tb: int | None = None, stream=None,
              want_probs=False, want_lse=False, scale: float = 0.0, local: bool = False,
-             side_stream=None):
+             side_stream=None, q_blocks: bool = False):
     """One LCSA invocation through the C-ABI: append, partition+pool, draft
     (or, with local=True, the FlashVSR+ local lists: every allowed key
-    block), attention, evict. With a side_stream, the transposed-v part of
-    the partition runs there, under the q/k part and the draft, and the
-    attention waits for it. Returns the StepBuffers holding the results."""
+    block), attention, evict. The attention reads q in token layout, so the
+    partition writes only q's block means; q_blocks=True instead writes the
+    query blocks to bufs.q_blk and reads them from there. With a side_stream,
+    the transposed-v part of the partition runs there, under the q/k part and
+    the draft, and the attention waits for it. Returns the StepBuffers
+    holding the results."""
     n_tb = geom.frames // 2
     first_slot = cache.append(n_tb, first_abs_tb)
     if local:
@@ -393,14 +420,17 @@ def run_step(geom: Geom, q, k, v, cache: KVCache, first_abs_tb: int, params: Sel
         n_keys = cache.c.count * cache.nby * cache.nbx
         bufs = StepBuffers(geom, kmax, device=q.device,
                            with_probs_keys=n_keys if want_probs and not local else 0,
-                           with_lse=want_lse)
+                           with_lse=want_lse, with_q_blk=q_blocks)
+    if q_blocks and bufs.q_blk is None:
+        raise ValueError("q_blocks=True needs StepBuffers(with_q_blk=True)")
+    q_blk = bufs.q_blk if q_blocks else None
     join = None
     if side_stream is not None:
         join = fork_v_part(geom, v, cache.c, first_slot, stream, side_stream)
-        lcsa_partition_pool_parts(geom, q, k, None, bufs.q_blk, bufs.q_pool, cache.c, first_slot,
+        lcsa_partition_pool_parts(geom, q, k, None, q_blk, bufs.q_pool, cache.c, first_slot,
                                   PART_QK, stream)
     else:
-        lcsa_partition_pool(geom, q, k, v, bufs.q_blk, bufs.q_pool, cache.c, first_slot, stream)
+        lcsa_partition_pool(geom, q, k, v, q_blk, bufs.q_pool, cache.c, first_slot, stream)
     if local:
         lcsa_local_lists(geom, first_abs_tb, cache.c, params, bufs.kmax, bufs.sel_idx,
                          bufs.sel_cnt, stream)
@@ -410,8 +440,12 @@ def run_step(geom: Geom, q, k, v, cache: KVCache, first_abs_tb: int, params: Sel
     if join is not None:
         import torch
         (stream if stream is not None else torch.cuda.current_stream()).wait_event(join)
-    lcsa_block_sparse_attn(geom, bufs.q_blk, cache.c, bufs.sel_idx, bufs.sel_cnt, bufs.kmax,
-                           bufs.out, bufs.lse, scale, stream)
+    if q_blocks:
+        lcsa_block_sparse_attn(geom, q_blk, cache.c, bufs.sel_idx, bufs.sel_cnt, bufs.kmax,
+                               bufs.out, bufs.lse, scale, stream)
+    else:
+        lcsa_block_sparse_attn_tok(geom, q, cache.c, bufs.sel_idx, bufs.sel_cnt, bufs.kmax,
+                                   bufs.out, bufs.lse, scale, stream)
     if keep_tb is not None:
         cache.evict(keep_tb)
     return bufs
@@ -419,20 +453,28 @@ def run_step(geom: Geom, q, k, v, cache: KVCache, first_abs_tb: int, params: Sel
 
 def run_segment_step(geom: Geom, q, k, v, cache: KVCache, first_abs_tb: int, frame_seg,
                      bufs: StepBuffers | None = None, stream=None, want_lse=False,
-                     scale: float = 0.0):
+                     scale: float = 0.0, q_blocks: bool = False):
     """Stage-1 segment-masked attention of one chunk through the C-ABI, as a
     cold start: append, partition+pool, segment lists, masked attention,
-    then the cache is emptied again. Returns the StepBuffers."""
+    then the cache is emptied again. q_blocks as in run_step. Returns the
+    StepBuffers."""
     n_tb = geom.frames // 2
     first_slot = cache.append(n_tb, first_abs_tb)
     kmax = lcsa_segment_max_list(geom, frame_seg)
     if bufs is None:
-        bufs = StepBuffers(geom, kmax, device=q.device, with_lse=want_lse)
-    lcsa_partition_pool(geom, q, k, v, bufs.q_blk, bufs.q_pool, cache.c, first_slot, stream)
+        bufs = StepBuffers(geom, kmax, device=q.device, with_lse=want_lse, with_q_blk=q_blocks)
+    if q_blocks and bufs.q_blk is None:
+        raise ValueError("q_blocks=True needs StepBuffers(with_q_blk=True)")
+    q_blk = bufs.q_blk if q_blocks else None
+    lcsa_partition_pool(geom, q, k, v, q_blk, bufs.q_pool, cache.c, first_slot, stream)
     lcsa_segment_lists(geom, first_abs_tb, cache.c, frame_seg, bufs.kmax, bufs.sel_idx,
                        bufs.sel_cnt, stream)
-    lcsa_segment_attn(geom, bufs.q_blk, first_abs_tb, cache.c, frame_seg, bufs.sel_idx,
-                      bufs.sel_cnt, bufs.kmax, bufs.out, bufs.lse, scale, stream)
+    if q_blocks:
+        lcsa_segment_attn(geom, q_blk, first_abs_tb, cache.c, frame_seg, bufs.sel_idx,
+                          bufs.sel_cnt, bufs.kmax, bufs.out, bufs.lse, scale, stream)
+    else:
+        lcsa_segment_attn_tok(geom, q, first_abs_tb, cache.c, frame_seg, bufs.sel_idx,
+                              bufs.sel_cnt, bufs.kmax, bufs.out, bufs.lse, scale, stream)
     cache.evict(0)
     return bufs
 

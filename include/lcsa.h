@@ -22,8 +22,11 @@
  *   lcsa_kv_cache_append   reserve ring slots for the chunk's temporal blocks
  *   lcsa_partition_pool    partition q/k/v into blocks, mean-pool q and k,
  *                          write k/v blocks straight into the ring slots
+ *                          (q's blocks only when q_blk is given)
  *   lcsa_draft_mask        masked draft scores, row softmax, per-row top-k
- *   lcsa_block_sparse_attn exact attention over the selected block pairs
+ *   lcsa_block_sparse_attn exact attention over the selected block pairs,
+ *                          q read from q_blk (lcsa_block_sparse_attn_tok: q
+ *                          read in token layout, so q_blk is never written)
  *   lcsa_kv_cache_evict    drop the oldest temporal blocks beyond capacity
  *
  * Conventions shared by every entry point:
@@ -180,8 +183,10 @@ lcsa_status lcsa_max_topk(const lcsa_geom* gq, int64_t q_first_abs_tb,
  * blocks. q goes to q_blk with its block means in q_pool (float64); k and v
  * of temporal block t of the chunk go to ring slot (first_slot + t) %
  * n_slots, with the block means of k in kpool_ring. Those slots must be held
- * by the cache (reserved by lcsa_kv_cache_append). q, q_blk and q_pool are
- * either all NULL (fill the cache only) or all non-NULL. */
+ * by the cache (reserved by lcsa_kv_cache_append). q and q_pool are both
+ * NULL (fill the cache only) or both non-NULL; q_blk may be NULL with them,
+ * and then only q's block means are written (for the _tok attention entry
+ * points, which read q in token layout). q_blk without q is LCSA_ERR_NULL. */
 lcsa_status lcsa_partition_pool(const lcsa_geom* g, const void* q, const void* k,
                                 const void* v, void* q_blk, double* q_pool,
                                 lcsa_kv_cache* cache, int32_t first_slot,
@@ -235,6 +240,17 @@ lcsa_status lcsa_block_sparse_attn(const lcsa_geom* gq, const void* q_blk,
                                    const int32_t* sel_idx, const int32_t* sel_cnt,
                                    int32_t kmax, float scale, void* out, float* lse,
                                    void* stream);
+
+/* lcsa_block_sparse_attn ([FN] Key design 2, as above) with q read in token
+ * layout [B][T][H][W][NH][D] (geometry gq, the chunk's q as given to
+ * lcsa_partition_pool) instead of from q_blk: each query row is D
+ * contiguous values there too, and the partition need not write q_blk.
+ * Same results, arguments, errors and layouts otherwise. */
+lcsa_status lcsa_block_sparse_attn_tok(const lcsa_geom* gq, const void* q,
+                                       const lcsa_kv_cache* cache,
+                                       const int32_t* sel_idx, const int32_t* sel_cnt,
+                                       int32_t kmax, float scale, void* out, float* lse,
+                                       void* stream);
 
 /* ---- FlashVSR+ local lists ----------------------------------------------- */
 
@@ -300,6 +316,13 @@ lcsa_status lcsa_segment_attn(const lcsa_geom* gq, const void* q_blk, int64_t q_
                               const int32_t* sel_idx, const int32_t* sel_cnt, int32_t kmax,
                               float scale, void* out, float* lse, void* stream);
 
+/* lcsa_segment_attn with q read in token layout, as lcsa_block_sparse_attn_tok
+ * does; everything else as lcsa_segment_attn. */
+lcsa_status lcsa_segment_attn_tok(const lcsa_geom* gq, const void* q, int64_t q_first_abs_tb,
+                                  const lcsa_kv_cache* cache, const int32_t* frame_seg,
+                                  const int32_t* sel_idx, const int32_t* sel_cnt, int32_t kmax,
+                                  float scale, void* out, float* lse, void* stream);
+
 /* ---- Backward of the block-sparse attention ------------------------------ */
 
 /* [FN] Key design 1 trains the student on all frames of a clip in parallel
@@ -333,7 +356,7 @@ lcsa_status lcsa_block_sparse_attn_bwd(const lcsa_geom* g, const void* q, const 
 /* Text of the last error on this thread ("" after success). */
 const char* lcsa_last_error(void);
 
-/* Interface version of this header: 3. */
+/* Interface version of this header: 4. */
 int32_t lcsa_abi_version(void);
 
 #ifdef __cplusplus

@@ -47,11 +47,13 @@ def lib_params(w) -> L.SelectParams:
 class Stream:
     """Runs the same stream of chunks on the GPU and in the oracle."""
 
-    def __init__(self, w, device, seed=None, zero_q=False, side_stream=None, q_scale=None):
+    def __init__(self, w, device, seed=None, zero_q=False, side_stream=None, q_scale=None,
+                 q_blocks=False):
         import torch
         self.w = w
         self.q_scale = q_scale  # a power of two: exact in bf16, the same on both sides
         self.side = side_stream  # run the transposed-v partition part there
+        self.q_blocks = q_blocks  # write q_blk and read q from it, not the token layout
         self.dev = device
         self.seed = w.seed if seed is None else seed
         self.zero_q = zero_q
@@ -98,7 +100,7 @@ class Stream:
         local = w.lists == "local"
         bufs = L.run_step(self.geom, q, k, v, self.gcache, tb0, self.lp, keep_tb=w.cap_tb,
                           want_probs=want_probs and not local, want_lse=True, local=local,
-                          side_stream=self.side)
+                          side_stream=self.side, q_blocks=self.q_blocks)
         torch.cuda.synchronize()
         g = {"sel_idx": bufs.sel_idx.cpu().numpy(), "sel_cnt": bufs.sel_cnt.cpu().numpy(),
              "out": bufs.out, "lse": bufs.lse.cpu().numpy(),

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(lib):
     assert len(names) >= 10
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.lcsa_abi_version() == 3
+    assert lib.lcsa_abi_version() == 4
 
 
 FAKE = 0x10000  # aligned, never dereferenced: validation fails first
@@ -140,7 +140,7 @@ def test_validation_rejects_bad_input_before_any_device_call(lib):
     expect(3, L.lcsa_partition_pool, L.make_geom(1, 12, 128, 2, 48, 88, 7), ok, ok, ok, ok, ok, c, 0, s)
     # pointers
     expect(1, L.lcsa_partition_pool, geom, ok, None, ok, ok, ok, c, 0, s)
-    expect(1, L.lcsa_partition_pool, geom, ok, ok, ok, None, ok, c, 0, s)
+    expect(1, L.lcsa_partition_pool, geom, ok, ok, ok, ok, None, c, 0, s)   # q_pool missing
     expect(5, L.lcsa_partition_pool, geom, _P(FAKE + 8), ok, ok, ok, ok, c, 0, s)
     # slot not held
     expect(6, L.lcsa_partition_pool, geom, ok, ok, ok, ok, ok, c, 2, s)
@@ -152,7 +152,9 @@ def test_validation_rejects_bad_input_before_any_device_call(lib):
     expect(4, P, geom, ok, ok, ok, ok, ok, c, 0, 4, s)
     expect(1, P, geom, None, None, None, None, None, c, 0, L.PART_V, s)      # v missing
     expect(1, P, geom, ok, None, None, ok, ok, c, 0, L.PART_QK, s)           # k missing
-    expect(1, P, geom, ok, ok, None, None, ok, c, 0, L.PART_QK, s)           # q without q_blk
+    expect(1, P, geom, ok, ok, None, None, None, c, 0, L.PART_QK, s)         # q without q_pool
+    expect(1, P, geom, None, ok, None, ok, None, c, 0, L.PART_QK, s)         # q_blk without q
+    expect(5, P, geom, ok, ok, None, _P(FAKE + 8), ok, c, 0, L.PART_QK, s)   # q_blk misaligned
     expect(5, P, geom, None, None, _P(FAKE + 8), None, None, c, 0, L.PART_V, s)
     expect(6, P, geom, None, None, ok, None, None, c, 2, L.PART_V, s)        # slot not held
     expect(2, P, L.make_geom(1, 12, 128, 3, 48, 88, 0), None, ok, None, None, None, c, 0,
@@ -177,6 +179,15 @@ def test_validation_rejects_bad_input_before_any_device_call(lib):
     expect(4, L.lcsa_block_sparse_attn, geom, ok, c, ok, ok, 13, ok, None, -1.0, s)
     expect(6, L.lcsa_block_sparse_attn, geom, ok, c, ok, ok, 0, ok, None, 0.0, s)
     expect(1, L.lcsa_block_sparse_attn, geom, ok, c, None, ok, 13, ok, None, 0.0, s)
+    expect(1, L.lcsa_block_sparse_attn, geom, None, c, ok, ok, 13, ok, None, 0.0, s)
+    # the same checks with q in token layout
+    A = L.lcsa_block_sparse_attn_tok
+    expect(4, A, geom, ok, c, ok, ok, 13, ok, None, float("nan"), s)
+    expect(6, A, geom, ok, c, ok, ok, 0, ok, None, 0.0, s)
+    msg = expect(1, A, geom, None, c, ok, ok, 13, ok, None, 0.0, s)
+    assert "q is NULL" in msg
+    expect(5, A, geom, _P(FAKE + 8), c, ok, ok, 13, ok, None, 0.0, s)
+    expect(2, A, L.make_geom(1, 8, 128, 2, 48, 88, 0), ok, c, ok, ok, 13, ok, None, 0.0, s)
 
 
 def test_empty_chunk_is_a_no_op(lib):
@@ -187,6 +198,8 @@ def test_empty_chunk_is_a_no_op(lib):
     L.lcsa_partition_pool(geom, ok, ok, ok, ok, ok, c, 0, 0)
     L.lcsa_draft_mask(geom, ok, 0, c, L.make_params(), 1, ok, ok, None, 0)
     L.lcsa_block_sparse_attn(geom, ok, c, ok, ok, 1, ok, None, 0.0, 0)
+    L.lcsa_block_sparse_attn_tok(geom, ok, c, ok, ok, 1, ok, None, 0.0, 0)
+    L.lcsa_partition_pool(geom, ok, ok, ok, None, ok, c, 0, 0)  # q's means only
     assert L.lcsa_last_error() == ""
 
 
@@ -228,6 +241,10 @@ def test_segment_validation_before_any_device_call(lib):
         L.lcsa_segment_lists(g, 10, c, seg, 179, P, P, stream=0)
     with pytest.raises(L.LcsaError, match="LCSA_ERR_PARAM"):
         L.lcsa_segment_attn(g, P, 0, c, seg, P, P, 180, P, stream=0)
+    with pytest.raises(L.LcsaError, match="LCSA_ERR_PARAM"):
+        L.lcsa_segment_attn_tok(g, P, 0, c, seg, P, P, 180, P, stream=0)
+    with pytest.raises(L.LcsaError, match="LCSA_ERR_NULL"):
+        L.lcsa_segment_attn_tok(g, None, 10, c, seg, P, P, 180, P, stream=0)
     lib_ = L.load_library()
     assert lib_.lcsa_segment_lists(ctypes.byref(g), 10, ctypes.byref(c), None, 180, FAKE, FAKE,
                                    None) == 1  # LCSA_ERR_NULL

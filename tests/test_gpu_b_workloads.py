@@ -43,9 +43,10 @@ def small(**kw) -> Workload:
 
 
 def check_layouts(st: Stream, g, ref):
-    """Partition outputs: q blocks and the ring's K / V^T blocks, bitwise."""
-    qb = to_host64(g["q_blk"])
-    assert np.array_equal(qb, ref.q_blocks)
+    """Partition outputs: q blocks (when the step wrote them) and the ring's
+    K / V^T blocks, bitwise."""
+    if g["q_blk"] is not None:
+        assert np.array_equal(to_host64(g["q_blk"]), ref.q_blocks)
     kb, vb = ref.key_blocks
     slots, _ = st.gcache.view()  # after eviction; compare the blocks still held
     nS = st.w.nS

@@ -54,7 +54,7 @@ def block_tokens(w, b, i):
             for tau in range(128)]
 
 
-def run_case(dev, w: Workload, blocks=None, first_abs_tb=0):
+def run_case(dev, w: Workload, blocks=None, first_abs_tb=0, both_q_paths=False):
     seg = list(w.frame_seg)
     T = w.frames
     say(f"segment case {w.name}: T {T} {w.height}x{w.width} heads {w.heads} D {w.head_dim} "
@@ -68,6 +68,12 @@ def run_case(dev, w: Workload, blocks=None, first_abs_tb=0):
     q, k, v = (to_dev(d[n][0], w.dtype, dev) for n in "qkv")
     bufs = L.run_segment_step(geom, q, k, v, cache, first_abs_tb, seg, want_lse=True)
     torch.cuda.synchronize()
+    if both_q_paths:  # q read from q_blk instead of the token layout: bitwise the same
+        blk = L.run_segment_step(geom, q, k, v, cache, first_abs_tb, seg, want_lse=True,
+                                 q_blocks=True)
+        torch.cuda.synchronize()
+        for key in ("sel_idx", "sel_cnt", "out", "lse"):
+            assert torch.equal(getattr(bufs, key), getattr(blk, key)), key
     sel_idx, sel_cnt = bufs.sel_idx.cpu().numpy(), bufs.sel_cnt.cpu().numpy()
     out = to_host64(bufs.out)
     assert cache.view() == ([], [])
@@ -116,7 +122,7 @@ def small(**kw) -> Workload:
     dict(batch=2, frames=4, frame_seg=(0, 0, 0, 1)),                   # batch 2
 ], ids=["video+images", "interleaved-d64", "one-segment", "per-frame", "f32", "batch2"])
 def test_segment_small_all_tokens(dev, case):
-    run_case(dev, small(**case))
+    run_case(dev, small(**case), both_q_paths=True)
 
 
 def test_segment_stage1_768x1280(dev):

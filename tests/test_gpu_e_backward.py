@@ -70,7 +70,7 @@ def run(dev, w: Workload, k_of_tb, kmax, list_seed, empty_rows=()):
                       device=dev)
     slot = cache.append(n_tb, 0)
     q, k, v, g = (to_dev(d[n][0], "bf16", dev) for n in ("q", "k", "v", "dout"))
-    bufs = L.StepBuffers(geom, kmax, device=dev, with_lse=True)
+    bufs = L.StepBuffers(geom, kmax, device=dev, with_lse=True, with_q_blk=True)
     si, sc = torch.from_numpy(sel_idx).to(dev), torch.from_numpy(sel_cnt).to(dev)
     L.lcsa_partition_pool(geom, q, k, v, bufs.q_blk, bufs.q_pool, cache.c, slot)
     L.lcsa_block_sparse_attn(geom, bufs.q_blk, cache.c, si, sc, kmax, bufs.out, bufs.lse)
