@@ -19,7 +19,9 @@
 // takes the softmax and selects exactly k candidates (value-range bucket
 // select, ties to the lower logical id). Scores are float64 so the
 // selection is decided on values equal to the exact ones up to summation
-// order.
+// order. Rows are ranked on the raw dot products: dividing by sqrt(D) is
+// monotone and leaves the order as it is, so the division is only applied
+// to the softmax written to probs.
 #include "lcsa_kernels.h"
 #include "lcsa_window.h"
 
@@ -38,6 +40,16 @@ __device__ inline int xcd_task(int n_tasks) {
   const int t = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
   return t < n_tasks ? t : -1;
 }
+
+// Quotient of a small non-negative int by a divisor d >= 1 through an fp32
+// reciprocal, exact for n < 2^22: (n + 0.5) / d lies at least 0.5 / d from
+// an integer, and the two correctly rounded fp32 steps (1/d, then the
+// product) move it by less than (n + 0.5) * 2^-23 / d < 0.5 / d.
+struct SmallDiv {
+  float inv;
+  __device__ explicit SmallDiv(int d) : inv(1.0f / (float)d) {}
+  __device__ int operator()(int n) const { return (int)(((float)n + 0.5f) * inv); }
+};
 
 __device__ inline void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -121,7 +133,8 @@ __device__ inline uint32_t wave_prefix_sum_dpp(uint32_t x) {
 // copies are then taken lowest index first. Each level removes at least
 // one distinct value, so the loop ends; smooth score rows need 1-2 levels.
 __device__ void select_row(const DraftArgs& a, const double* s, size_t row, int nvis, int ylo,
-                           int ny, int gxlo, int gxhi, int64_t n_keys, uint32_t* hist, int lane) {
+                           int ny, int gxlo, int gxhi, int64_t n_keys, uint32_t* hist, int lane,
+                           double sqrt_d) {
   const int nby = a.nby, nbx = a.nbx, nS = nby * nbx;
   const int yhi = ylo + ny - 1;
   const int nx = gxhi - gxlo + 1;
@@ -141,14 +154,14 @@ __device__ void select_row(const DraftArgs& a, const double* s, size_t row, int 
   if (a.probs) {
     double* pr = a.probs + row * n_keys;
     double z = 0.0;
-    for (int c = lane; c < n; c += 64) z += exp(s[c] - hi);
+    for (int c = lane; c < n; c += 64) z += exp((s[c] - hi) / sqrt_d);
     z = wave_sum_f64(z);
     for (int64_t j = lane; j < n_keys; j += 64) {
       const int p = (int)(j / nS), rem = (int)(j % nS);
       const int y = rem / nbx, x = rem % nbx;
       double val = 0.0;
       if (p < nvis && y >= ylo && y <= yhi && x >= gxlo && x <= gxhi)
-        val = exp(s[(p * ny + (y - ylo)) * nx + (x - gxlo)] - hi) / z;
+        val = exp((s[(p * ny + (y - ylo)) * nx + (x - gxlo)] - hi) / sqrt_d) / z;
       pr[j] = val;
     }
   }
@@ -215,6 +228,7 @@ __device__ void select_row(const DraftArgs& a, const double* s, size_t row, int 
   // Emit in ascending candidate order (= ascending logical id): values above
   // the final range, then the first kr values inside it.
   int eq_before = 0, sel_before = 0;
+  const SmallDiv div_nx(nx), div_ny(ny);
   if (k > 0) {
     for (int base = 0; base < n; base += 64) {
       const int c = base + lane;
@@ -229,8 +243,8 @@ __device__ void select_row(const DraftArgs& a, const double* s, size_t row, int 
       const bool sel = want && pos < k;  // never more than k (only NaN scores could ask)
       const uint64_t bsel = __ballot(sel);
       if (sel) {
-        const int xx = c % nx, r3 = c / nx;
-        const int yy = r3 % ny, p = r3 / ny;
+        const int r3 = div_nx(c), xx = c - r3 * nx;
+        const int p = div_ny(r3), yy = r3 - p * ny;
         out[pos] = p * nS + (ylo + yy) * nbx + gxlo + xx;
       }
       eq_before += __popcll(beq);
@@ -292,11 +306,10 @@ __global__ __launch_bounds__(kThreads) void draft_mask_kernel(DraftArgs a) {
   __syncthreads();
 
   // Phase A: score every key of the group's union window against each row.
-  const double sqrt_d = sqrt((double)D);
+  const SmallDiv div_nux(nux), div_ny(ny);
   for (int u = tid; u < n_union; u += kThreads) {
-    const int ux = u % nux;
-    const int r2 = u / nux;
-    const int yy = r2 % ny, p = r2 / ny;
+    const int r2 = div_nux(u), ux = u - r2 * nux;
+    const int p = div_ny(r2), yy = r2 - p * ny;
     const int x = uxlo + ux, y = ylo + yy;
     const double* kp = a.kpool_ring + (bh * a.n_slots + a.view.slot[p]) * (size_t)D * nS +
                        (size_t)y * nbx + x;
@@ -313,7 +326,7 @@ __global__ __launch_bounds__(kThreads) void draft_mask_kernel(DraftArgs a) {
     for (int g = 0; g < GX; ++g) {
       if (g < ng && x >= xlo[g] && x <= xhi[g]) {
         const int nx = xhi[g] - xlo[g] + 1;
-        sc[(size_t)g * a.row_stride + (p * ny + yy) * nx + (x - xlo[g])] = acc[g] / sqrt_d;
+        sc[(size_t)g * a.row_stride + (p * ny + yy) * nx + (x - xlo[g])] = acc[g];
       }
     }
   }
@@ -325,7 +338,7 @@ __global__ __launch_bounds__(kThreads) void draft_mask_kernel(DraftArgs a) {
     int gxlo, gxhi;  // recomputed: a dynamic index into xlo[] would spill
     window_range(bx0 + g, nbx, a.local_range, a.border, &gxlo, &gxhi);
     select_row(a, sc + (size_t)g * a.row_stride, bh * nq + row0 + g, nvis, ylo, ny, gxlo, gxhi,
-               n_keys, hist, lane);
+               n_keys, hist, lane, sqrt((double)D));
   }
 }
 
@@ -394,19 +407,28 @@ __global__ __launch_bounds__(64 * kTileWaves) void draft_tile_kernel(DraftArgs a
     af[s2] = arow ? v : 0.0;
   }
 
-  // this lane's four output rows: (qy, qx) = (by0 + j, bx0 + dq)
+  // this lane's four output rows: (qy, qx) = (by0 + j, bx0 + dq), with
+  // their windows; an empty y range marks a row outside the grid
   const int oqx = bx0 + dq;
   int oxlo, oxhi;
   window_range(min(oqx, nbx - 1), nbx, a.local_range, a.border, &oxlo, &oxhi);
-  const double sqrt_d = sqrt((double)D);
+  const int onx = oxhi - oxlo + 1;
+  const bool ocol = oqx < nbx;
+  int oylo[4], oyhi[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    window_range(min(by0 + j, nby - 1), nby, a.local_range, a.border, &oylo[j], &oyhi[j]);
+    if (by0 + j >= nby) oyhi[j] = oylo[j] - 1;
+  }
+  const SmallDiv div_nux(nux), div_nuy(nuy);
 
   // key u of tile t lives at (p, y, x); u >= U pads with key 0 (a valid
   // address) and is zeroed after the load
   auto key_ptr = [&](int u, int& p, int& y, int& x) {
     const int uu = u < U ? u : 0;
-    const int ux = uu % nux, r2 = uu / nux;
-    y = uylo + r2 % nuy;
-    p = r2 / nuy;
+    const int r2 = div_nux(uu), ux = uu - r2 * nux;
+    p = div_nuy(r2);
+    y = uylo + r2 - p * nuy;
     x = uxlo + ux;
     return a.kpool_ring + (bh * a.n_slots + a.view.slot[p]) * (size_t)D * nS + (size_t)y * nbx + x;
   };
@@ -427,28 +449,25 @@ __global__ __launch_bounds__(64 * kTileWaves) void draft_tile_kernel(DraftArgs a
     load_half(2 * it + 1, b1);
     const int t = wave + it * kTileWaves;
     const int u = 16 * t + r;
-    const bool uval = u < U;
+    // a padding key (u >= U, loaded from key 0) only feeds output column u,
+    // which is never stored
     f64x4 acc = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int s2 = 0; s2 < HS; ++s2)
-      acc = __builtin_amdgcn_mfma_f64_16x16x4f64(af[s2], uval ? b0[s2] : 0.0, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64(af[s2], b0[s2], acc, 0, 0, 0);
     if (it + 1 < ntiles) load_half(2 * it + 2, b0);  // uniform
 #pragma unroll
     for (int s2 = 0; s2 < HS; ++s2)
-      acc = __builtin_amdgcn_mfma_f64_16x16x4f64(af[HS + s2], uval ? b1[s2] : 0.0, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64(af[HS + s2], b1[s2], acc, 0, 0, 0);
     int p, y, x;
     key_ptr(u, p, y, x);
-    if (uval && oqx < nbx && x >= oxlo && x <= oxhi) {
+    if (u < U && ocol && x >= oxlo && x <= oxhi) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int oqy = by0 + j;
-        if (oqy >= nby) continue;
-        int oylo, oyhi;
-        window_range(oqy, nby, a.local_range, a.border, &oylo, &oyhi);
-        if (y < oylo || y > oyhi) continue;
-        const int ny = oyhi - oylo + 1, nx = oxhi - oxlo + 1;
-        sc[(size_t)(4 * j + dq) * a.row_stride + (p * ny + (y - oylo)) * nx + (x - oxlo)] =
-            acc[j] / sqrt_d;
+        if (y < oylo[j] || y > oyhi[j]) continue;
+        const int ny = oyhi[j] - oylo[j] + 1;
+        sc[(size_t)(4 * j + dq) * a.row_stride + (p * ny + (y - oylo[j])) * onx + (x - oxlo)] =
+            acc[j];
       }
     }
   }
@@ -462,7 +481,7 @@ __global__ __launch_bounds__(64 * kTileWaves) void draft_tile_kernel(DraftArgs a
     window_range(qy, nby, a.local_range, a.border, &ylo, &yhi);
     window_range(qx, nbx, a.local_range, a.border, &xlo, &xhi);
     select_row(a, sc + (size_t)ro * a.row_stride, bh * nq + (size_t)tq * nS + qy * nbx + qx, nvis,
-               ylo, yhi - ylo + 1, xlo, xhi, n_keys, hist, lane);
+               ylo, yhi - ylo + 1, xlo, xhi, n_keys, hist, lane, sqrt((double)D));
   }
 }
 
