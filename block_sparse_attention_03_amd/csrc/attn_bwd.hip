@@ -14,24 +14,28 @@
 //
 // Four kernels, all bf16 on the gfx950 matrix cores (v_mfma_f32_32x32x16_bf16,
 // float32 accumulation):
-//  * prep:  per (block, head) the transposed tiles Q^T, K^T, dO^T ([D][128]),
-//           lse * log2(e) and delta, into the workspace;
+//  * prep:  per (block, head) lse * log2(e) and delta, into the workspace;
 //  * inverse lists: for each key block, the query blocks whose list holds
 //           it, ascending (binary search in the sorted lists, wave ballot),
 //           so dK / dV need no atomics and are deterministic;
 //  * dQ:    one workgroup per query block, walking its list;
 //           S^T = K Q^T and dP^T = V dO^T (A = K, V rows from LDS, B = Q, dO
-//           rows in registers), then dQ^T += K^T dS^T (A = K^T rows from LDS,
-//           B = dS^T straight from the accumulators);
+//           rows in registers), then dQ^T += K^T dS^T (A = K^T fragments by
+//           transposing LDS reads of the same K rows, B = dS^T straight from
+//           the accumulators);
 //  * dK/dV: one workgroup per key block, walking its inverse list;
 //           S = Q K^T and dP = dO V^T (A = Q, dO rows from LDS, B = K, V rows
-//           in registers), then dV^T += dO^T P and dK^T += Q^T dS (A = the
-//           transposed tiles from LDS, B = P, dS from the accumulators).
+//           in registers), then dV^T += dO^T P and dK^T += Q^T dS (A = dO^T,
+//           Q^T fragments by transposing reads of the same row tiles, B = P,
+//           dS from the accumulators).
+// Only row tiles travel from memory: the transposed operands come from
+// gfx950's ds_read_b64_tr_b16, so no transposed copy of q, k or dO exists.
 // As in the forward, the rows of the first products' A operands are read in
 // a permuted order so that each lane's accumulator values form the 8
 // contiguous k-elements of the next product's B fragment. Tiles are staged
 // in 32-row quarters, double-buffered in LDS with direct global->LDS loads,
-// and rows are XOR-swizzled in 16-byte chunks (conflict-free fragment reads).
+// and rows are XOR-swizzled in 16-byte chunks (conflict-free fragment and
+// transposing reads).
 #include "lcsa_kernels.h"
 #include "mfma_tiles.h"
 
@@ -41,13 +45,23 @@ namespace {
 template <int D>
 struct Q4 {                                   // one 32-row quarter of a block
   static constexpr int ROWB = 32 * D * 2;     // [32][D] row tile bytes
-  static constexpr int TRB = D * 32 * 2;      // [D][32] transposed tile bytes
   static constexpr int KCH = D / 8;           // 16-byte chunks per row
   static constexpr int NS = D / 16;           // k-steps over D
   static constexpr int NO = D / 32;           // 32-row tiles over D
   static constexpr int RLD = ROWB / 4096;     // 1 KB loads per wave for a row tile
-  static constexpr int TLD = TRB / 4096;      // and for a transposed tile
 };
+
+// Swizzle of the row tiles in LDS: 16-byte chunk c of row r sits at chunk
+// c ^ g(r), with g a bijection of the row's low four bits, so sixteen rows
+// read at one chunk (the 128-bit fragment reads) hit sixteen bank groups; g
+// also sends the four aligned rows that one transposing read covers (at four
+// aligned chunks) to four different 64-byte bank groups, which a plain
+// c ^ (r & 15) would not. An involution, like the forward's swizzles.
+template <int D>
+__device__ inline int swz_b(int row, int c) {
+  if constexpr (D == 128) return c ^ (((row & 3) << 2) | ((row >> 2) & 3));
+  else return c ^ ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));  // rows of 128 bytes
+}
 
 // Geometry of a chunk-relative block n and its token tau in the token layout.
 struct Tok {
@@ -91,28 +105,55 @@ __device__ inline void row_unit_offsets(const Tok& tk, int w, int lane,
 #pragma unroll
   for (int it = 0; it < G::RLD; ++it) {
     const int u = (it * 4 + w) * 64 + lane;
-    const int row = u / G::KCH, c = swz_row<D>(row, u % G::KCH);
+    const int row = u / G::KCH, c = swz_b<D>(row, u % G::KCH);
     const size_t tok = ((size_t)((row >> 3) & 7) * tk.W + (row & 7)) * tk.NH * tk.D;
     off[it] = (uint32_t)((tok + c * 8) * 2);
   }
 }
 
-// Offsets of this lane's units of a [D][32] column tile inside a [D][128]
-// transposed block (add 64 qq bytes for quarter qq).
+// A fragments of the transposed products (dV^T += dO^T P, dK^T += Q^T dS,
+// dQ^T += K^T dS^T) straight from a swizzled [32][D] row tile in LDS, with
+// gfx950's transposing LDS read (ds_read_b64_tr_b16). Within each group of
+// 16 lanes that instruction gives lane j, as element t, element j % 4 of the
+// 8 bytes read by lane 4 t + j / 4 of the group. So for the fragment of
+// column d = 32 dt + (L % 32) and rows 16 ks + 8 (L / 32) + 0..7, lane L
+// reads, for half h of the rows, row 16 ks + 8 (L / 32) + 4 h + (L % 16) / 4
+// at column 32 dt + 16 ((L / 16) % 2) + 4 (L % 4). The row's swizzle
+// (swz_b) does not depend on ks (it reads rows modulo 16), so one
+// offset per (h, dt) serves every k-step: add ks * 16 rows.
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef short short8v __attribute__((ext_vector_type(8)));
+
 template <int D>
-__device__ inline void col_unit_offsets(int w, int lane, uint32_t (&off)[Q4<D>::TLD]) {
+struct TrOff {
+  uint32_t off[2][Q4<D>::NO];
+  __device__ explicit TrOff(int lane) {
+    const int grp = lane >> 4, sl = lane & 15;
 #pragma unroll
-  for (int it = 0; it < Q4<D>::TLD; ++it) {
-    const int u = (it * 4 + w) * 64 + lane;
-    const int d = u >> 2, c = swz4(d, u & 3);
-    off[it] = (uint32_t)((d * 128 + c * 8) * 2);
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int dt = 0; dt < Q4<D>::NO; ++dt) {
+        const int row = 8 * (grp >> 1) + 4 * h + (sl >> 2);
+        const int col = 32 * dt + 16 * (grp & 1) + 4 * (sl & 3);
+        off[h][dt] = (uint32_t)(row * (D * 2) + swz_b<D>(row, col >> 3) * 16 + (col & 7) * 2);
+      }
   }
+};
+
+template <int D>
+__device__ __forceinline__ bf16x8 tr_frag(const char* tile, const TrOff<D>& t, int ks, int dt) {
+  typedef __attribute__((address_space(3))) short4v* lp;
+  const char* base = tile + ks * 16 * (D * 2);
+  const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(base + t.off[0][dt]));
+  const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(base + t.off[1][dt]));
+  const short8v v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
 }
 
-// Issue the direct loads of one quarter: a row tile (block base + per-lane
-// offsets) and / or a column tile. Buffer loads: the scalar resource holds
-// the tile's base and extent, the lane offset is the vector offset, so the
-// loads need no vector address arithmetic.
+// Issue the direct loads of one quarter's row tile (block base + per-lane
+// offsets). Buffer loads: the scalar resource holds the tile's base and
+// extent, the lane offset is the vector offset, so the loads need no vector
+// address arithmetic.
 template <int D>
 __device__ __forceinline__ void load_rows(const char* qblk, uint32_t span, const uint32_t* off,
                                           char* dst, int w) {  // qblk: the quarter's first token
@@ -123,49 +164,32 @@ __device__ __forceinline__ void load_rows(const char* qblk, uint32_t span, const
                                              0, 0);
 }
 
-template <int D>
-__device__ __forceinline__ void load_cols(const char* blk, const uint32_t* off,
-                                          int qq, char* dst, int w) {
-  const __amdgpu_buffer_rsrc_t r = raw_rsrc(blk, D * 128 * 2);
-#pragma unroll
-  for (int it = 0; it < Q4<D>::TLD; ++it)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, LDS_PTR(dst + (it * 4 + w) * 1024), 16, off[it],
-                                             64 * qq, 0, 0);
-}
-
-// Issue the loads of quarter qq of one key block for the dQ kernel: K rows,
-// V rows and K^T columns.
+// Issue the loads of quarter qq of one key block for the dQ kernel: K rows
+// and V rows.
 template <int D>
 __device__ __forceinline__ void issue_dq(const Tok& tk, const char* kb, const char* vb,
-                                         const char* ktb, const uint32_t* roff,
-                                         const uint32_t* coff, int qq, char* buf,
-                                         int w) {
+                                         const uint32_t* roff, int qq, char* buf, int w) {
   using G = Q4<D>;
   const size_t qo = tk.quarter_bytes(qq);
   load_rows<D>(kb + qo, tk.qspan, roff, buf, w);
   load_rows<D>(vb + qo, tk.qspan, roff, buf + G::ROWB, w);
-  load_cols<D>(ktb, coff, qq, buf + 2 * G::ROWB, w);
 }
 
 // Issue the loads of quarter qq of one query block for the dK/dV kernel: Q
-// rows, dO rows, Q^T and dO^T columns, and (wave 0) the quarter's lse2 and
+// rows, dO rows, and (wave 0) the quarter's lse2 and
 // delta values: lanes 0-7 fetch 32 lse2 values, lanes 8-15 the 32 delta
 // values, the other lanes repeat them into the rest of a 1 KB region.
 template <int D>
 __device__ __forceinline__ void issue_dkdv(const Tok& tk, const char* qb, const char* ob,
-                                           const char* qtb, const char* otb, const char* lb,
-                                           const uint32_t* roff, const uint32_t* coff, uint32_t loff,
+                                           const char* lb, const uint32_t* roff, uint32_t loff,
                                            int qq, char* buf, int w) {
   using G = Q4<D>;
   const size_t qo = tk.quarter_bytes(qq);
   load_rows<D>(qb + qo, tk.qspan, roff, buf, w);
   load_rows<D>(ob + qo, tk.qspan, roff, buf + G::ROWB, w);
-  load_cols<D>(qtb, coff, qq, buf + 2 * G::ROWB, w);
-  load_cols<D>(otb, coff, qq, buf + 2 * G::ROWB + G::TRB, w);
   if (w == 0)  // lb: the block's 256 floats (1 KB) of lse2 then delta
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(raw_rsrc(lb, 1024),
-                                             LDS_PTR(buf + 2 * G::ROWB + 2 * G::TRB), 16, loff,
-                                             128 * qq, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(raw_rsrc(lb, 1024), LDS_PTR(buf + 2 * G::ROWB), 16,
+                                             loff, 128 * qq, 0, 0);
 }
 
 // B fragments of 32 rows (this wave's rows 32w + l32) of block n: D values
@@ -209,19 +233,18 @@ __device__ __forceinline__ void store_rows(const Tok& tk, void* dst, int b, int 
 }
 
 // ---------------------------------------------------------------- prep ----
-// One workgroup per (block, head), heads fastest. Transposes q, k and dO of
-// the block into [D][128] tiles through one LDS stage and computes delta.
+// One workgroup per (block, head), heads fastest: lse * log2(e) and
+// delta = rowsum(dO * O) of the block's 128 queries, into the workspace.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
-  constexpr int CPT = D / 8, ITERS = 128 * CPT / 256, TPI = 256 / CPT, PITCH = D * 2 + 16;
-  __shared__ __attribute__((aligned(16))) char stage[128 * PITCH];
+  constexpr int CPT = D / 8, ITERS = 128 * CPT / 256, TPI = 256 / CPT;
   const Tok tk = make_tok(a);
   const int nq = (a.T / 2) * tk.nS;
   const int h = blockIdx.x % a.NH, n = (blockIdx.x / a.NH) % nq, b = blockIdx.x / (a.NH * nq);
   const size_t blk = ((size_t)b * a.NH + h) * nq + n;
   const int tid = threadIdx.x, c = tid % CPT, tsub = tid / CPT;
 
-  // delta: each token's CPT chunks sit on CPT consecutive lanes
+  // each token's CPT chunks sit on CPT consecutive lanes
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
     const int tau = it * TPI + tsub;
@@ -237,34 +260,6 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
       a.ld2[blk * 256 + tau] = a.lse[blk * 128 + tau] * kLog2e;
       a.ld2[blk * 256 + 128 + tau] = s;
     }
-  }
-
-  const void* srcs[3] = {a.q, a.k, a.dout};
-  void* dsts[3] = {a.qT, a.kT, a.doT};
-#pragma unroll
-  for (int tI = 0; tI < 3; ++tI) {
-    const char* src = (const char*)srcs[tI];
-#pragma unroll
-    for (int it = 0; it < ITERS; ++it) {
-      const int tau = it * TPI + tsub;
-      *reinterpret_cast<u32x4*>(stage + tau * PITCH + c * 16) =
-          *reinterpret_cast<const u32x4*>(src + (tk.off(b, h, n, tau) + c * 8) * 2);
-    }
-    __syncthreads();
-    char* dst = (char*)dsts[tI] + blk * (size_t)D * 128 * 2;
-#pragma unroll
-    for (int it = 0; it < ITERS; ++it) {  // [D][128]: 16 chunks of 8 tokens per row d
-      const int e = it * 256 + tid, d = e / 16, kc = e % 16;
-      uint32_t wv[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t lo = *reinterpret_cast<const uint16_t*>(stage + (kc * 8 + 2 * u) * PITCH + d * 2);
-        const uint32_t hi = *reinterpret_cast<const uint16_t*>(stage + (kc * 8 + 2 * u + 1) * PITCH + d * 2);
-        wv[u] = lo | (hi << 16);
-      }
-      *reinterpret_cast<u32x4*>(dst + ((size_t)d * 128 + kc * 8) * 2) = u32x4{wv[0], wv[1], wv[2], wv[3]};
-    }
-    __syncthreads();
   }
 }
 
@@ -307,7 +302,7 @@ template <int D>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   using G = Q4<D>;
   constexpr int NS = G::NS, NO = G::NO;
-  constexpr int BUF = 2 * G::ROWB + G::TRB;  // K rows, V rows, K^T columns
+  constexpr int BUF = 2 * G::ROWB;  // K rows, V rows
   __shared__ __attribute__((aligned(16))) char lds[2 * BUF > 128 * D * 2 ? 2 * BUF : 128 * D * 2];
 
   const Tok tk = make_tok(a);
@@ -338,22 +333,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     const float lse2 = a.ld2[row * 256 + 32 * w + l32];
     const float dlt = a.ld2[row * 256 + 128 + 32 * w + l32];
     const int prow = perm32(l32);
-    uint32_t roff[G::RLD], coff[G::TLD];
+    uint32_t roff[G::RLD];
     row_unit_offsets<D>(tk, w, lane, roff);
-    col_unit_offsets<D>(w, lane, coff);
-    const char *kb = nullptr, *vb = nullptr, *ktb = nullptr;
+    const TrOff<D> tro(lane);
+    const char *kb = nullptr, *vb = nullptr;
     auto block = [&](int j) {  // an invalid id loads block 0 and is skipped
       j = (unsigned)j < (unsigned)nq ? j : 0;
       const size_t base = tk.off(b, h, j, 0) * 2;
       kb = (const char*)a.k + base;
       vb = (const char*)a.v + base;
-      ktb = (const char*)a.kT + ((size_t)bh * nq + j) * D * 128 * 2;
     };
-    auto issue = [&](int qq, char* buf) { issue_dq<D>(tk, kb, vb, ktb, roff, coff, qq, buf, w); };
+    auto issue = [&](int qq, char* buf) { issue_dq<D>(tk, kb, vb, roff, qq, buf, w); };
     auto compute = [&](const char* cur) {
       const char* kr = cur;
       const char* vr = cur + G::ROWB;
-      const char* kt = cur + 2 * G::ROWB;
       f32x16 st, dp;
 #pragma unroll
       for (int e = 0; e < 16; ++e) st[e] = dp[e] = 0.f;
@@ -362,7 +355,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       bf16x8 ka[NS], va[NS];
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        const int off = prow * (D * 2) + swz_row<D>(prow, 2 * s + g) * 16;
+        const int off = prow * (D * 2) + swz_b<D>(prow, 2 * s + g) * 16;
         ka[s] = *reinterpret_cast<const bf16x8*>(kr + off);
         va[s] = *reinterpret_cast<const bf16x8*>(vr + off);
       }
@@ -372,15 +365,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
         st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s], qf[s], st, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[s], of[s], dp, 0, 0, 0);
       }
-      // the K^T fragments of the dQ^T products, read while the products run
+      // the K^T fragments of the dQ^T products (transposing reads of the K
+      // rows), read while the products run
       bf16x8 kta[2][NO];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int dt = 0; dt < NO; ++dt) {
-          const int d = 32 * dt + l32;
-          kta[ks][dt] = *reinterpret_cast<const bf16x8*>(kt + d * 64 + swz4(d, 2 * ks + g) * 16);
-        }
+        for (int dt = 0; dt < NO; ++dt) kta[ks][dt] = tr_frag<D>(kr, tro, ks, dt);
       __builtin_amdgcn_sched_barrier(0);
       bf16x8 ds[2];
 #pragma unroll
@@ -428,14 +419,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 
 // --------------------------------------------------------------- dK / dV ----
 // One workgroup per CU: the K / V fragments and both accumulators take about
-// 320 registers per lane, more than two workgroups per CU leave. Quarter
+// 350 registers per lane, more than two workgroups per CU leave. Quarter
 // buffers are double-buffered in LDS (a deeper prefetch measured no faster).
 template <int D>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   using G = Q4<D>;
   constexpr int NS = G::NS, NO = G::NO;
-  // Q rows, dO rows, Q^T columns, dO^T columns, then 1 KB for lse2 / delta
-  constexpr int BUF = 2 * G::ROWB + 2 * G::TRB + 1024;
+  // Q rows, dO rows, then 1 KB for lse2 / delta
+  constexpr int BUF = 2 * G::ROWB + 1024;
   __shared__ __attribute__((aligned(16))) char lds[2 * BUF > 128 * D * 2 ? 2 * BUF : 128 * D * 2];
 
   const Tok tk = make_tok(a);
@@ -466,29 +457,26 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
     row_frags<D>(tk, a.v, b, h, j, 32 * w + l32, g, vf);
     const float sl2 = a.scale * kLog2e;
     const int prow = perm32(l32);
-    uint32_t roff[G::RLD], coff[G::TLD];
+    uint32_t roff[G::RLD];
     row_unit_offsets<D>(tk, w, lane, roff);
-    col_unit_offsets<D>(w, lane, coff);
+    const TrOff<D> tro(lane);
     const uint32_t loff = 16 * (lane & 7) + ((lane & 8) ? 512 : 0);
     struct Src {
-      const char *q, *o, *qt, *ot, *l;
+      const char *q, *o, *l;
     };
     auto source = [&](int i) {
       const size_t base = tk.off(b, h, i, 0) * 2;
       const size_t qrow = (size_t)bh * nq + i;
       return Src{(const char*)a.q + base, (const char*)a.dout + base,
-                 (const char*)a.qT + qrow * D * 128 * 2, (const char*)a.doT + qrow * D * 128 * 2,
                  (const char*)(a.ld2 + qrow * 256)};
     };
     auto issue = [&](const Src& p, int qq, char* buf) {
-      issue_dkdv<D>(tk, p.q, p.o, p.qt, p.ot, p.l, roff, coff, loff, qq, buf, w);
+      issue_dkdv<D>(tk, p.q, p.o, p.l, roff, loff, qq, buf, w);
     };
     auto compute = [&](const char* cur) {
       const char* qr = cur;
       const char* orr = cur + G::ROWB;
-      const char* qt = cur + 2 * G::ROWB;
-      const char* ot = qt + G::TRB;
-      const float* ld = (const float*)(ot + G::TRB);  // [0, 32) lse2, [32, 64) delta
+      const float* ld = (const float*)(cur + 2 * G::ROWB);  // [0, 32) lse2, [32, 64) delta
       f32x16 st, dp;
 #pragma unroll
       for (int e = 0; e < 16; ++e) st[e] = dp[e] = 0.f;
@@ -497,7 +485,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
       bf16x8 qa[NS], oa[NS];
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        const int off = prow * (D * 2) + swz_row<D>(prow, 2 * s + g) * 16;
+        const int off = prow * (D * 2) + swz_b<D>(prow, 2 * s + g) * 16;
         qa[s] = *reinterpret_cast<const bf16x8*>(qr + off);
         oa[s] = *reinterpret_cast<const bf16x8*>(orr + off);
       }
@@ -507,17 +495,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
         st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], kf[s], st, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[s], vf[s], dp, 0, 0, 0);
       }
-      // the dO^T and Q^T fragments of the dV^T and dK^T products, read while
-      // the products above run
+      // the dO^T and Q^T fragments of the dV^T and dK^T products
+      // (transposing reads of the row tiles), read while the products above run
       bf16x8 ota[2][NO], qta[2][NO];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int dt = 0; dt < NO; ++dt) {
-          const int d = 32 * dt + l32;
-          const int off = d * 64 + swz4(d, 2 * ks + g) * 16;
-          ota[ks][dt] = *reinterpret_cast<const bf16x8*>(ot + off);
-          qta[ks][dt] = *reinterpret_cast<const bf16x8*>(qt + off);
+          ota[ks][dt] = tr_frag<D>(orr, tro, ks, dt);
+          qta[ks][dt] = tr_frag<D>(qr, tro, ks, dt);
         }
       __builtin_amdgcn_sched_barrier(0);
       // element 8ks + e is query 16ks + 8g + e of the quarter

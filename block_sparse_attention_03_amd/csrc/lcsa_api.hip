@@ -113,7 +113,7 @@ lcsa_status attn_args(const lcsa_geom* gq, const void* q, bool tokens,
 
 // Workspace sections of the backward, each rounded up to 256 bytes.
 struct BwdLayout {
-  size_t qT, kT, doT, delta, inv_cnt, inv_idx, total;
+  size_t delta, inv_cnt, inv_idx, total;
 };
 
 BwdLayout bwd_layout(const lcsa_geom& g) {
@@ -121,11 +121,7 @@ BwdLayout bwd_layout(const lcsa_geom& g) {
   const size_t nq = (size_t)(g.frames / 2) * (g.height / 8) * (g.width / 8);
   const size_t rows = (size_t)g.batch * g.heads * nq;
   BwdLayout L{};
-  const size_t tile = up(rows * g.head_dim * 128 * 2);
-  L.qT = 0;
-  L.kT = L.qT + tile;
-  L.doT = L.kT + tile;
-  L.delta = L.doT + tile;
+  L.delta = 0;
   L.inv_cnt = L.delta + up(rows * 256 * 4);
   L.inv_idx = L.inv_cnt + up(rows * 4);
   L.total = L.inv_idx + up(rows * nq * 4);
@@ -393,9 +389,6 @@ lcsa_status lcsa_block_sparse_attn_bwd(const lcsa_geom* g, const void* q, const 
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  a.qT = ws + lay.qT;
-  a.kT = ws + lay.kT;
-  a.doT = ws + lay.doT;
   a.ld2 = (float*)(ws + lay.delta);
   a.inv_cnt = (int32_t*)(ws + lay.inv_cnt);
   a.inv_idx = (int32_t*)(ws + lay.inv_idx);

@@ -96,9 +96,6 @@ struct BwdArgs {
   void* dq;                 // token layout, bf16
   void* dk;
   void* dv;
-  void* qT;                 // workspace [B][NH][nq][D][128] bf16 (transposed tiles)
-  void* kT;
-  void* doT;
   float* ld2;               // workspace [B][NH][nq][256]: lse * log2(e) of the 128 queries,
                             // then rowsum(dO * O) of the same queries
   int32_t* inv_cnt;         // workspace [B][NH][nq]: query blocks selecting key block j

@@ -337,9 +337,9 @@ lcsa_status lcsa_segment_attn_tok(const lcsa_geom* gq, const void* q, int64_t q_
  * with ids < nq; larger ids are skipped, as in the forward. scale 0 means
  * 1/sqrt(D). bf16 only (LCSA_ERR_DTYPE otherwise). */
 
-/* Bytes of device workspace lcsa_block_sparse_attn_bwd needs for g:
- * transposed q, k, dout tiles, rowsum(dout * out) and the inverse lists
- * (B*NH*nq*nq int32). Host only. */
+/* Bytes of device workspace lcsa_block_sparse_attn_bwd needs for g: the
+ * scaled lse and rowsum(dout * out) of every query (B*NH*nq*256 float32)
+ * and the inverse lists (B*NH*nq counts, B*NH*nq*nq int32). Host only. */
 lcsa_status lcsa_attn_bwd_workspace_size(const lcsa_geom* g, size_t* bytes_out);
 
 /* dq, dk, dv of the attention over the listed blocks (all three written in
