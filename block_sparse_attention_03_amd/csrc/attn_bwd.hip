@@ -37,6 +37,7 @@
 // and rows are XOR-swizzled in 16-byte chunks (conflict-free fragment and
 // transposing reads).
 #include "lcsa_kernels.h"
+#include "lds_transpose.h"
 #include "mfma_tiles.h"
 
 namespace lcsa {
@@ -50,18 +51,6 @@ struct Q4 {                                   // one 32-row quarter of a block
   static constexpr int NO = D / 32;           // 32-row tiles over D
   static constexpr int RLD = ROWB / 4096;     // 1 KB loads per wave for a row tile
 };
-
-// Swizzle of the row tiles in LDS: 16-byte chunk c of row r sits at chunk
-// c ^ g(r), with g a bijection of the row's low four bits, so sixteen rows
-// read at one chunk (the 128-bit fragment reads) hit sixteen bank groups; g
-// also sends the four aligned rows that one transposing read covers (at four
-// aligned chunks) to four different 64-byte bank groups, which a plain
-// c ^ (r & 15) would not. An involution, like the forward's swizzles.
-template <int D>
-__device__ inline int swz_b(int row, int c) {
-  if constexpr (D == 128) return c ^ (((row & 3) << 2) | ((row >> 2) & 3));
-  else return c ^ ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));  // rows of 128 bytes
-}
 
 // Geometry of a chunk-relative block n and its token tau in the token layout.
 struct Tok {
@@ -105,50 +94,15 @@ __device__ inline void row_unit_offsets(const Tok& tk, int w, int lane,
 #pragma unroll
   for (int it = 0; it < G::RLD; ++it) {
     const int u = (it * 4 + w) * 64 + lane;
-    const int row = u / G::KCH, c = swz_b<D>(row, u % G::KCH);
+    const int row = u / G::KCH, c = swz_t<D>(row, u % G::KCH);
     const size_t tok = ((size_t)((row >> 3) & 7) * tk.W + (row & 7)) * tk.NH * tk.D;
     off[it] = (uint32_t)((tok + c * 8) * 2);
   }
 }
 
 // A fragments of the transposed products (dV^T += dO^T P, dK^T += Q^T dS,
-// dQ^T += K^T dS^T) straight from a swizzled [32][D] row tile in LDS, with
-// gfx950's transposing LDS read (ds_read_b64_tr_b16). Within each group of
-// 16 lanes that instruction gives lane j, as element t, element j % 4 of the
-// 8 bytes read by lane 4 t + j / 4 of the group. So for the fragment of
-// column d = 32 dt + (L % 32) and rows 16 ks + 8 (L / 32) + 0..7, lane L
-// reads, for half h of the rows, row 16 ks + 8 (L / 32) + 4 h + (L % 16) / 4
-// at column 32 dt + 16 ((L / 16) % 2) + 4 (L % 4). The row's swizzle
-// (swz_b) does not depend on ks (it reads rows modulo 16), so one
-// offset per (h, dt) serves every k-step: add ks * 16 rows.
-typedef short short4v __attribute__((ext_vector_type(4)));
-typedef short short8v __attribute__((ext_vector_type(8)));
-
-template <int D>
-struct TrOff {
-  uint32_t off[2][Q4<D>::NO];
-  __device__ explicit TrOff(int lane) {
-    const int grp = lane >> 4, sl = lane & 15;
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int dt = 0; dt < Q4<D>::NO; ++dt) {
-        const int row = 8 * (grp >> 1) + 4 * h + (sl >> 2);
-        const int col = 32 * dt + 16 * (grp & 1) + 4 * (sl & 3);
-        off[h][dt] = (uint32_t)(row * (D * 2) + swz_b<D>(row, col >> 3) * 16 + (col & 7) * 2);
-      }
-  }
-};
-
-template <int D>
-__device__ __forceinline__ bf16x8 tr_frag(const char* tile, const TrOff<D>& t, int ks, int dt) {
-  typedef __attribute__((address_space(3))) short4v* lp;
-  const char* base = tile + ks * 16 * (D * 2);
-  const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(base + t.off[0][dt]));
-  const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(base + t.off[1][dt]));
-  const short8v v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, v);
-}
+// dQ^T += K^T dS^T) come straight from the row tiles in LDS by transposing
+// reads (lds_transpose.h); the row tiles use its swizzle swz_t.
 
 // Issue the direct loads of one quarter's row tile (block base + per-lane
 // offsets). Buffer loads: the scalar resource holds the tile's base and
@@ -355,7 +309,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       bf16x8 ka[NS], va[NS];
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        const int off = prow * (D * 2) + swz_b<D>(prow, 2 * s + g) * 16;
+        const int off = prow * (D * 2) + swz_t<D>(prow, 2 * s + g) * 16;
         ka[s] = *reinterpret_cast<const bf16x8*>(kr + off);
         va[s] = *reinterpret_cast<const bf16x8*>(vr + off);
       }
@@ -485,7 +439,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
       bf16x8 qa[NS], oa[NS];
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        const int off = prow * (D * 2) + swz_b<D>(prow, 2 * s + g) * 16;
+        const int off = prow * (D * 2) + swz_t<D>(prow, 2 * s + g) * 16;
         qa[s] = *reinterpret_cast<const bf16x8*>(qr + off);
         oa[s] = *reinterpret_cast<const bf16x8*>(orr + off);
       }

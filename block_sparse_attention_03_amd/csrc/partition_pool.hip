@@ -12,19 +12,19 @@
 // channels contiguous (D*esize = 128..512 bytes), so every read is a run of
 // whole 16-byte chunks; every write is a fully contiguous 128 x D tile. V is
 // written transposed ([D][128]) because the attention kernel feeds V^T to
-// the matrix cores as the A operand. Block means of q and k are accumulated
+// the matrix cores as the A operand; bf16 V is transposed in LDS by
+// gfx950's transposing read. Block means of q and k are accumulated
 // in float64 (exact for bf16 inputs of moderate range) and written as
 // float64, so the draft selection downstream takes its decision on exact
 // pooled values. HBM-bound: the algorithmic traffic of one (block, head) is
 // 3 tiles read + 3 tiles written + 2 pooled rows.
 #include "lcsa_kernels.h"
+#include "lds_transpose.h"
 
 namespace lcsa {
 namespace {
 
 constexpr int kThreads = 256;
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // native vector: stays in VGPRs
 
 template <int ESZ>
 __device__ inline void widen_chunk(const u32x4& v, double* out);
@@ -146,7 +146,32 @@ __global__ __launch_bounds__(kThreads) void partition_pool_kernel(PartitionArgs 
   load_block<ESZ, D>(a, (const char*)src, b, h, bt, by, bx, v);
 
   if (role == 1) {
-    // v: stage the block, then write it transposed ([D][128])
+    char* vdst = (char*)a.v_ring + ring_blk * tile * ESZ;
+    if constexpr (ESZ == 2) {
+      // v (bf16): stage the block row-major under the transposing-read
+      // swizzle, then every 16-byte chunk of the [D][128] tile (8 tokens of
+      // one channel d) comes from two transposing reads. Wave w takes the
+      // pairs (column group dt, 16-token step ks) w, w + 4, ...
+      const int c = tid % G::CPT, tsub = tid / G::CPT;
+#pragma unroll
+      for (int it = 0; it < G::ITERS; ++it) {
+        const int tau = it * G::TPI + tsub;
+        *reinterpret_cast<u32x4*>(smem + tau * (D * 2) + swz_t<D>(tau, c) * 16) = v[it];
+      }
+      __syncthreads();
+      const int lane = tid & 63, w = tid >> 6;
+      const TrOff<D> tro(lane);
+#pragma unroll
+      for (int pi = w; pi < (D / 32) * 8; pi += kThreads / 64) {
+        const int dt = pi % (D / 32), ks = pi / (D / 32);
+        const int d = 32 * dt + (lane & 31), kc = 2 * ks + (lane >> 5);
+        const bf16x8 x = tr_frag<D>(smem, tro, ks, dt);
+        *reinterpret_cast<u32x4*>(vdst + ((size_t)d * 128 + kc * 8) * 2) =
+            __builtin_bit_cast(u32x4, x);
+      }
+      return;
+    }
+    // v (float32): stage the block, then write it transposed ([D][128])
     const int c = tid % G::CPT, tsub = tid / G::CPT;
 #pragma unroll
     for (int it = 0; it < G::ITERS; ++it) {
@@ -154,27 +179,15 @@ __global__ __launch_bounds__(kThreads) void partition_pool_kernel(PartitionArgs 
       *reinterpret_cast<u32x4*>(smem + tau * G::PITCH + c * 16) = v[it];
     }
     __syncthreads();
-    char* vdst = (char*)a.v_ring + ring_blk * tile * ESZ;
     constexpr int KC = 128 / G::EPC;  // 16-byte chunks per transposed row
 #pragma unroll
     for (int it = 0; it < G::ITERS; ++it) {
       const int e = it * kThreads + tid;
       const int d = e / KC, kc = e % KC;
       uint32_t w[4];
-      if constexpr (ESZ == 2) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const uint32_t lo =
-              *reinterpret_cast<const uint16_t*>(smem + (kc * 8 + 2 * u) * G::PITCH + d * 2);
-          const uint32_t hi =
-              *reinterpret_cast<const uint16_t*>(smem + (kc * 8 + 2 * u + 1) * G::PITCH + d * 2);
-          w[u] = lo | (hi << 16);
-        }
-      } else {
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          w[u] = *reinterpret_cast<const uint32_t*>(smem + (kc * 4 + u) * G::PITCH + d * 4);
-      }
+      for (int u = 0; u < 4; ++u)
+        w[u] = *reinterpret_cast<const uint32_t*>(smem + (kc * 4 + u) * G::PITCH + d * 4);
       *reinterpret_cast<u32x4*>(vdst + ((size_t)d * 128 + kc * G::EPC) * ESZ) =
           u32x4{w[0], w[1], w[2], w[3]};
     }
