@@ -372,11 +372,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 }
 
 // --------------------------------------------------------------- dK / dV ----
-// One workgroup per CU: the K / V fragments and both accumulators take about
-// 350 registers per lane, more than two workgroups per CU leave. Quarter
-// buffers are double-buffered in LDS (a deeper prefetch measured no faster).
+// Two workgroups per CU (256 registers per lane, 34 KB of LDS each): the
+// fragments of every product are read from LDS right before it, and the
+// co-resident workgroup covers that latency. Quarter buffers are
+// double-buffered in LDS (a deeper prefetch measured no faster).
 template <int D>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   using G = Q4<D>;
   constexpr int NS = G::NS, NO = G::NO;
   // Q rows, dO rows, then 1 KB for lse2 / delta
@@ -434,33 +435,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
       f32x16 st, dp;
 #pragma unroll
       for (int e = 0; e < 16; ++e) st[e] = dp[e] = 0.f;
-      // every A fragment of the S and dP products is read before the first
-      // product (one LDS wait per quarter, not one per product)
-      bf16x8 qa[NS], oa[NS];
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const int off = prow * (D * 2) + swz_t<D>(prow, 2 * s + g) * 16;
-        qa[s] = *reinterpret_cast<const bf16x8*>(qr + off);
-        oa[s] = *reinterpret_cast<const bf16x8*>(orr + off);
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(qr + off),
+                                                     kf[s], st, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(orr + off),
+                                                     vf[s], dp, 0, 0, 0);
       }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], kf[s], st, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[s], vf[s], dp, 0, 0, 0);
-      }
-      // the dO^T and Q^T fragments of the dV^T and dK^T products
-      // (transposing reads of the row tiles), read while the products above run
-      bf16x8 ota[2][NO], qta[2][NO];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int dt = 0; dt < NO; ++dt) {
-          ota[ks][dt] = tr_frag<D>(orr, tro, ks, dt);
-          qta[ks][dt] = tr_frag<D>(qr, tro, ks, dt);
-        }
-      __builtin_amdgcn_sched_barrier(0);
-      // element 8ks + e is query 16ks + 8g + e of the quarter
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const int q = 16 * ks + 8 * g;
@@ -473,21 +455,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
         }
 #pragma unroll
         for (int dt = 0; dt < NO; ++dt) {
-          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ota[ks][dt], pb, dv[dt], 0, 0, 0);
-          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qta[ks][dt], dsb, dk[dt], 0, 0, 0);
+          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(orr, tro, ks, dt), pb, dv[dt], 0, 0, 0);
+          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(qr, tro, ks, dt), dsb, dk[dt], 0, 0, 0);
         }
       }
-      // issue order: the lse / delta reads and the first k-step's softmax,
-      // then the first k-step's products each followed by a share of the
-      // second k-step's softmax, then the second k-step's products
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 36, 0);
-#pragma unroll
-      for (int i = 0; i < 2 * NO; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 2 * NO, 0);
     };
     // quarter qq of query block n sits in buffer qq & 1; the next is in flight
     char* buf0 = lds;
