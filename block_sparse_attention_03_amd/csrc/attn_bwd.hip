@@ -301,32 +301,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     auto compute = [&](const char* cur) {
       const char* kr = cur;
       const char* vr = cur + G::ROWB;
+      // every product's A fragments are read from LDS right before it; the
+      // co-resident workgroup covers that latency
       f32x16 st, dp;
 #pragma unroll
       for (int e = 0; e < 16; ++e) st[e] = dp[e] = 0.f;
-      // every A fragment of the S^T and dP^T products is read before the
-      // first product, so the wave waits for LDS once, not per product
-      bf16x8 ka[NS], va[NS];
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const int off = prow * (D * 2) + swz_t<D>(prow, 2 * s + g) * 16;
-        ka[s] = *reinterpret_cast<const bf16x8*>(kr + off);
-        va[s] = *reinterpret_cast<const bf16x8*>(vr + off);
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(kr + off),
+                                                     qf[s], st, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(vr + off),
+                                                     of[s], dp, 0, 0, 0);
       }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s], qf[s], st, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[s], of[s], dp, 0, 0, 0);
-      }
-      // the K^T fragments of the dQ^T products (transposing reads of the K
-      // rows), read while the products run
-      bf16x8 kta[2][NO];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int dt = 0; dt < NO; ++dt) kta[ks][dt] = tr_frag<D>(kr, tro, ks, dt);
-      __builtin_amdgcn_sched_barrier(0);
       bf16x8 ds[2];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -337,7 +324,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int dt = 0; dt < NO; ++dt)
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kta[ks][dt], ds[ks], acc[dt], 0, 0, 0);
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(kr, tro, ks, dt), ds[ks],
+                                                            acc[dt], 0, 0, 0);
     };
     char* buf0 = lds;
     char* buf1 = lds + BUF;
@@ -432,6 +420,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
       const char* qr = cur;
       const char* orr = cur + G::ROWB;
       const float* ld = (const float*)(cur + 2 * G::ROWB);  // [0, 32) lse2, [32, 64) delta
+      // every product's A fragments are read from LDS right before it
       f32x16 st, dp;
 #pragma unroll
       for (int e = 0; e < 16; ++e) st[e] = dp[e] = 0.f;
@@ -443,6 +432,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(orr + off),
                                                      vf[s], dp, 0, 0, 0);
       }
+      // element 8ks + e of the accumulators is query 16ks + 8g + e of the quarter
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const int q = 16 * ks + 8 * g;
@@ -455,8 +445,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
         }
 #pragma unroll
         for (int dt = 0; dt < NO; ++dt) {
-          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(orr, tro, ks, dt), pb, dv[dt], 0, 0, 0);
-          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(qr, tro, ks, dt), dsb, dk[dt], 0, 0, 0);
+          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(orr, tro, ks, dt), pb,
+                                                           dv[dt], 0, 0, 0);
+          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(qr, tro, ks, dt), dsb,
+                                                           dk[dt], 0, 0, 0);
         }
       }
     };
