@@ -347,19 +347,24 @@ typedef double f64x4 __attribute__((ext_vector_type(4)));
 // Matrix-core path for windows of up to kTileMaxCand candidates per row. A
 // workgroup scores a 4 x 4 tile of query blocks (16 rows, one
 // v_mfma_f64_16x16x4f64 row tile) against the union of their windows in
-// tiles of 16 keys: A = pooled queries (registers), B = pooled keys read
-// straight from the d-major pooled ring (16 consecutive keys per d are one
-// 128-byte run). Lane l holds A[l%16][l/16], B[l/16][l%16] and outputs
-// D[4j + l/16][l%16], j = 0..3. Each output lands in LDS at its row's
-// candidate index; then one wave per row runs select_row().
+// tiles of 16 keys: A = pooled queries (staged d-major in LDS), B = pooled
+// keys read straight from the d-major pooled ring (16 consecutive keys per d
+// are one 128-byte run). Lane l holds A[l%16][l/16], B[l/16][l%16] and
+// outputs D[4j + l/16][l%16], j = 0..3. Each output lands in LDS at its
+// row's candidate index; then one wave per row runs select_row(). At most
+// 128 registers per lane, so two workgroups share a CU where the LDS allows
+// (up to 484 candidates per row): one's selection overlaps the other's
+// scoring, and a half tile of key loads in flight per wave suffices.
 constexpr int kTileMaxCand = 768;
 constexpr int kTileWaves = 8;  // 16 rows: two per wave in the selection phase
 
 template <int D>
-__global__ __launch_bounds__(64 * kTileWaves) void draft_tile_kernel(DraftArgs a) {
+__global__ __launch_bounds__(64 * kTileWaves, 4) void draft_tile_kernel(DraftArgs a) {
   extern __shared__ double smem[];
-  double* sc = smem;                                                         // [16][row_stride]
-  uint32_t* hist_all = reinterpret_cast<uint32_t*>(sc + 16 * (size_t)a.row_stride);  // [waves][256]
+  double* sc = smem;                                  // [16][row_stride] scores
+  double* sa = sc + 16 * (size_t)a.row_stride;        // [D][16] pooled queries, d-major
+  // the selection's histograms reuse the pooled-query region once scoring is done
+  uint32_t* hist_all = reinterpret_cast<uint32_t*>(sa);  // [waves][256]
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int nby = a.nby, nbx = a.nbx, nS = nby * nbx;
@@ -392,20 +397,20 @@ __global__ __launch_bounds__(64 * kTileWaves) void draft_tile_kernel(DraftArgs a
   const int nuy = uyhi - uylo + 1, nux = uxhi - uxlo + 1;
   const int U = nvis * nuy * nux;
 
-  // A fragments: row lane%16 is query block (by0 + r/4, bx0 + r%4)
-  const int r = lane & 15, dq = lane >> 4;
-  const int aqy = by0 + (r >> 2), aqx = bx0 + (r & 3);
-  const bool arow = aqy < nby && aqx < nbx;
-  // clamped address: loads are unconditional (no per-load branches), the
-  // padding rows of an edge tile are zeroed afterwards
-  const double* qrow =
-      a.q_pool + (bh * nq + (size_t)tq * nS + min(aqy, nby - 1) * nbx + min(aqx, nbx - 1)) * D;
-  double af[D / 4];
-#pragma unroll
-  for (int s2 = 0; s2 < D / 4; ++s2) {
-    const double v = qrow[4 * s2 + dq];
-    af[s2] = arow ? v : 0.0;
+  // A operand: row rr of the tile is query block (by0 + rr/4, bx0 + rr%4),
+  // staged d-major ([D][16]) so that the 16 rows of one k read 128
+  // contiguous bytes (conflict-free); padding rows of an edge tile are 0
+  for (int e = tid; e < 16 * D; e += 64 * kTileWaves) {
+    const int rr = e % 16, d = e / 16;
+    const int qy = by0 + (rr >> 2), qx = bx0 + (rr & 3);
+    sa[e] = (qy < nby && qx < nbx)
+                ? a.q_pool[(bh * nq + (size_t)tq * nS + qy * nbx + qx) * D + d]
+                : 0.0;
   }
+  __syncthreads();
+  // lane (r, dq) holds A[r][4 s2 + dq] of k-step s2
+  const int r = lane & 15, dq = lane >> 4;
+  const double* arow = sa + dq * 16 + r;
 
   // this lane's four output rows: (qy, qx) = (by0 + j, bx0 + dq), with
   // their windows; an empty y range marks a row outside the grid
@@ -432,35 +437,27 @@ __global__ __launch_bounds__(64 * kTileWaves) void draft_tile_kernel(DraftArgs a
     x = uxlo + ux;
     return a.kpool_ring + (bh * a.n_slots + a.view.slot[p]) * (size_t)D * nS + (size_t)y * nbx + x;
   };
-  // Software pipeline over half tiles (16 of the 32 k-steps): the next
-  // half's 16 loads are in flight while the current half's MFMAs run.
+  // One half tile (16 of the 32 k-steps) of key loads in flight at a time;
+  // the other resident workgroup covers their latency.
   constexpr int HS = D / 8;  // k-steps per half tile
-  auto load_half = [&](int q, double (&bf)[HS]) {
-    int p, y, x;
-    const int t = wave + (q >> 1) * kTileWaves;
-    const double* kp = key_ptr(16 * t + r, p, y, x) + (size_t)((q & 1) * HS * 4) * nS;
-#pragma unroll
-    for (int s2 = 0; s2 < HS; ++s2) bf[s2] = kp[(size_t)(4 * s2 + dq) * nS];
-  };
   const int ntiles = U > 16 * wave ? (U - 16 * wave + 16 * kTileWaves - 1) / (16 * kTileWaves) : 0;
-  double b0[HS], b1[HS];
-  if (ntiles > 0) load_half(0, b0);
   for (int it = 0; it < ntiles; ++it) {
-    load_half(2 * it + 1, b1);
     const int t = wave + it * kTileWaves;
     const int u = 16 * t + r;
+    int p, y, x;
+    const double* kp = key_ptr(u, p, y, x);
     // a padding key (u >= U, loaded from key 0) only feeds output column u,
     // which is never stored
     f64x4 acc = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-    for (int s2 = 0; s2 < HS; ++s2)
-      acc = __builtin_amdgcn_mfma_f64_16x16x4f64(af[s2], b0[s2], acc, 0, 0, 0);
-    if (it + 1 < ntiles) load_half(2 * it + 2, b0);  // uniform
+    for (int hh = 0; hh < 2; ++hh) {
+      double bf[HS];
 #pragma unroll
-    for (int s2 = 0; s2 < HS; ++s2)
-      acc = __builtin_amdgcn_mfma_f64_16x16x4f64(af[HS + s2], b1[s2], acc, 0, 0, 0);
-    int p, y, x;
-    key_ptr(u, p, y, x);
+      for (int s2 = 0; s2 < HS; ++s2) bf[s2] = kp[(size_t)(hh * HS * 4 + 4 * s2 + dq) * nS];
+#pragma unroll
+      for (int s2 = 0; s2 < HS; ++s2)
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(arow[(hh * HS + s2) * 64], bf[s2], acc, 0, 0, 0);
+    }
     if (u < U && ocol && x >= oxlo && x <= oxhi) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -471,7 +468,7 @@ __global__ __launch_bounds__(64 * kTileWaves) void draft_tile_kernel(DraftArgs a
       }
     }
   }
-  __syncthreads();
+  __syncthreads();  // scores complete; the pooled-query region becomes the histograms
 
   uint32_t* hist = hist_all + wave * 256;
   for (int ro = wave; ro < 16; ro += kTileWaves) {
@@ -489,7 +486,10 @@ template <int D>
 hipError_t launch_tile(const DraftArgs& a, hipStream_t s) {
   const long long tasks = (long long)a.B * a.NH * a.ntb_q * ((a.nby + 3) / 4) * ((a.nbx + 3) / 4);
   const long long wgs = 8 * ((tasks + 7) / 8);
-  const size_t shmem = 16 * (size_t)a.row_stride * sizeof(double) + kTileWaves * 256 * 4;
+  constexpr size_t kAux = (size_t)D * 16 * sizeof(double) > kTileWaves * 256 * 4
+                             ? (size_t)D * 16 * sizeof(double)
+                             : kTileWaves * 256 * 4;
+  const size_t shmem = 16 * (size_t)a.row_stride * sizeof(double) + kAux;
   if (shmem > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute((const void*)draft_tile_kernel<D>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);

@@ -20,12 +20,11 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // native vector: s
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// XOR swizzles of 16-byte chunk c in LDS rows of 256, 128 and 64 bytes:
-// sixteen consecutive rows read at one logical chunk hit sixteen different
-// bank groups. Involutions: the same map goes logical -> physical and back.
+// XOR swizzles of 16-byte chunk c in LDS rows of 256 and 128 bytes: sixteen
+// consecutive rows read at one logical chunk hit sixteen different bank
+// groups. Involutions: the same map goes logical -> physical and back.
 __device__ inline int swz16(int row, int c) { return c ^ (row & 15); }
 __device__ inline int swz8(int row, int c) { return c ^ ((row >> 1) & 7); }
-__device__ inline int swz4(int row, int c) { return c ^ ((row >> 2) & 3); }
 
 // Swizzle of a row of D bf16 values (256 bytes at D = 128, 128 at D = 64).
 template <int D>
