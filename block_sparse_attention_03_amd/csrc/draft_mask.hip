@@ -255,8 +255,10 @@ __device__ void select_row(const DraftArgs& a, const double* s, size_t row, int 
   if (lane == 0) a.sel_cnt[row] = sel_before;
 }
 
-template <int GX, int D>
-__global__ __launch_bounds__(kThreads) void draft_mask_kernel(DraftArgs a) {
+// NW waves per workgroup: one key of the group's union per thread, so a
+// union of up to 64 * NW keys is scored in one round of D loads per thread.
+template <int GX, int D, int NW>
+__global__ __launch_bounds__(64 * NW) void draft_mask_kernel(DraftArgs a) {
   extern __shared__ double smem[];
   double* qs = smem;                                    // [D][GX]
   double* sc = smem + D * GX;                           // [GX][row_stride]
@@ -299,7 +301,7 @@ __global__ __launch_bounds__(kThreads) void draft_mask_kernel(DraftArgs a) {
 
   const size_t bh = (size_t)b * a.NH + h;
   const int row0 = tq * nS + by * nbx + bx0;
-  for (int i = tid; i < D * GX; i += kThreads) {
+  for (int i = tid; i < D * GX; i += 64 * NW) {
     const int d = i / GX, g = i % GX;
     qs[i] = g < ng ? a.q_pool[(bh * nq + row0 + g) * D + d] : 0.0;
   }
@@ -307,7 +309,7 @@ __global__ __launch_bounds__(kThreads) void draft_mask_kernel(DraftArgs a) {
 
   // Phase A: score every key of the group's union window against each row.
   const SmallDiv div_nux(nux), div_ny(ny);
-  for (int u = tid; u < n_union; u += kThreads) {
+  for (int u = tid; u < n_union; u += 64 * NW) {
     const int r2 = div_nux(u), ux = u - r2 * nux;
     const int p = div_ny(r2), yy = r2 - p * ny;
     const int x = uxlo + ux, y = ylo + yy;
@@ -316,7 +318,7 @@ __global__ __launch_bounds__(kThreads) void draft_mask_kernel(DraftArgs a) {
     double acc[GX];
 #pragma unroll
     for (int g = 0; g < GX; ++g) acc[g] = 0.0;
-#pragma unroll 8
+#pragma unroll 16
     for (int d = 0; d < D; ++d) {
       const double kv = kp[(size_t)d * nS];
 #pragma unroll
@@ -334,7 +336,7 @@ __global__ __launch_bounds__(kThreads) void draft_mask_kernel(DraftArgs a) {
 
   // Phase B: one wave per row: softmax, exact top-k, sorted index list.
   uint32_t* hist = hist_all + wave * 256;
-  for (int g = wave; g < ng; g += kWaves) {
+  for (int g = wave; g < ng; g += NW) {
     int gxlo, gxhi;  // recomputed: a dynamic index into xlo[] would spill
     window_range(bx0 + g, nbx, a.local_range, a.border, &gxlo, &gxhi);
     select_row(a, sc + (size_t)g * a.row_stride, bh * nq + row0 + g, nvis, ylo, ny, gxlo, gxhi,
@@ -499,31 +501,42 @@ hipError_t launch_tile(const DraftArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int GX, int D>
+template <int GX, int D, int NW>
 hipError_t launch(const DraftArgs& a, hipStream_t s) {
   const int ngx = (a.nbx + GX - 1) / GX;
   const long long tasks = (long long)a.B * a.NH * a.ntb_q * a.nby * ngx;
   const long long groups = 8 * ((tasks + 7) / 8);
   const size_t shmem =
-      (size_t)D * GX * sizeof(double) + (size_t)GX * a.row_stride * sizeof(double) + kWaves * 256 * 4;
+      (size_t)D * GX * sizeof(double) + (size_t)GX * a.row_stride * sizeof(double) + NW * 256 * 4;
   if (shmem > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute((const void*)draft_mask_kernel<GX, D>,
+    hipError_t e = hipFuncSetAttribute((const void*)draft_mask_kernel<GX, D, NW>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((draft_mask_kernel<GX, D>), dim3((unsigned)groups), dim3(kThreads), shmem, s,
+  hipLaunchKernelGGL((draft_mask_kernel<GX, D, NW>), dim3((unsigned)groups), dim3(64 * NW), shmem, s,
                      a);
   return hipGetLastError();
 }
 
+template <int D, int NW>
+hipError_t launch_gx(const DraftArgs& a, hipStream_t s) {
+  switch (a.gx) {
+    case 8: return launch<8, D, NW>(a, s);
+    case 4: return launch<4, D, NW>(a, s);
+    case 2: return launch<2, D, NW>(a, s);
+    default: return launch<1, D, NW>(a, s);
+  }
+}
+
+// Eight waves where the group's union window has 257..512 keys (one key per
+// thread, one round of loads instead of a second round for a few threads);
+// four otherwise.
 template <int D>
 hipError_t launch_d(const DraftArgs& a, hipStream_t s) {
-  switch (a.gx) {
-    case 8: return launch<8, D>(a, s);
-    case 4: return launch<4, D>(a, s);
-    case 2: return launch<2, D>(a, s);
-    default: return launch<1, D>(a, s);
-  }
+  const long long uy = a.local_range < a.nby ? a.local_range : a.nby;
+  const long long ux = a.local_range + a.gx - 1 < a.nbx ? a.local_range + a.gx - 1 : a.nbx;
+  const long long union_max = (long long)a.view.n * uy * ux;
+  return union_max > 256 && union_max <= 512 ? launch_gx<D, 8>(a, s) : launch_gx<D, 4>(a, s);
 }
 
 }  // namespace
