@@ -28,8 +28,6 @@
 namespace lcsa {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
 
 // XCD-contiguous task order: workgroups are dealt to the 8 XCDs in turn, so
 // XCD x takes tasks [x*per, (x+1)*per) and neighbouring query tiles, whose
