@@ -28,7 +28,6 @@
 namespace lcsa {
 namespace {
 
-
 // XCD-contiguous task order: workgroups are dealt to the 8 XCDs in turn, so
 // XCD x takes tasks [x*per, (x+1)*per) and neighbouring query tiles, whose
 // windows share pooled keys, hit the same L2. Launch 8*per workgroups;
