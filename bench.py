@@ -1,7 +1,10 @@
 """LCSA benchmark: one streaming step = partition+pool -> draft mask ->
-block-sparse attention -> cache evict, through the C-ABI, on one GPU, on one
-stream (--overlap-v moves the transposed-v part of the partition to a second
-stream; measured slower).
+block-sparse attention -> cache evict, through the C-ABI, on one GPU, one
+kernel after the other on one stream. --pipeline runs the partition and lists
+of step n + 1 on a second stream under the attention of step n (a ring with
+one more slot keeps step n's keys intact; lcsa.StepPipeline); --overlap-v
+moves only the transposed-v part of the partition to a second stream. Both
+measured no faster: the overlapped kernels share the chip with the attention.
 
 Default workload: the steady-state streaming step at 768x1408 (2 new latent
 frames of 48x88 tokens, 12 heads, head_dim 128, bf16, a 6-frame KV cache,
@@ -45,6 +48,10 @@ def parse():
                     help="run the transposed-v part of the partition on a second stream, under "
                          "the q/k part and the lists (measured slower: the cross-stream "
                          "fork and join cost more than the overlap saves)")
+    ap.add_argument("--pipeline", action="store_true",
+                    help="streaming workloads: the partition and lists of step n + 1 on a second "
+                         "stream under the attention of step n (measured: 768x1408 -2.5 %%, "
+                         "larger grids +1 %%: the attention slows by about what is overlapped)")
     ap.add_argument("--q-blocks", action="store_true",
                     help="have the partition write the query blocks (q_blk) and the attention "
                          "read q from them, instead of reading q in token layout (measured "
@@ -120,6 +127,14 @@ def main():
     stream = torch.cuda.current_stream()
     # --overlap-v: a second stream (default priority) for the transposed-v part
     side = torch.cuda.Stream() if args.overlap_v else None
+    # --pipeline: the partition and lists of step n + 1 on a second stream
+    # (default priority) under the attention of step n, with one more ring
+    # slot (lcsa.StepPipeline); streaming layers only (chunk workloads - cold
+    # starts, the training shape, Stage-1 segments - run sequentially).
+    pipelined = (args.pipeline and not args.q_blocks and not args.overlap_v
+                 and all(sp.cache_frames and not sp.backward and not sp.frame_seg
+                         for sp in specs))
+    side_p = torch.cuda.Stream() if pipelined else None
     tb_first = t_first // 2
 
     import ctypes
@@ -132,7 +147,7 @@ def main():
             self.sp = sp
             self.seg = list(sp.frame_seg) if sp.frame_seg else None
             self.cache = L.KVCache(w.batch, w.heads, w.head_dim, w.height, w.width, tdt,
-                                   sp.n_slots, device=dev)
+                                   sp.n_slots + (1 if pipelined else 0), device=dev)
             self.params = L.make_params(local_range=sp.local_range, border=sp.border,
                                         topk_fixed=sp.topk_fixed, ratio=sp.ratio,
                                         scale_by_resolution=sp.scale_by_resolution,
@@ -157,6 +172,9 @@ def main():
                 self.kmax = L.lcsa_max_topk(geom, tb_first, probe, self.params)
             self.bufs = L.StepBuffers(geom, self.kmax, device=dev, with_lse=sp.backward,
                                       with_q_blk=args.q_blocks)
+            self.pipe = (L.StepPipeline(geom, self.cache, self.params, self.kmax, stream, side_p,
+                                        local=sp.lists == "local", device=dev)
+                         if pipelined else None)
             self.fork_join = (torch.cuda.Event(), torch.cuda.Event())
             self.keep = sp.cap_tb if sp.cache_frames else 0  # cold chunks: empty after each step
             if sp.backward:  # training shape: the keys are the chunk's own blocks
@@ -169,6 +187,10 @@ def main():
                 self.grads = [torch.empty_like(self.dout) for _ in range(3)]
 
         def run(self, tb, q, k, v, ev=None, evb=None):
+            if self.pipe is not None:
+                self.pipe.prep(q, k, v, tb)
+                self.bufs = self.pipe.attend(self.keep, ev)
+                return
             c, b = self.cache, self.bufs
             slot = c.append(w.frames // 2, tb)
             join = None
@@ -224,6 +246,7 @@ def main():
             return pairs * (fp + (backward_flops_per_pair(w.head_dim) if self.sp.backward else 0))
 
     layers = [Layer(sp) for sp in specs]
+    torch.cuda.synchronize()  # the primed rings are complete before any side-stream work
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in layers] for _ in range(n_steps)]
 
@@ -249,6 +272,8 @@ def main():
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
+    if side_p is not None:  # no step's work starts before the clock does
+        side_p.wait_event(start)
     for n in range(W, W + K):
         step(n, timed=True)
     end.record(stream)
@@ -290,7 +315,8 @@ def main():
                    **({"frame_segments": seg} if seg else {}),
                    **({"layers": list(w.layers)} if w.layers else {}),
                    "kmax": kmax, "q_read_from": "q_blk" if args.q_blocks else "token layout",
-                   "streams": 2 if args.overlap_v else 1, "parallelism": "single GPU"},
+                   "streams": 2 if (args.overlap_v or pipelined) else 1,
+                   "pipelined_steps": pipelined, "parallelism": "single GPU"},
         "attn_ms": round(attn_avg, 4),
         **({"bwd_ms": round(float(np.mean(bwd_ms)), 4)} if has_bwd else {}),
         "attn_ms_median": round(float(np.median(attn_ms)), 4),

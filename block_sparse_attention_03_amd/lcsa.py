@@ -451,6 +451,67 @@ def run_step(geom: Geom, q, k, v, cache: KVCache, first_abs_tb: int, params: Sel
     return bufs
 
 
+class StepPipeline:
+    """Consecutive streaming steps of one layer with the partition and the
+    lists of step n + 1 on a side stream, running under the attention of
+    step n on the main stream. Call prep(n) then attend(n) for n = 0, 1, ...
+    in that order (the attention takes the ring's view as it is after prep).
+
+    The ring must have one slot more than a step's view (cache + chunk TBs
+    + 1): step n + 1's new blocks then overwrite the blocks of step n - 1's
+    oldest TB, which step n's attention no longer reads, so prep(n + 1)
+    waits only for attention(n - 1). Lists, pooled queries and outputs are
+    double-buffered by step parity for the same reason. attend(n) waits for
+    prep(n)'s lists. Results equal those of run_step, step by step.
+    """
+
+    def __init__(self, geom: Geom, cache: KVCache, params: SelectParams, kmax: int,
+                 main, side, local: bool = False, with_lse: bool = False, device="cuda"):
+        import torch
+        self.geom, self.cache, self.params, self.local = geom, cache, params, local
+        self.main, self.side = main, side
+        self.bufs = [StepBuffers(geom, kmax, device=device, with_lse=with_lse) for _ in range(2)]
+        self.lists_ready = [torch.cuda.Event() for _ in range(2)]  # by step parity
+        self.attn_done = [torch.cuda.Event() for _ in range(3)]    # by step mod 3
+        self.n = 0
+        self.pending = None
+
+    def prep(self, q, k, v, first_abs_tb: int):
+        n, g, c = self.n, self.geom, self.cache
+        if n >= 2:  # the slot and the buffers this step reuses were read by attention(n - 2)
+            self.side.wait_event(self.attn_done[(n - 2) % 3])
+        slot = c.append(g.frames // 2, first_abs_tb)
+        b = self.bufs[n % 2]
+        lcsa_partition_pool(g, q, k, v, None, b.q_pool, c.c, slot, self.side)
+        if self.local:
+            lcsa_local_lists(g, first_abs_tb, c.c, self.params, b.kmax, b.sel_idx, b.sel_cnt,
+                             self.side)
+        else:
+            lcsa_draft_mask(g, b.q_pool, first_abs_tb, c.c, self.params, b.kmax, b.sel_idx,
+                            b.sel_cnt, None, self.side)
+        self.lists_ready[n % 2].record(self.side)
+        self.pending = (n, q)
+        self.n += 1
+
+    def attend(self, keep_tb: int, events=None):
+        """The attention of the step prep() last queued; events: an optional
+        (start, end) pair of timing events recorded around it on the main
+        stream. Returns that step's StepBuffers."""
+        n, q = self.pending
+        b = self.bufs[n % 2]
+        self.main.wait_event(self.lists_ready[n % 2])
+        if events is not None:
+            events[0].record(self.main)
+        lcsa_block_sparse_attn_tok(self.geom, q, self.cache.c, b.sel_idx, b.sel_cnt, b.kmax,
+                                   b.out, b.lse, 0.0, self.main)
+        if events is not None:
+            events[1].record(self.main)
+        self.attn_done[n % 3].record(self.main)
+        self.cache.evict(keep_tb)
+        self.pending = None
+        return b
+
+
 def run_segment_step(geom: Geom, q, k, v, cache: KVCache, first_abs_tb: int, frame_seg,
                      bufs: StepBuffers | None = None, stream=None, want_lse=False,
                      scale: float = 0.0, q_blocks: bool = False):
