@@ -383,8 +383,9 @@ def cpu_baseline(w, sample_heads, sample_steps, flops_pair):
 
 ATTN_KERNEL = "attn_bf16"
 # The files whose text makes up the attention kernel. traffic.json keeps a
-# digest of them from when its counters were summarized; a run on other
-# sources reports traffic as null instead of figures taken on older code.
+# digest of them and of the kernel's compile flags from when its counters
+# were summarized; a run on other sources or flags reports traffic as null
+# instead of figures taken on older code.
 ATTN_SOURCES = ("block_sparse_attention_03_amd/csrc/sparse_attn.hip",
                 "block_sparse_attention_03_amd/csrc/mfma_tiles.h",
                 "block_sparse_attention_03_amd/csrc/lcsa_kernels.h")
@@ -396,6 +397,9 @@ def attn_source_digest() -> str:
     for rel in ATTN_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
+    # the compile flags shape the machine code as much as the sources do
+    from block_sparse_attention_03_amd import build_lib
+    h.update(" ".join(build_lib.HIP_FLAGS + build_lib.EXTRA.get("sparse_attn.hip", [])).encode())
     return h.hexdigest()[:16]
 
 

@@ -37,10 +37,13 @@ def _run(cmd):
     return err
 
 
-# per-source extras: the attention kernel's max reductions need no NaN
-# propagation (a NaN input yields NaN output either way), which lets the
-# compiler use v_max3 without canonicalising every operand
-EXTRA = {"sparse_attn.hip": ["-fno-honor-nans"]}
+# per-source extras for the attention kernel:
+# - its max reductions need no NaN propagation (a NaN input yields NaN output
+#   either way), which lets the compiler use v_max3 without canonicalising
+#   every operand;
+# - the scheduler that favours instruction-level parallelism over register
+#   pressure orders its main loop about 1 % faster at the same 225 registers
+EXTRA = {"sparse_attn.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 
 
 def build(verbose: bool = False) -> str:
