@@ -415,3 +415,133 @@ def test_planted_transposed_scores_are_caught(monkeypatch):
     diff = sum(list(res.sel[0][h][i]) != bf_sel[(h, i)]
                for h in range(2) for i in range(len(res.sel[0][h])))
     assert diff > 0
+
+
+# ---------------------------------------------------------------- cache priming and row subsets
+
+def _primed_stream(prime, H=16, W=24, NH=2, D=32, seed=13, p=None, n_steps=2):
+    """Prime a cap-3 cache with frames 0-5 through ``prime`` (k/v only), then
+    step frames 6-7, 8-9, ...: per step the oracle's result and the key
+    frames the step attends ([HW] 2.3: the cache keeps the newest temporal
+    blocks and drops the oldest)."""
+    p = p or O.SelectParams(local_range=3, ratio_num=1, ratio_den=4)
+    cache = O.KVCache(cap_tb=3)
+    d0 = synth.make_qkv(seed, NH, D, H, W, 0, 6, dtype="bf16", which="kv")
+    prime(cache, d0["k"][1], d0["v"][1], 0)
+    out = []
+    for n in range(n_steps):
+        t0 = 6 + 2 * n
+        d = synth.make_qkv(seed, NH, D, H, W, t0, t0 + 2, dtype="bf16")
+        res = O.lcsa_step(d["q"][1], d["k"][1], d["v"][1], cache, t0 // 2, p)
+        out.append((t0, d["q"][1], res, list(cache.tbs())))
+    return out, p
+
+
+def _check_against_bruteforce(steps, p, H=16, W=24, NH=2, D=32, seed=13):
+    for t0, q, res, tbs_after in steps:
+        kt0 = t0 - 6  # the view: the 3 cached TBs and the new one
+        dk = synth.make_qkv(seed, NH, D, H, W, kt0, t0 + 2, dtype="bf16", which="kv")
+        bf_out, bf_sel, _ = lcsa_bruteforce(q[0], dk["k"][1][0], dk["v"][1][0], t0, kt0,
+                                            p.local_range, p.border,
+                                            lambda na, nk: O.topk_count(na, nk, p))
+        for h in range(NH):
+            for i in range(len(res.sel[0][h])):
+                assert list(res.sel[0][h][i]) == bf_sel[(h, i)], (t0, h, i)
+        assert np.abs(res.out[0] - bf_out).max() < 1e-12
+        assert res.key_tbs == list(range(kt0 // 2, t0 // 2 + 1))
+        assert tbs_after == list(range(kt0 // 2 + 1, t0 // 2 + 1))
+
+
+def test_prime_cache_then_steps_match_bruteforce():
+    """prime_cache over frames 0-5 followed by streaming steps equals the
+    token-space brute force over the explicitly concatenated key frames."""
+    steps, p = _primed_stream(O.prime_cache)
+    _check_against_bruteforce(steps, p)
+
+
+def test_prime_cache_entries_are_the_token_windows():
+    """Each primed entry is its temporal block: label first_abs_tb + t, and
+    block (by, bx) holds tokens (2t + dt, 8by + dy, 8bx + dx) at position
+    (dt*8 + dy)*8 + dx, gathered here straight from token coordinates."""
+    H, W, NH, D = 16, 24, 2, 8
+    d = synth.make_qkv(4, NH, D, H, W, 0, 6, dtype="f32", which="kv")
+    k, v = d["k"][1], d["v"][1]
+    cache = O.KVCache(cap_tb=8)
+    O.prime_cache(cache, k, v, 5)
+    assert cache.tbs() == [5, 6, 7]
+    nbx = W // 8
+    for t, (tb, kb, vb, kp) in enumerate(cache.entries):
+        for s in range(kb.shape[2]):
+            by, bx = divmod(s, nbx)
+            for tau in range(128):
+                dt, dy, dx = tau // 64, (tau // 8) % 8, tau % 8
+                tok = (0, 2 * t + dt, 8 * by + dy, 8 * bx + dx)
+                assert np.array_equal(kb[0, :, s, tau], k[tok])
+                assert np.array_equal(vb[0, :, s, tau], v[tok])
+            assert np.allclose(kp[0, :, s], kb[0, :, s].mean(axis=1), rtol=0, atol=1e-15)
+
+
+def test_planted_prime_cache_mistakes_are_caught(monkeypatch):
+    """Positive controls: a primed cache whose temporal-block labels are
+    shifted (the newest primed block then counts as later than the query)
+    or whose blocks are appended in the wrong order disagrees with the
+    brute force."""
+    def shifted(cache, k, v, first_abs_tb):
+        O.prime_cache(cache, k, v, first_abs_tb + 2)
+
+    def reversed_order(cache, k, v, first_abs_tb):
+        tmp = O.KVCache(cap_tb=8)
+        O.prime_cache(tmp, k, v, first_abs_tb)
+        for e in reversed(tmp.entries):
+            cache.append(*e)
+
+    for bad in (shifted, reversed_order):
+        steps, p = _primed_stream(bad, n_steps=1)
+        with pytest.raises(AssertionError):
+            _check_against_bruteforce(steps, p)
+
+
+def test_lcsa_step_rows_subset_equals_full_run_on_those_rows():
+    """rows=R computes exactly the full run's values on the rows in R
+    (bitwise: the same per-row arithmetic) and leaves every other row at
+    out = 0, lse = -inf; the selections do not depend on R."""
+    H, W, NH, D = 16, 24, 2, 32
+    p = O.SelectParams(local_range=3, ratio_num=1, ratio_den=3)
+    d = synth.make_qkv(21, NH, D, H, W, 0, 4, dtype="bf16")
+    q, k, v = (d[n][1] for n in "qkv")
+    full = O.lcsa_step(q, k, v, O.KVCache(cap_tb=3), 0, p)
+    rows = [(0, 0, 0), (0, 1, 5), (0, 1, 11)]
+    part = O.lcsa_step(q, k, v, O.KVCache(cap_tb=3), 0, p, rows=rows)
+    ob_full = O.partition(full.out)
+    ob_part = O.partition(part.out)
+    nq = ob_full.shape[2]
+    for h in range(NH):
+        assert [list(r) for r in part.sel[0][h]] == [list(r) for r in full.sel[0][h]]
+        for i in range(nq):
+            if (0, h, i) in rows:
+                assert np.array_equal(ob_part[0, h, i], ob_full[0, h, i])
+                assert np.array_equal(part.lse[0, h, i], full.lse[0, h, i])
+                assert np.abs(ob_full[0, h, i]).max() > 0
+            else:
+                assert not ob_part[0, h, i].any()
+                assert np.all(np.isneginf(part.lse[0, h, i]))
+
+
+def test_planted_rows_subset_mistake_is_caught(monkeypatch):
+    """Positive control: a row-subset branch that computes the wrong row
+    (an off-by-one block index) fails the subset pin's comparison."""
+    real = O.sparse_attention_row
+    calls = {}
+
+    def wrong_row(qb, kb, vb, sel_row, scale):
+        calls["n"] = calls.get("n", 0) + 1
+        return real(qb[::-1].copy(), kb, vb, sel_row, scale)  # rows of the block reversed
+    H, W, NH, D = 16, 16, 1, 16
+    p = O.SelectParams(local_range=3, topk_fixed=2)
+    d = synth.make_qkv(2, NH, D, H, W, 0, 2, dtype="f32")
+    q, k, v = (d[n][1] for n in "qkv")
+    full = O.lcsa_step(q, k, v, O.KVCache(cap_tb=3), 0, p)
+    monkeypatch.setattr(O, "sparse_attention_row", wrong_row)
+    part = O.lcsa_step(q, k, v, O.KVCache(cap_tb=3), 0, p, rows=[(0, 0, 1)])
+    assert calls["n"] == 1
+    assert not np.array_equal(O.partition(part.out)[0, 0, 1], O.partition(full.out)[0, 0, 1])
