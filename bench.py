@@ -1,10 +1,6 @@
 """LCSA benchmark: one streaming step = partition+pool -> draft mask ->
 block-sparse attention -> cache evict, through the C-ABI, on one GPU, one
-kernel after the other on one stream. --pipeline runs the partition and lists
-of step n + 1 on a second stream under the attention of step n (a ring with
-one more slot keeps step n's keys intact; lcsa.StepPipeline); --overlap-v
-moves only the transposed-v part of the partition to a second stream. Both
-measured no faster: the overlapped kernels share the chip with the attention.
+kernel after the other on one stream.
 
 Default workload: the steady-state streaming step at 768x1408 (2 new latent
 frames of 48x88 tokens, 12 heads, head_dim 128, bf16, a 6-frame KV cache,
@@ -44,14 +40,6 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="step_768x1408")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--overlap-v", action="store_true",
-                    help="run the transposed-v part of the partition on a second stream, under "
-                         "the q/k part and the lists (measured slower: the cross-stream "
-                         "fork and join cost more than the overlap saves)")
-    ap.add_argument("--pipeline", action="store_true",
-                    help="streaming workloads: the partition and lists of step n + 1 on a second "
-                         "stream under the attention of step n (measured: 768x1408 -2.5 %%, "
-                         "larger grids +1 %%: the attention slows by about what is overlapped)")
     ap.add_argument("--q-blocks", action="store_true",
                     help="have the partition write the query blocks (q_blk) and the attention "
                          "read q from them, instead of reading q in token layout (measured "
@@ -125,16 +113,6 @@ def main():
     torch.cuda.synchronize()
     geom = L.make_geom(w.batch, w.heads, w.head_dim, w.frames, w.height, w.width, code)
     stream = torch.cuda.current_stream()
-    # --overlap-v: a second stream (default priority) for the transposed-v part
-    side = torch.cuda.Stream() if args.overlap_v else None
-    # --pipeline: the partition and lists of step n + 1 on a second stream
-    # (default priority) under the attention of step n, with one more ring
-    # slot (lcsa.StepPipeline); streaming layers only (chunk workloads - cold
-    # starts, the training shape, Stage-1 segments - run sequentially).
-    pipelined = (args.pipeline and not args.q_blocks and not args.overlap_v
-                 and all(sp.cache_frames and not sp.backward and not sp.frame_seg
-                         for sp in specs))
-    side_p = torch.cuda.Stream() if pipelined else None
     tb_first = t_first // 2
 
     import ctypes
@@ -147,7 +125,7 @@ def main():
             self.sp = sp
             self.seg = list(sp.frame_seg) if sp.frame_seg else None
             self.cache = L.KVCache(w.batch, w.heads, w.head_dim, w.height, w.width, tdt,
-                                   sp.n_slots + (1 if pipelined else 0), device=dev)
+                                   sp.n_slots, device=dev)
             self.params = L.make_params(local_range=sp.local_range, border=sp.border,
                                         topk_fixed=sp.topk_fixed, ratio=sp.ratio,
                                         scale_by_resolution=sp.scale_by_resolution,
@@ -172,10 +150,6 @@ def main():
                 self.kmax = L.lcsa_max_topk(geom, tb_first, probe, self.params)
             self.bufs = L.StepBuffers(geom, self.kmax, device=dev, with_lse=sp.backward,
                                       with_q_blk=args.q_blocks)
-            self.pipe = (L.StepPipeline(geom, self.cache, self.params, self.kmax, stream, side_p,
-                                        local=sp.lists == "local", device=dev)
-                         if pipelined else None)
-            self.fork_join = (torch.cuda.Event(), torch.cuda.Event())
             self.keep = sp.cap_tb if sp.cache_frames else 0  # cold chunks: empty after each step
             if sp.backward:  # training shape: the keys are the chunk's own blocks
                 assert sp.cache_frames == 0 and not self.seg
@@ -187,19 +161,9 @@ def main():
                 self.grads = [torch.empty_like(self.dout) for _ in range(3)]
 
         def run(self, tb, q, k, v, ev=None, evb=None):
-            if self.pipe is not None:
-                self.pipe.prep(q, k, v, tb)
-                self.bufs = self.pipe.attend(self.keep, ev)
-                return
             c, b = self.cache, self.bufs
             slot = c.append(w.frames // 2, tb)
-            join = None
-            if side is not None:  # the transposed v tiles under the q/k part and the lists
-                join = L.fork_v_part(geom, v, c.c, slot, stream, side, self.fork_join)
-                L.lcsa_partition_pool_parts(geom, q, k, None, b.q_blk, b.q_pool, c.c, slot,
-                                            L.PART_QK, stream)
-            else:
-                L.lcsa_partition_pool(geom, q, k, v, b.q_blk, b.q_pool, c.c, slot, stream)
+            L.lcsa_partition_pool(geom, q, k, v, b.q_blk, b.q_pool, c.c, slot, stream)
             if self.seg:
                 L.lcsa_segment_lists(geom, tb, c.c, self.seg, self.kmax, b.sel_idx, b.sel_cnt,
                                      stream)
@@ -209,8 +173,6 @@ def main():
             else:
                 L.lcsa_draft_mask(geom, b.q_pool, tb, c.c, self.params, self.kmax, b.sel_idx,
                                   b.sel_cnt, None, stream)
-            if join is not None:
-                stream.wait_event(join)
             if ev is not None:
                 ev[0].record(stream)
             if self.seg and b.q_blk is not None:
@@ -246,7 +208,7 @@ def main():
             return pairs * (fp + (backward_flops_per_pair(w.head_dim) if self.sp.backward else 0))
 
     layers = [Layer(sp) for sp in specs]
-    torch.cuda.synchronize()  # the primed rings are complete before any side-stream work
+    torch.cuda.synchronize()
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in layers] for _ in range(n_steps)]
 
@@ -272,8 +234,6 @@ def main():
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
-    if side_p is not None:  # no step's work starts before the clock does
-        side_p.wait_event(start)
     for n in range(W, W + K):
         step(n, timed=True)
     end.record(stream)
@@ -315,8 +275,7 @@ def main():
                    **({"frame_segments": seg} if seg else {}),
                    **({"layers": list(w.layers)} if w.layers else {}),
                    "kmax": kmax, "q_read_from": "q_blk" if args.q_blocks else "token layout",
-                   "streams": 2 if (args.overlap_v or pipelined) else 1,
-                   "pipelined_steps": pipelined, "parallelism": "single GPU"},
+                   "streams": 1, "parallelism": "single GPU"},
         "attn_ms": round(attn_avg, 4),
         **({"bwd_ms": round(float(np.mean(bwd_ms)), 4)} if has_bwd else {}),
         "attn_ms_median": round(float(np.median(attn_ms)), 4),

@@ -132,24 +132,18 @@ BwdLayout bwd_layout(const lcsa_geom& g) {
 
 extern "C" {
 
-// lcsa_partition_pool and lcsa_partition_pool_parts: `parts` selects the
-// q/k tiles with their means and / or the transposed v tiles.
-static lcsa_status partition_parts(const lcsa_geom* g, const void* q, const void* k,
-                                   const void* v, void* q_blk, double* q_pool,
-                                   lcsa_kv_cache* cache, int32_t first_slot, int32_t parts,
-                                   void* stream, const char* fn) {
+lcsa_status lcsa_partition_pool(const lcsa_geom* g, const void* q, const void* k, const void* v,
+                                void* q_blk, double* q_pool, lcsa_kv_cache* cache,
+                                int32_t first_slot, void* stream) {
+  const char* fn = "lcsa_partition_pool";
   lcsa_status st;
   if ((st = check_geom(g, fn)) || (st = check_cache(cache)) ||
       (st = check_matches_cache(g, cache)))
     return st;
-  if (parts < 1 || parts > (LCSA_PART_QK | LCSA_PART_V))
-    return fail(LCSA_ERR_PARAM, "%s: parts %d is not LCSA_PART_QK, LCSA_PART_V or both", fn,
-                parts);
-  const bool do_qk = parts & LCSA_PART_QK, do_v = parts & LCSA_PART_V;
-  const bool has_q = do_qk && (q || q_blk || q_pool);
+  const bool has_q = q || q_blk || q_pool;
   if (has_q && !(q && q_pool))
     return fail(LCSA_ERR_NULL, "q and q_pool must be both NULL or both non-NULL (q_blk needs q)");
-  if ((do_qk && (st = check_ptr(k, "k"))) || (do_v && (st = check_ptr(v, "v"))) ||
+  if ((st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
       (has_q && ((st = check_ptr(q, "q")) || (st = check_ptr(q_blk, "q_blk", true)) ||
                  (st = check_ptr(q_pool, "q_pool")))))
     return st;
@@ -157,18 +151,21 @@ static lcsa_status partition_parts(const lcsa_geom* g, const void* q, const void
   if (ntb == 0) return ok();
   if (first_slot < 0 || first_slot >= cache->n_slots)
     return fail(LCSA_ERR_PARAM, "first_slot %d outside [0, %d)", first_slot, cache->n_slots);
-  for (int32_t t = 0; t < ntb; ++t) {
-    const int32_t slot = (first_slot + t) % cache->n_slots;
-    const int32_t pos = (slot - cache->head + cache->n_slots) % cache->n_slots;
-    if (pos >= cache->count)
-      return fail(LCSA_ERR_CAPACITY,
-                  "slot %d (TB %d of the chunk) is not held by the cache; append first", slot, t);
-  }
+  if (ntb > cache->count)
+    return fail(LCSA_ERR_CAPACITY, "%s: a chunk of %d TBs but the cache holds %d; append first",
+                fn, ntb, cache->count);
+  // the chunk's TBs are the newest ones held, in order: the slots the last
+  // append returned (any other first_slot would overwrite older cached TBs)
+  const int32_t pos = (first_slot - cache->head + cache->n_slots) % cache->n_slots;
+  if (pos + ntb != cache->count)
+    return fail(LCSA_ERR_PARAM,
+                "%s: first_slot %d is view position %d of %d held TBs; the chunk's %d TBs must "
+                "be the newest (position %d)", fn, first_slot, pos, cache->count, ntb,
+                cache->count - ntb);
   PartitionArgs a{};
   a.q = has_q ? q : nullptr;
-  a.k = do_qk ? k : nullptr;
-  a.v = do_v ? v : nullptr;
-  a.parts = parts;
+  a.k = k;
+  a.v = v;
   a.q_blk = has_q ? q_blk : nullptr;
   a.q_pool = q_pool;
   a.k_ring = cache->k_ring;
@@ -186,25 +183,10 @@ static lcsa_status partition_parts(const lcsa_geom* g, const void* q, const void
   return device_status(launch_partition_pool(a, (hipStream_t)stream), fn);
 }
 
-lcsa_status lcsa_partition_pool(const lcsa_geom* g, const void* q, const void* k, const void* v,
-                                void* q_blk, double* q_pool, lcsa_kv_cache* cache,
-                                int32_t first_slot, void* stream) {
-  return partition_parts(g, q, k, v, q_blk, q_pool, cache, first_slot,
-                         LCSA_PART_QK | LCSA_PART_V, stream, "lcsa_partition_pool");
-}
-
-lcsa_status lcsa_partition_pool_parts(const lcsa_geom* g, const void* q, const void* k,
-                                      const void* v, void* q_blk, double* q_pool,
-                                      lcsa_kv_cache* cache, int32_t first_slot, int32_t parts,
-                                      void* stream) {
-  return partition_parts(g, q, k, v, q_blk, q_pool, cache, first_slot, parts, stream,
-                         "lcsa_partition_pool_parts");
-}
-
 lcsa_status lcsa_draft_mask(const lcsa_geom* gq, const double* q_pool, int64_t q_first_abs_tb,
                             const lcsa_kv_cache* cache, const lcsa_select_params* params,
                             int32_t kmax, int32_t* sel_idx, int32_t* sel_cnt, double* probs,
-                            void* stream) {
+                            size_t probs_bytes, void* stream) {
   lcsa_status st;
   if ((st = check_geom(gq, "lcsa_draft_mask")) || (st = check_params(params)) ||
       (st = check_cache(cache)) || (st = check_matches_cache(gq, cache)) ||
@@ -221,6 +203,14 @@ lcsa_status lcsa_draft_mask(const lcsa_geom* gq, const double* q_pool, int64_t q
   if (amax > LCSA_MAX_CANDIDATES)
     return fail(LCSA_ERR_CAPACITY, "a row has %lld candidates; at most %d are supported",
                 (long long)amax, LCSA_MAX_CANDIDATES);
+  if (probs) {
+    const uint64_t nq = (uint64_t)ntb * (gq->height / 8) * (gq->width / 8);
+    const uint64_t n_keys = (uint64_t)cache->count * (gq->height / 8) * (gq->width / 8);
+    const uint64_t need = (uint64_t)gq->batch * gq->heads * nq * n_keys * sizeof(double);
+    if ((uint64_t)probs_bytes < need)
+      return fail(LCSA_ERR_CAPACITY, "probs of %zu bytes; %llu needed for %llu keys", probs_bytes,
+                  (unsigned long long)need, (unsigned long long)n_keys);
+  }
 
   DraftArgs a{};
   a.q_pool = q_pool;

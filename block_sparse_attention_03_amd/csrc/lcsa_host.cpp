@@ -156,7 +156,8 @@ extern "C" {
 lcsa_status lcsa_kv_cache_init(lcsa_kv_cache* cache, int32_t batch, int32_t heads,
                                int32_t head_dim, int32_t nby, int32_t nbx, int32_t dtype,
                                int32_t n_slots, void* k_ring, void* v_ring,
-                               double* kpool_ring) {
+                               double* kpool_ring, size_t bytes_k, size_t bytes_v,
+                               size_t bytes_kpool) {
   if (!cache) return fail(LCSA_ERR_NULL, "cache is NULL");
   lcsa_geom g{batch, heads, head_dim, 0, nby * 8, nbx * 8, dtype};
   if (nby < 1 || nbx < 1) return fail(LCSA_ERR_SHAPE, "cache grid %dx%d blocks", nby, nbx);
@@ -167,6 +168,19 @@ lcsa_status lcsa_kv_cache_init(lcsa_kv_cache* cache, int32_t batch, int32_t head
   if ((st = check_ptr(k_ring, "k_ring")) || (st = check_ptr(v_ring, "v_ring")) ||
       (st = check_ptr(kpool_ring, "kpool_ring")))
     return st;
+  // every block of every slot the kernels may touch must lie inside the
+  // caller's buffers (sizes of at most 2^40 elements, so no overflow)
+  const uint64_t blocks = (uint64_t)batch * heads * n_slots * nby * nbx;
+  const uint64_t esize = dtype == LCSA_BF16 ? 2 : 4;
+  const uint64_t need_kv = blocks * 128 * head_dim * esize;
+  const uint64_t need_pool = blocks * head_dim * sizeof(double);
+  if ((uint64_t)bytes_k < need_kv || (uint64_t)bytes_v < need_kv ||
+      (uint64_t)bytes_kpool < need_pool)
+    return fail(LCSA_ERR_CAPACITY,
+                "ring buffers too small for %d slots: k %zu, v %zu, kpool %zu bytes given; "
+                "%llu, %llu, %llu needed",
+                n_slots, bytes_k, bytes_v, bytes_kpool, (unsigned long long)need_kv,
+                (unsigned long long)need_kv, (unsigned long long)need_pool);
   std::memset(cache, 0, sizeof(*cache));
   cache->batch = batch;
   cache->heads = heads;
@@ -270,6 +284,6 @@ lcsa_status lcsa_max_candidates(const lcsa_geom* gq, int64_t q_first_abs_tb,
   return ok();
 }
 
-int32_t lcsa_abi_version(void) { return 4; }
+int32_t lcsa_abi_version(void) { return 5; }
 
 }  // extern "C"

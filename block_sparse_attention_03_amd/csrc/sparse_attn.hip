@@ -194,7 +194,10 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
   const float sl2 = a.scale * kLog2e;
-  float m = -INFINITY, lsum = 0.f;
+  float m = -INFINITY;
+  // row sums in four independent v_dot2 chains (one chain of sixteen waits
+  // on the instruction's accumulate latency at every step)
+  float ls[4] = {0.f, 0.f, 0.f, 0.f};
 
   // Lane-invariant LDS fragment offsets. K rows prow and prow + 32 share
   // the swizzle (it depends on row & 15), V^T rows 32dt + l32 share it for
@@ -249,7 +252,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     if (__ballot(mx > m + kLazy)) {  // lazy rescale: only when the max grows by > 2^8
       const float mnew = fmaxf(m, mx);
       const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-      lsum *= alpha;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ls[e] *= alpha;
 #pragma unroll
       for (int dt = 0; dt < NO; ++dt)
 #pragma unroll
@@ -267,7 +271,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
           const bf16x2 pr = {pf[kt][hh][e], pf[kt][hh][e + 1]};
-          lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones2(), lsum, false);
+          ls[e >> 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones2(), ls[e >> 1], false);
         }
       }
 #pragma unroll
@@ -329,6 +333,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   }
 
   // epilogue: normalise, stage the 128 x D tile in LDS, write whole rows
+  const float lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
   const float lt = lsum + partner32(lsum, g);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;  // 0 only if every listed id was skipped
   __syncthreads();

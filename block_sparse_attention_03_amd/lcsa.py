@@ -73,7 +73,8 @@ def load_library(path: str = LIB_PATH):
     G, P, C = POINTER(Geom), POINTER(SelectParams), POINTER(KvCacheStruct)
     sig = {
         "lcsa_kv_cache_init": [C, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
-                               c_void_p, c_void_p, c_void_p],
+                               c_void_p, c_void_p, c_void_p, ctypes.c_size_t, ctypes.c_size_t,
+                               ctypes.c_size_t],
         "lcsa_kv_cache_append": [C, c_int32, c_int64, POINTER(c_int32)],
         "lcsa_kv_cache_evict": [C, c_int32],
         "lcsa_kv_cache_view": [C, POINTER(c_int32), POINTER(c_int32), POINTER(c_int64)],
@@ -81,10 +82,8 @@ def load_library(path: str = LIB_PATH):
         "lcsa_max_topk": [G, c_int64, C, P, POINTER(c_int32)],
         "lcsa_partition_pool": [G, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, C,
                                 c_int32, c_void_p],
-        "lcsa_partition_pool_parts": [G, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, C,
-                                      c_int32, c_int32, c_void_p],
         "lcsa_draft_mask": [G, c_void_p, c_int64, C, P, c_int32, c_void_p, c_void_p, c_void_p,
-                            c_void_p],
+                            ctypes.c_size_t, c_void_p],
         "lcsa_block_sparse_attn": [G, c_void_p, C, c_void_p, c_void_p, c_int32, c_float,
                                    c_void_p, c_void_p, c_void_p],
         "lcsa_block_sparse_attn_tok": [G, c_void_p, C, c_void_p, c_void_p, c_int32, c_float,
@@ -156,11 +155,23 @@ def make_params(local_range=11, border=BORDER_PRESERVED, topk_fixed=0, ratio=(1,
 
 # ---------------------------------------------------------------- C names
 
+def _nbytes(t):
+    """Size in bytes of a tensor (0 for None or an object without one)."""
+    if t is None or not hasattr(t, "numel"):
+        return 0
+    return t.numel() * t.element_size()
+
+
 def lcsa_kv_cache_init(cache: KvCacheStruct, batch, heads, head_dim, nby, nbx, dtype, n_slots,
-                       k_ring, v_ring, kpool_ring):
+                       k_ring, v_ring, kpool_ring, bytes_k=None, bytes_v=None, bytes_kpool=None):
+    """The buffer sizes default to the tensors' own sizes."""
     lib = load_library()
+    bk = _nbytes(k_ring) if bytes_k is None else bytes_k
+    bv = _nbytes(v_ring) if bytes_v is None else bytes_v
+    bp = _nbytes(kpool_ring) if bytes_kpool is None else bytes_kpool
     _check(lib.lcsa_kv_cache_init(ctypes.byref(cache), batch, heads, head_dim, nby, nbx, dtype,
-                                  n_slots, _ptr(k_ring), _ptr(v_ring), _ptr(kpool_ring)))
+                                  n_slots, _ptr(k_ring), _ptr(v_ring), _ptr(kpool_ring), bk, bv,
+                                  bp))
 
 
 def lcsa_kv_cache_append(cache: KvCacheStruct, n_tb: int, first_abs_tb: int) -> int:
@@ -208,41 +219,15 @@ def lcsa_partition_pool(geom: Geom, q, k, v, q_blk, q_pool, cache: KvCacheStruct
                                    _stream(stream)))
 
 
-PART_QK, PART_V = 1, 2  # LCSA_PART_QK, LCSA_PART_V
-
-
-def lcsa_partition_pool_parts(geom: Geom, q, k, v, q_blk, q_pool, cache: KvCacheStruct,
-                              first_slot: int, parts: int, stream=None):
-    lib = load_library()
-    _check(lib.lcsa_partition_pool_parts(ctypes.byref(geom), _ptr(q), _ptr(k), _ptr(v),
-                                         _ptr(q_blk), _ptr(q_pool), ctypes.byref(cache),
-                                         first_slot, parts, _stream(stream)))
-
-
-def fork_v_part(geom: Geom, v, cache: KvCacheStruct, first_slot: int, stream, side_stream,
-                events=None):
-    """Start the transposed-v part of the partition on side_stream (a torch
-    stream) once the work already queued on `stream` is done: the ring slot
-    it fills may have been read by that work. Returns the event the attention
-    launch on `stream` must wait for. `events` may pass a reusable (fork,
-    join) pair of torch events."""
-    import torch
-    main = stream if stream is not None else torch.cuda.current_stream()
-    fork, join = events if events is not None else (torch.cuda.Event(), torch.cuda.Event())
-    fork.record(main)
-    side_stream.wait_event(fork)
-    lcsa_partition_pool_parts(geom, None, None, v, None, None, cache, first_slot, PART_V,
-                              side_stream)
-    join.record(side_stream)
-    return join
-
-
 def lcsa_draft_mask(geom: Geom, q_pool, q_first_abs_tb: int, cache: KvCacheStruct,
-                    params: SelectParams, kmax: int, sel_idx, sel_cnt, probs=None, stream=None):
+                    params: SelectParams, kmax: int, sel_idx, sel_cnt, probs=None, stream=None,
+                    probs_bytes=None):
+    """probs_bytes defaults to the probs tensor's own size."""
     lib = load_library()
+    pb = _nbytes(probs) if probs_bytes is None else probs_bytes
     _check(lib.lcsa_draft_mask(ctypes.byref(geom), _ptr(q_pool), q_first_abs_tb,
                                ctypes.byref(cache), ctypes.byref(params), kmax, _ptr(sel_idx),
-                               _ptr(sel_cnt), _ptr(probs), _stream(stream)))
+                               _ptr(sel_cnt), _ptr(probs), pb, _stream(stream)))
 
 
 def lcsa_block_sparse_attn(geom: Geom, q_blk, cache: KvCacheStruct, sel_idx, sel_cnt, kmax: int,
@@ -401,15 +386,13 @@ class StepBuffers:
 def run_step(geom: Geom, q, k, v, cache: KVCache, first_abs_tb: int, params: SelectParams,
              bufs: StepBuffers | None = None, keep_tb: int | None = None, stream=None,
              want_probs=False, want_lse=False, scale: float = 0.0, local: bool = False,
-             side_stream=None, q_blocks: bool = False):
+             q_blocks: bool = False):
     """One LCSA invocation through the C-ABI: append, partition+pool, draft
     (or, with local=True, the FlashVSR+ local lists: every allowed key
     block), attention, evict. The attention reads q in token layout, so the
     partition writes only q's block means; q_blocks=True instead writes the
-    query blocks to bufs.q_blk and reads them from there. With a side_stream,
-    the transposed-v part of the partition runs there, under the q/k part and
-    the draft, and the attention waits for it. Returns the StepBuffers
-    holding the results."""
+    query blocks to bufs.q_blk and reads them from there. Returns the
+    StepBuffers holding the results."""
     n_tb = geom.frames // 2
     first_slot = cache.append(n_tb, first_abs_tb)
     if local:
@@ -424,22 +407,13 @@ def run_step(geom: Geom, q, k, v, cache: KVCache, first_abs_tb: int, params: Sel
     if q_blocks and bufs.q_blk is None:
         raise ValueError("q_blocks=True needs StepBuffers(with_q_blk=True)")
     q_blk = bufs.q_blk if q_blocks else None
-    join = None
-    if side_stream is not None:
-        join = fork_v_part(geom, v, cache.c, first_slot, stream, side_stream)
-        lcsa_partition_pool_parts(geom, q, k, None, q_blk, bufs.q_pool, cache.c, first_slot,
-                                  PART_QK, stream)
-    else:
-        lcsa_partition_pool(geom, q, k, v, q_blk, bufs.q_pool, cache.c, first_slot, stream)
+    lcsa_partition_pool(geom, q, k, v, q_blk, bufs.q_pool, cache.c, first_slot, stream)
     if local:
         lcsa_local_lists(geom, first_abs_tb, cache.c, params, bufs.kmax, bufs.sel_idx,
                          bufs.sel_cnt, stream)
     else:
         lcsa_draft_mask(geom, bufs.q_pool, first_abs_tb, cache.c, params, bufs.kmax,
                         bufs.sel_idx, bufs.sel_cnt, bufs.probs, stream)
-    if join is not None:
-        import torch
-        (stream if stream is not None else torch.cuda.current_stream()).wait_event(join)
     if q_blocks:
         lcsa_block_sparse_attn(geom, q_blk, cache.c, bufs.sel_idx, bufs.sel_cnt, bufs.kmax,
                                bufs.out, bufs.lse, scale, stream)
@@ -449,67 +423,6 @@ def run_step(geom: Geom, q, k, v, cache: KVCache, first_abs_tb: int, params: Sel
     if keep_tb is not None:
         cache.evict(keep_tb)
     return bufs
-
-
-class StepPipeline:
-    """Consecutive streaming steps of one layer with the partition and the
-    lists of step n + 1 on a side stream, running under the attention of
-    step n on the main stream. Call prep(n) then attend(n) for n = 0, 1, ...
-    in that order (the attention takes the ring's view as it is after prep).
-
-    The ring must have one slot more than a step's view (cache + chunk TBs
-    + 1): step n + 1's new blocks then overwrite the blocks of step n - 1's
-    oldest TB, which step n's attention no longer reads, so prep(n + 1)
-    waits only for attention(n - 1). Lists, pooled queries and outputs are
-    double-buffered by step parity for the same reason. attend(n) waits for
-    prep(n)'s lists. Results equal those of run_step, step by step.
-    """
-
-    def __init__(self, geom: Geom, cache: KVCache, params: SelectParams, kmax: int,
-                 main, side, local: bool = False, with_lse: bool = False, device="cuda"):
-        import torch
-        self.geom, self.cache, self.params, self.local = geom, cache, params, local
-        self.main, self.side = main, side
-        self.bufs = [StepBuffers(geom, kmax, device=device, with_lse=with_lse) for _ in range(2)]
-        self.lists_ready = [torch.cuda.Event() for _ in range(2)]  # by step parity
-        self.attn_done = [torch.cuda.Event() for _ in range(3)]    # by step mod 3
-        self.n = 0
-        self.pending = None
-
-    def prep(self, q, k, v, first_abs_tb: int):
-        n, g, c = self.n, self.geom, self.cache
-        if n >= 2:  # the slot and the buffers this step reuses were read by attention(n - 2)
-            self.side.wait_event(self.attn_done[(n - 2) % 3])
-        slot = c.append(g.frames // 2, first_abs_tb)
-        b = self.bufs[n % 2]
-        lcsa_partition_pool(g, q, k, v, None, b.q_pool, c.c, slot, self.side)
-        if self.local:
-            lcsa_local_lists(g, first_abs_tb, c.c, self.params, b.kmax, b.sel_idx, b.sel_cnt,
-                             self.side)
-        else:
-            lcsa_draft_mask(g, b.q_pool, first_abs_tb, c.c, self.params, b.kmax, b.sel_idx,
-                            b.sel_cnt, None, self.side)
-        self.lists_ready[n % 2].record(self.side)
-        self.pending = (n, q)
-        self.n += 1
-
-    def attend(self, keep_tb: int, events=None):
-        """The attention of the step prep() last queued; events: an optional
-        (start, end) pair of timing events recorded around it on the main
-        stream. Returns that step's StepBuffers."""
-        n, q = self.pending
-        b = self.bufs[n % 2]
-        self.main.wait_event(self.lists_ready[n % 2])
-        if events is not None:
-            events[0].record(self.main)
-        lcsa_block_sparse_attn_tok(self.geom, q, self.cache.c, b.sel_idx, b.sel_cnt, b.kmax,
-                                   b.out, b.lse, 0.0, self.main)
-        if events is not None:
-            events[1].record(self.main)
-        self.attn_done[n % 3].record(self.main)
-        self.cache.evict(keep_tb)
-        self.pending = None
-        return b
 
 
 def run_segment_step(geom: Geom, q, k, v, cache: KVCache, first_abs_tb: int, frame_seg,

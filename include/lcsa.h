@@ -138,13 +138,18 @@ typedef struct {
 
 /* ---- cache metadata (host only, O(1), no HIP calls) -------------------- */
 
-/* Set up an empty ring over caller-allocated device buffers of at least
- * B*NH*n_slots*nS*128*D elements (k_ring, v_ring, in `dtype`) and
- * B*NH*n_slots*nS*D doubles (kpool_ring). 1 <= n_slots <= LCSA_MAX_SLOTS. */
+/* [HW] 2.3: the streaming KV cache that keeps the newest temporal blocks.
+ * Set up an empty ring over caller-allocated device buffers: k_ring and
+ * v_ring of B*NH*n_slots*nS*128*D elements in `dtype` (bytes_k, bytes_v
+ * their sizes in bytes), kpool_ring of B*NH*n_slots*D*nS doubles
+ * (bytes_kpool), nS = nby*nbx. 1 <= n_slots <= LCSA_MAX_SLOTS. A buffer
+ * smaller than that is LCSA_ERR_CAPACITY: every later call writes and reads
+ * the rings only inside those sizes. */
 lcsa_status lcsa_kv_cache_init(lcsa_kv_cache* cache, int32_t batch, int32_t heads,
                                int32_t head_dim, int32_t nby, int32_t nbx,
                                int32_t dtype, int32_t n_slots, void* k_ring,
-                               void* v_ring, double* kpool_ring);
+                               void* v_ring, double* kpool_ring, size_t bytes_k,
+                               size_t bytes_v, size_t bytes_kpool);
 
 /* Reserve slots for n_tb new temporal blocks numbered first_abs_tb,
  * first_abs_tb+1, ... (must be greater than every TB held). The slot of the
@@ -157,21 +162,26 @@ lcsa_status lcsa_kv_cache_append(lcsa_kv_cache* cache, int32_t n_tb,
  * segment is discarded). keep_tb >= 0. O(1); no bytes move. */
 lcsa_status lcsa_kv_cache_evict(lcsa_kv_cache* cache, int32_t keep_tb);
 
-/* The held TBs oldest -> newest: slots[i] and abs_tb[i] for i < *n_out.
- * Either output array may be NULL. */
+/* [HW] 2.3: the keys a streaming step attends are the cached segments
+ * followed by the new one. The held TBs oldest -> newest: slots[i] and
+ * abs_tb[i] for i < *n_out (at most LCSA_MAX_SLOTS entries each). Either
+ * output array may be NULL. */
 lcsa_status lcsa_kv_cache_view(const lcsa_kv_cache* cache, int32_t* n_out,
                                int32_t* slots, int64_t* abs_tb);
 
 /* ---- selection helpers (host only) ------------------------------------ */
 
-/* k for a row with n_allowed candidates out of n_keys key blocks, by the
- * rule in lcsa_select_params; 0 when n_allowed == 0. */
+/* [HW] 2.2 step 3, the topk_ratio rule (k shrinks as the output grows
+ * past the 768x1280 base). k for a row with n_allowed candidates out of
+ * n_keys key blocks, by the rule in lcsa_select_params; 0 when n_allowed
+ * == 0. LCSA_ERR_PARAM unless 0 <= n_allowed <= n_keys. */
 lcsa_status lcsa_topk_count(const lcsa_select_params* params, int32_t n_allowed,
                             int32_t n_keys, int32_t* k_out);
 
-/* Largest k over the query rows of a chunk (geometry gq, first temporal
- * block q_first_abs_tb) against the TBs currently held by `cache`: the
- * smallest kmax lcsa_draft_mask accepts. */
+/* [HW] 2.2 steps 2-3 (the local window and causal TBs give each row its
+ * candidates; the topk_ratio rule its k). Largest k over the query rows of
+ * a chunk (geometry gq, first temporal block q_first_abs_tb) against the
+ * TBs currently held by `cache`: the smallest kmax lcsa_draft_mask accepts. */
 lcsa_status lcsa_max_topk(const lcsa_geom* gq, int64_t q_first_abs_tb,
                           const lcsa_kv_cache* cache,
                           const lcsa_select_params* params, int32_t* kmax_out);
@@ -182,32 +192,18 @@ lcsa_status lcsa_max_topk(const lcsa_geom* gq, int64_t q_first_abs_tb,
  * Partition the chunk's q, k, v (token layout, geometry g) into 128-token
  * blocks. q goes to q_blk with its block means in q_pool (float64); k and v
  * of temporal block t of the chunk go to ring slot (first_slot + t) %
- * n_slots, with the block means of k in kpool_ring. Those slots must be held
- * by the cache (reserved by lcsa_kv_cache_append). q and q_pool are both
- * NULL (fill the cache only) or both non-NULL; q_blk may be NULL with them,
- * and then only q's block means are written (for the _tok attention entry
- * points, which read q in token layout). q_blk without q is LCSA_ERR_NULL. */
+ * n_slots, with the block means of k in kpool_ring. Those slots must be
+ * the cache's newest TBs, in order: first_slot is the slot that
+ * lcsa_kv_cache_append returned for this chunk (LCSA_ERR_PARAM otherwise;
+ * LCSA_ERR_CAPACITY if the chunk has more TBs than the cache holds). q and
+ * q_pool are both NULL (fill the cache only) or both non-NULL; q_blk may be
+ * NULL with them, and then only q's block means are written (for the _tok
+ * attention entry points, which read q in token layout). q_blk without q is
+ * LCSA_ERR_NULL. */
 lcsa_status lcsa_partition_pool(const lcsa_geom* g, const void* q, const void* k,
                                 const void* v, void* q_blk, double* q_pool,
                                 lcsa_kv_cache* cache, int32_t first_slot,
                                 void* stream);
-
-/* One part of lcsa_partition_pool, for callers that overlap the two parts
- * on two streams ([HW] 2.2 step 1 and step 3's pooling, as above).
- * parts = LCSA_PART_QK moves q (when given) and k into their blocks with
- * the block means: everything lcsa_draft_mask reads. parts = LCSA_PART_V
- * writes the transposed v blocks into the ring, which only
- * lcsa_block_sparse_attn reads. Both bits together equal
- * lcsa_partition_pool. A pointer the requested parts do not touch may be
- * NULL (v for LCSA_PART_QK alone; q, k, q_blk, q_pool for LCSA_PART_V
- * alone); the rules of lcsa_partition_pool hold for the others. The two
- * parts write disjoint memory. Any other value of parts is LCSA_ERR_PARAM. */
-#define LCSA_PART_QK 1
-#define LCSA_PART_V 2
-lcsa_status lcsa_partition_pool_parts(const lcsa_geom* g, const void* q, const void* k,
-                                      const void* v, void* q_blk, double* q_pool,
-                                      lcsa_kv_cache* cache, int32_t first_slot, int32_t parts,
-                                      void* stream);
 
 /* Steps 3-4 ([HW] 2.2 steps 2-3; [FN] Key designs 1-3). For each query
  * block of the chunk (geometry gq, first temporal block q_first_abs_tb) and
@@ -215,7 +211,8 @@ lcsa_status lcsa_partition_pool_parts(const lcsa_geom* g, const void* q, const v
  * later than the query's and it lies in the local window; score =
  * q_pool . kpool / sqrt(D) (float64); softmax over the candidates (written to
  * probs, [B][NH][nq][n_keys] float64 with 0 off the candidates, when probs is
- * non-NULL; n_keys = cache count * nS); keep the k candidates of largest
+ * non-NULL; n_keys = cache count * nS; probs_bytes is its size in bytes and
+ * a smaller buffer is LCSA_ERR_CAPACITY); keep the k candidates of largest
  * score, equal scores ordered by lower logical id. sel_idx receives the kept
  * logical ids in ascending order, padded with -1 up to kmax; sel_cnt the
  * count. kmax >= lcsa_max_topk() (LCSA_ERR_CAPACITY otherwise). */
@@ -223,7 +220,7 @@ lcsa_status lcsa_draft_mask(const lcsa_geom* gq, const double* q_pool,
                             int64_t q_first_abs_tb, const lcsa_kv_cache* cache,
                             const lcsa_select_params* params, int32_t kmax,
                             int32_t* sel_idx, int32_t* sel_cnt, double* probs,
-                            void* stream);
+                            size_t probs_bytes, void* stream);
 
 /* Step 5 ([FN] Key design 2: full 128x128 attention with the original Q, K,
  * V on the selected block pairs only; [HW] 2.2: unselected blocks are
@@ -233,8 +230,10 @@ lcsa_status lcsa_draft_mask(const lcsa_geom* gq, const double* q_pool,
  * scale == 0 means 1/sqrt(D). bf16 runs on MFMA with float32 accumulation;
  * f32 runs on the vector ALU. out is in token layout; lse (nullable,
  * [B][NH][nq][128] float32) receives the natural log-sum-exp of the scaled
- * logits. A row with sel_cnt 0 gets out = 0 and lse = -inf. Every listed id
- * must be < cache count * nS: ids are not checked on the device. */
+ * logits. A row with sel_cnt 0 gets out = 0 and lse = -inf. A listed id
+ * outside [0, cache count * nS) is skipped on the device: its block is never
+ * read and contributes nothing (a row whose ids are all skipped gets out = 0
+ * and lse = -inf). sel_cnt is clamped to [0, kmax]. */
 lcsa_status lcsa_block_sparse_attn(const lcsa_geom* gq, const void* q_blk,
                                    const lcsa_kv_cache* cache,
                                    const int32_t* sel_idx, const int32_t* sel_cnt,
@@ -356,7 +355,7 @@ lcsa_status lcsa_block_sparse_attn_bwd(const lcsa_geom* g, const void* q, const 
 /* Text of the last error on this thread ("" after success). */
 const char* lcsa_last_error(void);
 
-/* Interface version of this header: 4. */
+/* Interface version of this header: 5. */
 int32_t lcsa_abi_version(void);
 
 #ifdef __cplusplus

@@ -33,19 +33,45 @@ def test_exports_every_declared_symbol(lib):
     assert len(names) >= 10
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.lcsa_abi_version() == 4
+    assert lib.lcsa_abi_version() == 5
 
 
 FAKE = 0x10000  # aligned, never dereferenced: validation fails first
 
 
+def ring_bytes(nby, nbx, heads, D, dtype, n_slots, batch=1):
+    """Bytes of the K (= V) ring and of the pooled-K ring, as include/lcsa.h sizes them."""
+    blocks = batch * heads * n_slots * nby * nbx
+    return blocks * 128 * D * (2 if dtype == L.LCSA_BF16 else 4), blocks * D * 8
+
+
 def fake_cache(nby=6, nbx=11, heads=12, D=128, dtype=L.LCSA_BF16, n_slots=4):
     c = L.KvCacheStruct()
+    kv, pool = ring_bytes(nby, nbx, heads, D, dtype, n_slots)
     L.lcsa_kv_cache_init(c, 1, heads, D, nby, nbx, dtype, n_slots,
                          type("P", (), {"data_ptr": lambda s: FAKE})(),
                          type("P", (), {"data_ptr": lambda s: FAKE * 2})(),
-                         type("P", (), {"data_ptr": lambda s: FAKE * 3})())
+                         type("P", (), {"data_ptr": lambda s: FAKE * 3})(), kv, kv, pool)
     return c
+
+
+def test_ring_init_refuses_undersized_buffers(lib):
+    """lcsa_kv_cache_init takes the ring buffers' sizes and refuses any
+    smaller than n_slots slots need (LCSA_ERR_CAPACITY), before the partition
+    could write past them ([HW] "How FlashVSR works" 2.3: the cache of past
+    segments the ring holds)."""
+    for dtype, D in ((L.LCSA_BF16, 128), (L.LCSA_F32, 64)):
+        kv, pool = ring_bytes(6, 11, 3, D, dtype, 4, batch=2)
+        P = lambda a: type("P", (), {"data_ptr": lambda s: a})()
+        for sizes in ((kv - 1, kv, pool), (kv, kv - 1, pool), (kv, kv, pool - 1), (0, 0, 0)):
+            c = L.KvCacheStruct()
+            with pytest.raises(L.LcsaError) as e:
+                L.lcsa_kv_cache_init(c, 2, 3, D, 6, 11, dtype, 4, P(FAKE), P(FAKE), P(FAKE), *sizes)
+            assert e.value.status == 6, sizes
+            assert "too small" in str(e.value)
+        c = L.KvCacheStruct()
+        L.lcsa_kv_cache_init(c, 2, 3, D, 6, 11, dtype, 4, P(FAKE), P(FAKE), P(FAKE), kv, kv, pool)
+        assert c.n_slots == 4 and c.count == 0
 
 
 def test_ring_append_evict_view_wraps(lib):
@@ -80,7 +106,7 @@ def test_ring_capacity_and_order_errors(lib):
     L.lcsa_kv_cache_evict(c, 5)                   # keeping more than held is a no-op
     with pytest.raises(L.LcsaError):
         bad = L.KvCacheStruct()
-        L.lcsa_kv_cache_init(bad, 1, 1, 128, 2, 2, L.LCSA_BF16, 17, None, None, None)
+        L.lcsa_kv_cache_init(bad, 1, 1, 128, 2, 2, L.LCSA_BF16, 17, None, None, None, 0, 0, 0)
 
 
 def test_topk_count_matches_hand_table(lib):
@@ -142,23 +168,9 @@ def test_validation_rejects_bad_input_before_any_device_call(lib):
     expect(1, L.lcsa_partition_pool, geom, ok, None, ok, ok, ok, c, 0, s)
     expect(1, L.lcsa_partition_pool, geom, ok, ok, ok, ok, None, c, 0, s)   # q_pool missing
     expect(5, L.lcsa_partition_pool, geom, _P(FAKE + 8), ok, ok, ok, ok, c, 0, s)
-    # slot not held
-    expect(6, L.lcsa_partition_pool, geom, ok, ok, ok, ok, ok, c, 2, s)
+    # the chunk's TBs must be the newest held, from the slot the last append returned
+    expect(4, L.lcsa_partition_pool, geom, ok, ok, ok, ok, ok, c, 2, s)
     expect(4, L.lcsa_partition_pool, geom, ok, ok, ok, ok, ok, c, 9, s)
-    # the partition's parts: only LCSA_PART_QK, LCSA_PART_V or both; the pointers a part
-    # touches are checked, the others may be NULL
-    P = L.lcsa_partition_pool_parts
-    expect(4, P, geom, ok, ok, ok, ok, ok, c, 0, 0, s)
-    expect(4, P, geom, ok, ok, ok, ok, ok, c, 0, 4, s)
-    expect(1, P, geom, None, None, None, None, None, c, 0, L.PART_V, s)      # v missing
-    expect(1, P, geom, ok, None, None, ok, ok, c, 0, L.PART_QK, s)           # k missing
-    expect(1, P, geom, ok, ok, None, None, None, c, 0, L.PART_QK, s)         # q without q_pool
-    expect(1, P, geom, None, ok, None, ok, None, c, 0, L.PART_QK, s)         # q_blk without q
-    expect(5, P, geom, ok, ok, None, _P(FAKE + 8), ok, c, 0, L.PART_QK, s)   # q_blk misaligned
-    expect(5, P, geom, None, None, _P(FAKE + 8), None, None, c, 0, L.PART_V, s)
-    expect(6, P, geom, None, None, ok, None, None, c, 2, L.PART_V, s)        # slot not held
-    expect(2, P, L.make_geom(1, 12, 128, 3, 48, 88, 0), None, ok, None, None, None, c, 0,
-           L.PART_QK, s)
     # selection parameters
     expect(4, L.lcsa_draft_mask, geom, ok, 0, c, L.make_params(local_range=10), 64, ok, ok, None, s)
     expect(4, L.lcsa_draft_mask, geom, ok, 0, c, L.make_params(local_range=0), 64, ok, ok, None, s)
@@ -171,6 +183,11 @@ def test_validation_rejects_bad_input_before_any_device_call(lib):
     msg = expect(6, L.lcsa_draft_mask, geom, ok, 0, c, L.make_params(), 12, ok, ok, None, s)
     assert "13" in msg
     expect(5, L.lcsa_draft_mask, geom, ok, 0, c, L.make_params(), 64, ok, ok, _P(FAKE + 4), s)
+    # probs one double short of [B][NH][nq][n_keys]: 12 heads x 66 rows x 66 keys
+    need = 12 * 66 * 66 * 8
+    msg = expect(6, L.lcsa_draft_mask, geom, ok, 0, c, L.make_params(), 64, ok, ok, ok, s,
+                 probs_bytes=need - 8)
+    assert str(need) in msg
     # geometry disagrees with the cache
     expect(2, L.lcsa_draft_mask, L.make_geom(1, 8, 128, 2, 48, 88, 0), ok, 0, c, L.make_params(), 64,
            ok, ok, None, s)
@@ -301,3 +318,30 @@ def test_backward_workspace_size_and_validation(lib):
     assert lib_.lcsa_block_sparse_attn_bwd(ctypes.byref(g), None, FAKE, FAKE, FAKE, FAKE, FAKE,
                                            FAKE, FAKE, 4, ctypes.c_float(0), FAKE, FAKE, FAKE,
                                            FAKE, need, None) == 1  # LCSA_ERR_NULL
+
+
+def test_partition_requires_the_newest_tbs_in_order(lib):
+    """The chunk's temporal blocks go to the slots the last append returned:
+    any other first_slot, or a chunk with more TBs than the cache holds, is
+    refused before any device call (it would overwrite older cached TBs)."""
+    ok = _P(FAKE)
+    c = fake_cache(n_slots=4)
+    L.lcsa_kv_cache_append(c, 2, 0)              # slots 0, 1
+    L.lcsa_kv_cache_evict(c, 1)                   # holds TB 1 in slot 1
+    assert L.lcsa_kv_cache_append(c, 2, 2) == 2   # TBs 2, 3 -> slots 2, 3
+    two = L.make_geom(1, 12, 128, 4, 48, 88, L.LCSA_BF16)
+    three = L.make_geom(1, 12, 128, 6, 48, 88, L.LCSA_BF16)
+    one = L.make_geom(1, 12, 128, 2, 48, 88, L.LCSA_BF16)
+    for first in (0, 1, 3):                       # not the slot the append returned
+        expect(4, L.lcsa_partition_pool, two, ok, ok, ok, ok, ok, c, first, 0)
+    expect(6, L.lcsa_partition_pool, L.make_geom(1, 12, 128, 8, 48, 88, 0), ok, ok, ok, ok, ok, c,
+           1, 0)                                  # 4 TBs, 3 held
+    expect(4, L.lcsa_partition_pool, three, ok, ok, ok, ok, ok, c, 2, 0)  # 3 TBs from slot 2 wrap
+    expect(4, L.lcsa_partition_pool, one, ok, ok, ok, ok, ok, c, 2, 0)    # TB 2 is not the newest
+    # wrap-around: the newest TB can sit in slot 0
+    c2 = fake_cache(n_slots=4)
+    L.lcsa_kv_cache_append(c2, 4, 0)
+    L.lcsa_kv_cache_evict(c2, 3)
+    assert L.lcsa_kv_cache_append(c2, 1, 4) == 0
+    expect(4, L.lcsa_partition_pool, one, ok, ok, ok, ok, ok, c2, 3, 0)
+    expect(4, L.lcsa_partition_pool, two, ok, ok, ok, ok, ok, c2, 0, 0)

@@ -110,59 +110,6 @@ def test_token_and_block_q_paths_agree(dev, kw):
     say(f"token vs block q: {stats}")
 
 
-@pytest.mark.parametrize("kw,local", [(dict(), False), (dict(head_dim=64), False),
-                                      (dict(dtype="f32"), False), (dict(local_range=3), True)],
-                         ids=["bf16-d128", "bf16-d64", "f32-d128", "local-lists"])
-def test_pipelined_steps_match_sequential(dev, kw, local):
-    """StepPipeline (partition and lists of step n + 1 on a side stream under
-    the attention of step n, a ring with one extra slot) gives bitwise the
-    lists, outputs and lse of sequential run_step calls, step after step."""
-    w = small(**{**dict(frames=2, cache_frames=6, cap_tb=3, local_range=5, ratio=(1, 4)), **kw})
-    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    code = L.LCSA_BF16 if w.dtype == "bf16" else L.LCSA_F32
-    n_tb = w.frames // 2
-    n_steps = 5
-    d = synth.make_qkv(w.seed, w.heads, w.head_dim, w.height, w.width, 0,
-                       w.cache_frames + n_steps * w.frames, dtype=w.dtype)
-    q, k, v = (to_dev(d[n][0], w.dtype, dev) for n in "qkv")
-    geom = L.make_geom(1, w.heads, w.head_dim, w.frames, w.height, w.width, code)
-    gprime = L.make_geom(1, w.heads, w.head_dim, w.cache_frames, w.height, w.width, code)
-    params = lib_params(w)
-    caches = []
-    for extra in (0, 1):  # the sequential ring, and one slot more for the pipeline
-        c = L.KVCache(1, w.heads, w.head_dim, w.height, w.width, tdt,
-                      w.cap_tb + n_tb + extra, device=dev)
-        first = c.append(w.cache_frames // 2, 0)
-        L.lcsa_partition_pool(gprime, None, k[:, :w.cache_frames], v[:, :w.cache_frames],
-                              None, None, c.c, first)
-        caches.append(c)
-    torch.cuda.synchronize()
-    seq = []
-    for n in range(n_steps):
-        f0 = w.cache_frames + n * w.frames
-        sl = slice(f0, f0 + w.frames)
-        b = L.run_step(geom, q[:, sl], k[:, sl], v[:, sl], caches[0], f0 // 2, params,
-                       keep_tb=w.cap_tb, want_lse=True, local=local)
-        seq.append({kk: getattr(b, kk).clone() for kk in ("sel_idx", "sel_cnt", "out", "lse")})
-    torch.cuda.synchronize()
-    kmax = seq[0]["sel_idx"].shape[-1]  # every step's row has the same candidate count
-    main, side = torch.cuda.current_stream(), torch.cuda.Stream()
-    pipe = L.StepPipeline(geom, caches[1], params, kmax, main, side, local=local, with_lse=True,
-                          device=dev)
-    got = []
-    for n in range(n_steps):
-        f0 = w.cache_frames + n * w.frames
-        sl = slice(f0, f0 + w.frames)
-        pipe.prep(q[:, sl], k[:, sl], v[:, sl], f0 // 2)
-        b = pipe.attend(w.cap_tb)
-        got.append({kk: getattr(b, kk).clone() for kk in ("sel_idx", "sel_cnt", "out", "lse")})
-    torch.cuda.synchronize()
-    for n in range(n_steps):
-        for kk in ("sel_idx", "sel_cnt", "out", "lse"):
-            assert torch.equal(seq[n][kk], got[n][kk]), (n, kk)
-    say(f"pipelined == sequential over {n_steps} steps ({w.dtype}, D {w.head_dim}, local {local})")
-
-
 def test_small_streaming_with_cache(dev):
     w = small(frames=2, cache_frames=6, cap_tb=3, local_range=5, ratio=(1, 4))
     st = Stream(w, dev)
@@ -171,32 +118,6 @@ def test_small_streaming_with_cache(dev):
         stats = compare_step(w, g, ref)
     say(f"small stream: {stats}")
 
-
-@pytest.mark.parametrize("kw", [dict(), dict(head_dim=64), dict(dtype="f32")],
-                         ids=["bf16-d128", "bf16-d64", "f32-d128"])
-def test_two_stream_partition_matches_one_stream(dev, kw):
-    """The transposed-v part of the partition on a second stream (forked after
-    the previous step, joined before the attention) gives bitwise the same
-    lists, outputs, pooled q and ring contents as the one-stream step, step
-    after step while ring slots are reused, and matches the oracle."""
-    w = small(frames=2, cache_frames=6, cap_tb=3, local_range=5, ratio=(1, 4), **kw)
-    one = Stream(w, dev)
-    two = Stream(w, dev, side_stream=torch.cuda.Stream())
-    for n in range(4):
-        g1, _ = one.step(want_probs=False)
-        g2, ref = two.step(want_probs=False)
-        for key in ("sel_idx", "sel_cnt", "lse", "q_pool"):
-            assert np.array_equal(g1[key], g2[key]), key
-        assert torch.equal(g1["out"], g2["out"])
-        slots, _ = two.gcache.view()
-        assert slots == one.gcache.view()[0]
-        for sl in slots:  # the blocks the caches hold (other slots were never written)
-            for ring in ("k_ring", "v_ring", "kpool_ring"):
-                assert torch.equal(getattr(one.gcache, ring)[:, :, sl],
-                                   getattr(two.gcache, ring)[:, :, sl]), (ring, sl)
-        check_layouts(two, g2, ref)
-        stats = compare_step(w, g2, ref)
-    say(f"two-stream partition: {stats}")
 
 
 @pytest.mark.parametrize("q_scale", [16.0, 64.0])
