@@ -55,6 +55,10 @@ def parse():
                     help="no GPU work: turn the rocprofv3 output of a --kernel-trace --stats run "
                          "and of --pmc FETCH_SIZE / --pmc WRITE_SIZE runs of this script into "
                          "profiles/<kernels>_<workload>.md and the workload's traffic.json entry")
+    ap.add_argument("--sq-dir", default=None,
+                    help="with --summarize-profiles: the output of a rocprofv3 --pmc run of this "
+                         "script with the SQ_COUNTERS set (instruction mix, matrix-core busy "
+                         "cycles, LDS bank conflicts, GPU clock)")
     ap.add_argument("--bench-log", default=None,
                     help="with --summarize-profiles: a log whose last line is this script's JSON")
     return ap.parse_args()
@@ -160,10 +164,14 @@ def main():
                                       device=dev)
                 self.grads = [torch.empty_like(self.dout) for _ in range(3)]
 
-        def run(self, tb, q, k, v, ev=None, evb=None):
+        def run(self, tb, q, k, v, ev=None, evb=None, evk=None):
             c, b = self.cache, self.bufs
             slot = c.append(w.frames // 2, tb)
+            if evk is not None:
+                evk[0].record(stream)
             L.lcsa_partition_pool(geom, q, k, v, b.q_blk, b.q_pool, c.c, slot, stream)
+            if evk is not None:
+                evk[1].record(stream)
             if self.seg:
                 L.lcsa_segment_lists(geom, tb, c.c, self.seg, self.kmax, b.sel_idx, b.sel_cnt,
                                      stream)
@@ -214,6 +222,10 @@ def main():
 
     evb = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             for _ in layers] for _ in range(n_steps)]
+    # partition start, partition end (= list kernel start): the lists end where
+    # the attention's start event is recorded
+    evk = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in layers] for _ in range(n_steps)]
 
     def step(n, timed=False):
         tb = tb_first + n * (w.frames // 2)
@@ -223,7 +235,8 @@ def main():
         k = qkv["k"][:, f0:f0 + w.frames]
         v = qkv["v"][:, f0:f0 + w.frames]
         for li, layer in enumerate(layers):
-            layer.run(tb, q, k, v, ev[n][li] if timed else None, evb[n][li] if timed else None)
+            layer.run(tb, q, k, v, ev[n][li] if timed else None, evb[n][li] if timed else None,
+                      evk[n][li] if timed else None)
 
     for n in range(W):
         step(n)
@@ -256,6 +269,42 @@ def main():
 
     traffic = traffic_for(args.traffic_json, args.workload)
 
+    # ---- the other kernels of the step, against HBM: algorithmic bytes of
+    # one launch (what the step must move) over the launch's mean duration
+    timed = range(W, W + K)
+    part_ms = [sum(a.elapsed_time(b_) for (a, b_) in evk[n]) for n in timed]
+    lists_ms = [sum(b_.elapsed_time(e0) for (a, b_), (e0, e1) in zip(evk[n], ev[n])) for n in timed]
+    esz = 2 if w.dtype == "bf16" else 4
+    blk_heads = w.batch * w.heads * w.nq  # (query block, head) pairs of a chunk
+    part_bytes = blk_heads * (5 * 128 * w.head_dim * esz + 2 * w.head_dim * 8
+                              + (128 * w.head_dim * esz if args.q_blocks else 0))
+    part_bytes *= len(layers)
+    lists_bytes = 0
+    lists_kind = set()
+    for la in layers:
+        # the draft's view: the cached TBs (steady state) and the chunk's own
+        view_keys = ((la.sp.cap_tb if la.sp.cache_frames else 0) + w.frames // 2) * w.nS
+        sel = blk_heads * (la.kmax + 1) * 4
+        if la.seg or la.sp.lists == "local":
+            lists_bytes += sel
+            lists_kind.add("segment lists" if la.seg else "local lists")
+        else:  # pooled queries and the pooled keys of the view in, ids out
+            lists_bytes += blk_heads * w.head_dim * 8 + w.batch * w.heads * view_keys * \
+                w.head_dim * 8 + sel
+            lists_kind.add("draft mask")
+
+    def hbm(byts, ms):
+        gbs = byts / (ms * 1e-3) / 1e9
+        return {"us": round(ms * 1e3, 2), "algorithmic_bytes": int(byts), "gb_s": round(gbs, 1),
+                "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+
+    kernels = {
+        "partition_pool": hbm(part_bytes, float(np.mean(part_ms))),
+        "lists": {"kind": " + ".join(sorted(lists_kind)), **hbm(lists_bytes, float(np.mean(lists_ms)))},
+        "attention": {"us": round(attn_avg * 1e3, 2), "tflop_s": round(achieved, 1),
+                      "mfma_frac": round(achieved / PEAK_BF16_TFLOPS, 4)},
+    }
+
     result = {
         "metric": "block-sparse attn effective TFLOP/s + ms per streaming step at 768x1408",
         "value": round(value, 3),
@@ -284,12 +333,143 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
+        "kernels": kernels,
     }
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_heads, args.cpu_sample_steps,
-                                              flops_pair)
+        single = (not w.layers and not w.backward and not w.frame_seg and w.lists == "draft")
+        if single:  # the oracle on the run's own last steps, compared with the GPU's last step
+            la = layers[0]
+            last = W + K - 1
+            result["cpu_baseline"] = cpu_baseline_run(
+                w, qkv, t_first, last, min(args.cpu_sample_steps, last + 1),
+                la.bufs, flops_pair)
+        else:
+            result["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_heads,
+                                                  args.cpu_sample_steps, flops_pair)
     print(json.dumps(result), flush=True)
+
+
+def _cpu_cores():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            return next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")),
+                        None)
+    except OSError:
+        return None
+
+
+def _tied_ok(scores, k, gpu_ids, ref_ids):
+    """Selection rule of the parity check: exact, or, where the k-th and
+    (k+1)-th draft scores are within 1e-5 relative (+1e-7), any set of k
+    holding every score above the tie and none below it. Returns (ok, tied)."""
+    import numpy as np
+    gpu = sorted(int(x) for x in gpu_ids)
+    fin = np.isfinite(scores)
+    n = int(fin.sum())
+    if len(gpu) != k or len(set(gpu)) != k or not all(fin[j] for j in gpu):
+        return False, False
+    if k == 0 or k >= n:
+        return gpu == sorted(np.nonzero(fin)[0].tolist()), False
+    vals = np.sort(scores[fin])[::-1]
+    sk, sk1 = vals[k - 1], vals[k]
+    tol = 1e-5 * max(abs(sk), abs(sk1)) + 1e-7
+    if abs(sk - sk1) > tol:
+        return gpu == sorted(int(x) for x in ref_ids), False
+    must = set(np.nonzero(fin & (scores > sk + tol))[0].tolist())
+    may = set(np.nonzero(fin & (scores >= sk1 - tol))[0].tolist())
+    return must <= set(gpu) <= may, True
+
+
+def cpu_baseline_run(w, qkv, t_first, last, n_steps, bufs, flops_pair):
+    """The float64 oracle, as it stands, on the last `n_steps` timed steps of
+    this very run (their device-generated q, k, v copied to the host; the
+    oracle's cache primed with the frames before them), timed on the host.
+    The last of them is then compared with the GPU's results for that step,
+    which are still in `bufs`: the selection on every row (exact, or the tie
+    rule), and the output and log-sum-exp on every row."""
+    import math
+
+    import numpy as np
+
+    from oracle import lcsa_oracle as O
+
+    F = w.frames
+
+    def host(t):
+        return t.float().cpu().numpy().astype(np.float64)
+
+    p = O.SelectParams(local_range=w.local_range, border=w.border, topk_fixed=w.topk_fixed,
+                       ratio_num=w.ratio[0], ratio_den=w.ratio[1],
+                       scale_by_resolution=w.scale_by_resolution, out_h=w.out_hw[0],
+                       out_w=w.out_hw[1], ratio_base=w.ratio_base)
+    first = last - n_steps + 1
+    cache = O.KVCache(cap_tb=w.cap_tb)
+    if w.cache_frames:
+        c0 = t_first + first * F - w.cache_frames
+        O.prime_cache(cache, host(qkv["k"][:, c0:c0 + w.cache_frames]),
+                      host(qkv["v"][:, c0:c0 + w.cache_frames]), c0 // 2)
+    sec, pairs, res = 0.0, 0, None
+    for n in range(first, last + 1):
+        f0 = t_first + n * F
+        q, k, v = host(qkv["q"][:, n * F:(n + 1) * F]), host(qkv["k"][:, f0:f0 + F]), \
+            host(qkv["v"][:, f0:f0 + F])
+        tic = time.perf_counter()
+        res = O.lcsa_step(q, k, v, cache, f0 // 2, p)
+        sec += time.perf_counter() - tic
+        pairs += int(sum(len(r) for bh in res.sel for hh in bh for r in hh))
+        if not w.cache_frames:
+            cache = O.KVCache(cap_tb=w.cap_tb)  # a cold start each step
+    # parity of the last step
+    sel = bufs.sel_idx.cpu().numpy()
+    cnt = bufs.sel_cnt.cpu().numpy()
+    out_g = O.partition(host(bufs.out))
+    out_r = O.partition(res.out)
+    kb, vb = res.key_blocks
+    mism, tied, rows = 0, 0, 0
+    got, exp = [], []
+    for b in range(w.batch):
+        for h in range(w.heads):
+            for i in range(w.nq):
+                rows += 1
+                kr = int(res.kcount[i])
+                ids = sel[b, h, i, :max(int(cnt[b, h, i]), 0)]
+                ok, t = _tied_ok(res.scores[b, h, i], kr, ids, res.sel[b][h][i])
+                tied += t
+                if not ok or int(cnt[b, h, i]) != kr:
+                    mism += 1
+                    continue
+                got.append(out_g[b, h, i])
+                if sorted(int(x) for x in ids) == list(res.sel[b][h][i]):
+                    exp.append(out_r[b, h, i])
+                else:  # a tied row: the oracle's attention over the GPU's set
+                    exp.append(O.sparse_attention_row(res.q_blocks[b, h, i], kb[b, h], vb[b, h],
+                                                      np.array(sorted(int(x) for x in ids)),
+                                                      1.0 / math.sqrt(w.head_dim))[0])
+    got, exp = np.stack(got), np.stack(exp)
+    d = got - exp
+    max_abs = float(np.abs(d).max())
+    rel = float(np.linalg.norm(d) / np.linalg.norm(exp))
+    tol = (2e-2, 5e-3) if w.dtype == "bf16" else (1e-4, 1e-5)
+    parity = {"step": last, "rows": rows, "selection_mismatches": mism, "tied_rows": tied,
+              "max_abs": float(f"{max_abs:.3e}"), "rel_l2": float(f"{rel:.3e}"),
+              "tolerance": {"max_abs": tol[0], "rel_l2": tol[1]},
+              "pass": mism == 0 and max_abs <= tol[0] and rel <= tol[1]}
+    return {"value": round(pairs * flops_pair / sec / 1e12, 6), "unit": "TFLOP/s",
+            "cores": _cpu_cores(), "kind": "oracle", "seconds": round(sec, 3),
+            "cpu_model": _cpu_model(),
+            "sample": f"the last {n_steps} timed steps of this run (steps {first}..{last}), every "
+                      f"head and row: full LCSA steps (partition, pool, draft, top-k, attention, "
+                      f"cache update) in float64 NumPy on the run's own inputs",
+            "parity": parity}
 
 
 def cpu_baseline(w, sample_heads, sample_steps, flops_pair):
@@ -402,6 +582,35 @@ def _counter_per_dispatch(d, counter):
     return copy, sum(attn) / len(attn), len(attn)
 
 
+# The shader-sequencer counters of the instruction-mix run: one rocprofv3
+# --pmc pass (at most 8 SQ and 2 GRBM counters).
+SQ_COUNTERS = ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_LDS",
+               "SQ_LDS_BANK_CONFLICT", "SQ_WAVES", "SQ_BUSY_CU_CYCLES", "GRBM_GUI_ACTIVE")
+N_SIMDS, N_XCDS = 1024, 8  # MI355X: 256 CUs x 4 SIMDs, 8 XCDs
+
+
+def _per_kernel_counters(d, names):
+    """{kernel short name: {counter: mean value per dispatch}} over the LCSA
+    kernels of a --pmc run, plus the calibration copy's values."""
+    rows = _csv_rows(d, "counter_collection.csv")
+    acc, disp, copy = {}, {}, {}
+    for r in rows:
+        c = r["Counter_Name"]
+        if c not in names:
+            continue
+        v = float(r["Counter_Value"])
+        if COPY_KERNEL in r["Kernel_Name"]:
+            copy.setdefault(c, v)  # the first copy of the process
+            continue
+        k = _short(r["Kernel_Name"])
+        if not k:
+            continue
+        acc.setdefault(k, {}).setdefault(c, 0.0)
+        acc[k][c] += v
+        disp.setdefault(k, {}).setdefault(c, set()).add(r["Dispatch_Id"])
+    return {k: {c: v / len(disp[k][c]) for c, v in cs.items()} for k, cs in acc.items()}, copy
+
+
 def summarize_profiles(args):
     """Host-only: write the kernel-trace summary and the counter-derived HBM
     traffic of the attention kernel for one workload."""
@@ -426,7 +635,15 @@ def summarize_profiles(args):
             bench = json.loads([ln for ln in f if ln.startswith("{")][-1])
     if cnt:
         _write_traffic(args, *cnt)
-    _write_summary(args, stats, bench, cnt)
+    per_kernel = None
+    if counters:
+        fk, fcopy = _per_kernel_counters(fetch_dir, ("FETCH_SIZE",))
+        wk, wcopy = _per_kernel_counters(write_dir, ("WRITE_SIZE",))
+        per_kernel = {"fetch": fk, "write": wk,
+                      "f_factor": probe_bytes / (fcopy["FETCH_SIZE"] * 1024.0),
+                      "w_factor": probe_bytes / (wcopy["WRITE_SIZE"] * 1024.0)}
+    sq = _per_kernel_counters(args.sq_dir, SQ_COUNTERS)[0] if args.sq_dir else None
+    _write_summary(args, stats, bench, cnt, per_kernel, sq)
 
 
 def _write_traffic(args, fetch_b, write_b, fa, wa, fc, wc, f_factor, w_factor, nf, nw):
@@ -449,7 +666,7 @@ def _write_traffic(args, fetch_b, write_b, fa, wa, fc, wc, f_factor, w_factor, n
         f.write("\n")
 
 
-def _write_summary(args, stats, bench, cnt):
+def _write_summary(args, stats, bench, cnt, per_kernel=None, sq=None):
     sw = (f"--steps {bench['steps']} --warmup {bench['warmup']}" if bench else "--steps S --warmup W")
     kernels = sorted({_short(r["Name"]) for r in stats})
     names = sorted({k.split("<")[0].replace("_kernel", "") for k in kernels})
@@ -464,9 +681,11 @@ def _write_summary(args, stats, bench, cnt):
              *([f"    rocprofv3 --pmc FETCH_SIZE --output-format csv -d FETCH_DIR -o pmc -- {cmd_b}",
                 f"    rocprofv3 --pmc WRITE_SIZE --output-format csv -d WRITE_DIR -o pmc -- {cmd_b}"]
                if cnt else []),
+             *([f"    rocprofv3 --pmc {' '.join(SQ_COUNTERS)} --output-format csv -d SQ_DIR -o pmc "
+                f"-- {cmd_b}"] if sq else []),
              f"    python3 bench.py --workload {args.workload} --copy-probe-mib {args.copy_probe_mib} "
              f"--summarize-profiles TRACE_DIR {'FETCH_DIR WRITE_DIR' if cnt else '- -'} "
-             "--bench-log BENCH_LOG", "",
+             f"{'--sq-dir SQ_DIR ' if sq else ''}--bench-log BENCH_LOG", "",
              "## Kernel durations (rocprofv3 --stats)", "",
              "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
     for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
@@ -496,6 +715,41 @@ def _write_summary(args, stats, bench, cnt):
               "| counter | raw KiB per launch | calibrated MB per launch | launches |", "|---|---|---|---|",
               f"| FETCH_SIZE | {fa:.0f} | {fetch_b / 1e6:.1f} | {nf} |",
               f"| WRITE_SIZE | {wa:.0f} | {write_b / 1e6:.1f} | {nw} |", ""]
+    avg_us = {_short(r["Name"]): float(r["AverageNs"]) / 1e3 for r in stats}
+    if per_kernel:
+        ff, wf = per_kernel["f_factor"], per_kernel["w_factor"]
+        lines += ["## HBM traffic of every kernel (the same --pmc runs, same calibration)", "",
+                  "Bytes the counters saw per launch, and that traffic over the kernel's mean "
+                  "duration in the trace run, against the 8 TB/s HBM peak.", "",
+                  "| kernel | fetched MB | written MB | average us | counted GB/s | fraction of HBM |",
+                  "|---|---|---|---|---|---|"]
+        for k in sorted(per_kernel["fetch"], key=lambda k: -avg_us.get(k, 0)):
+            fb = per_kernel["fetch"][k].get("FETCH_SIZE", 0) * 1024 * ff
+            wb = per_kernel["write"].get(k, {}).get("WRITE_SIZE", 0) * 1024 * wf
+            us = avg_us.get(k)
+            if not us:
+                continue
+            gbs = (fb + wb) / (us * 1e-6) / 1e9
+            lines.append(f"| {k} | {fb / 1e6:.2f} | {wb / 1e6:.2f} | {us:.1f} | {gbs:.0f} | "
+                         f"{gbs / PEAK_HBM_GBS:.3f} |")
+        lines.append("")
+    if sq:
+        lines += ["## Instruction mix and matrix-core use (rocprofv3 --pmc, one pass)", "",
+                  "Per launch. GRBM_GUI_ACTIVE sums the 8 XCDs' busy cycles, so the clock is "
+                  "GRBM_GUI_ACTIVE / 8 over the trace's mean duration; the matrix cores are busy "
+                  "SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8) of the time. "
+                  "SQ_INSTS_VALU counts the MFMA instructions too.", "",
+                  "| kernel | " + " | ".join(SQ_COUNTERS) + " | clock GHz | MFMA busy |",
+                  "|---|" + "---|" * (len(SQ_COUNTERS) + 2)]
+        for k in sorted(sq, key=lambda k: -avg_us.get(k, 0)):
+            c = sq[k]
+            us = avg_us.get(k)
+            cyc = c.get("GRBM_GUI_ACTIVE", 0) / N_XCDS
+            ghz = cyc / (us * 1e3) if us else 0.0
+            busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0) / (N_SIMDS * cyc) if cyc else 0.0
+            lines.append(f"| {k} | " + " | ".join(f"{c.get(n, 0):.0f}" for n in SQ_COUNTERS) +
+                         f" | {ghz:.2f} | {busy:.3f} |")
+        lines.append("")
     with open(out, "w") as f:
         f.write("\n".join(lines))
     print(json.dumps({"wrote": out}))

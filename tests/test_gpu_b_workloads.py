@@ -5,8 +5,9 @@ The HIP path through the C-ABI against the float64 oracle.
 Every case runs on the GPU and in the oracle from the same seeded inputs.
 Selections are compared on every row (exact, or the tie rule for rows whose
 k-th and (k+1)-th scores are within 1e-5 relative); outputs element by
-element on every row for small cases and on sampled rows at the full
-workload sizes (the oracle computes those rows one by one).
+element on every row of every head for one step of each of the four
+full-size workloads, and on sampled rows for the further steps of a stream
+(the oracle computes those rows one by one).
 """
 from __future__ import annotations
 
@@ -72,31 +73,33 @@ def test_tiny_fp32_all_rows(dev):
     say(f"tiny: {stats}")
 
 
-def test_cold_start_768x1408(dev):
+def test_cold_start_768x1408_every_row(dev):
     w = WORKLOADS["cold_768x1408"]
     st = Stream(w, dev)
-    rows = sample_rows(w, 8)
-    g, ref = st.step(rows=rows)
+    g, ref = st.step()
     assert sorted(set(int(x) for x in ref.kcount)) == [13, 26, 39]
-    stats = compare_step(w, g, ref, rows=rows)
-    say(f"cold 768x1408: {stats}")
+    stats = compare_step(w, g, ref)
+    assert stats["rows"] == w.heads * w.nq
+    say(f"cold 768x1408, every row of 12 heads: {stats}")
 
 
-def test_streaming_step_768x1408_full_heads(dev):
+def test_streaming_step_768x1408_every_row(dev):
+    """The first step every row of all 12 heads, two more on sampled rows."""
     w = WORKLOADS["step_768x1408"]
     st = Stream(w, dev)
     for n in range(3):
-        rows = sample_rows(w, 6, rng_seed=n)
+        rows = "all" if n == 0 else sample_rows(w, 6, rng_seed=n)
         g, ref = st.step(rows=rows)
         assert set(int(x) for x in ref.kcount) == {52}
         stats = compare_step(w, g, ref, rows=rows)
         say(f"step {n} 768x1408: {stats}")
 
 
-def test_streaming_100_steps_768x1408(dev):
-    """100 consecutive steps of a 768x1408 stream (2 heads to keep the host
-    generator fast): every selection of every step, sampled outputs."""
-    w = dataclasses.replace(WORKLOADS["step_768x1408"], heads=2, seed=4242)
+def test_streaming_100_steps_768x1408_12_heads(dev):
+    """100 consecutive steps of the 768x1408 stream at its 12 heads: every
+    selection of every step (tie rule), outputs on sampled rows of every
+    head, and the ring holding exactly the last 3 TBs after each step."""
+    w = dataclasses.replace(WORKLOADS["step_768x1408"], seed=4242)
     st = Stream(w, dev)
     tied = 0
     for n in range(100):
@@ -106,18 +109,18 @@ def test_streaming_100_steps_768x1408(dev):
         tied += stats["tied"]
         slots, tbs = st.gcache.view()
         assert tbs == [n + 1, n + 2, n + 3] and st.ocache.tbs() == tbs
-    say(f"100 steps ok, tied rows {tied}")
+    say(f"100 steps x 12 heads ok, tied rows {tied}")
 
 
 @pytest.mark.parametrize("name", ["step_1536x2688", "step_4k"])
-def test_streaming_step_large(dev, name):
+def test_streaming_step_large_every_row(dev, name):
     w = WORKLOADS[name]
     st = Stream(w, dev)
-    rows = sample_rows(w, 4)
-    g, ref = st.step(rows=rows, want_probs=False)
+    g, ref = st.step(want_probs=False)
     assert set(int(x) for x in ref.kcount) == {23 if name == "step_1536x2688" else 11}
-    stats = compare_step(w, g, ref, rows=rows, check_probs=False)
-    say(f"{name}: {stats}")
+    stats = compare_step(w, g, ref, check_probs=False)
+    assert stats["rows"] == w.heads * w.nq
+    say(f"{name}, every row of 12 heads: {stats}")
 
 
 
