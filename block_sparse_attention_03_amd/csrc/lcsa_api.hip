@@ -2,6 +2,7 @@
 // on the host (lcsa_host.cpp) before the first HIP call; on any failure
 // nothing is enqueued.
 #include <cmath>
+#include <mutex>
 #include <numeric>
 
 #include "lcsa_host.h"
@@ -10,6 +11,44 @@
 using namespace lcsa;
 
 namespace {
+
+// Scratch of the allocation-free backward (lcsa_block_sparse_attn_bwd_noalloc):
+// a file-scope device array, one copy on every GPU the library runs on, held
+// until the process ends. Its host-side name is only a stand-in; the device
+// address comes from hipGetSymbolAddress, once per device, with that device
+// current, and is kept per device.
+constexpr size_t kNoAllocScratchBytes = LCSA_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address, or nullptr (with the error recorded).
+void* noalloc_scratch(const char* fn) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    fail(LCSA_ERR_DEVICE, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    fail(LCSA_ERR_DEVICE, "%s: device %d beyond the %d the scratch table covers", fn, dev,
+         kMaxDevices);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      fail(LCSA_ERR_DEVICE, "%s: hipGetSymbolAddress(scratch): %s", fn, hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
 
 RingView make_view(const lcsa_kv_cache& c) {
   RingView v{};
@@ -335,20 +374,22 @@ lcsa_status lcsa_attn_bwd_workspace_size(const lcsa_geom* g, size_t* bytes_out) 
   return ok();
 }
 
-lcsa_status lcsa_block_sparse_attn_bwd(const lcsa_geom* g, const void* q, const void* k,
-                                       const void* v, const void* out, const void* dout,
-                                       const float* lse, const int32_t* sel_idx,
-                                       const int32_t* sel_cnt, int32_t kmax, float scale,
-                                       void* dq, void* dk, void* dv, void* workspace,
-                                       size_t workspace_bytes, void* stream) {
-  const char* fn = "lcsa_block_sparse_attn_bwd";
+// Validation and launch of the backward, shared by the entry point that
+// takes a caller workspace and the one that uses the library's scratch.
+// check_ws: whether workspace / workspace_bytes come from the caller.
+static lcsa_status attn_bwd(const lcsa_geom* g, const void* q, const void* k, const void* v,
+                            const void* out, const void* dout, const float* lse,
+                            const int32_t* sel_idx, const int32_t* sel_cnt, int32_t kmax,
+                            float scale, void* dq, void* dk, void* dv, void* workspace,
+                            size_t workspace_bytes, void* stream, const char* fn,
+                            bool check_ws) {
   lcsa_status st;
   if ((st = check_geom(g, fn)) || (st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) ||
       (st = check_ptr(v, "v")) || (st = check_ptr(out, "out")) ||
       (st = check_ptr(dout, "dout")) || (st = check_ptr(lse, "lse")) ||
       (st = check_ptr(sel_idx, "sel_idx")) || (st = check_ptr(sel_cnt, "sel_cnt")) ||
       (st = check_ptr(dq, "dq")) || (st = check_ptr(dk, "dk")) || (st = check_ptr(dv, "dv")) ||
-      (st = check_ptr(workspace, "workspace")))
+      (check_ws && (st = check_ptr(workspace, "workspace"))))
     return st;
   if (g->dtype != LCSA_BF16) return fail(LCSA_ERR_DTYPE, "%s: bf16 only", fn);
   if (kmax < 1) return fail(LCSA_ERR_CAPACITY, "kmax %d < 1", kmax);
@@ -359,13 +400,21 @@ lcsa_status lcsa_block_sparse_attn_bwd(const lcsa_geom* g, const void* q, const 
   if ((int64_t)(3 * (int64_t)g->width + 8) * g->heads * g->head_dim * 2 >= ((int64_t)1 << 31))
     return fail(LCSA_ERR_CAPACITY, "%s: token rows of %d x %d x %d are too wide", fn, g->width,
                 g->heads, g->head_dim);
-  if (reinterpret_cast<uintptr_t>(workspace) % 256)
-    return fail(LCSA_ERR_ALIGN, "%s: workspace is not 256-byte aligned", fn);
   const BwdLayout lay = bwd_layout(*g);
-  if (workspace_bytes < lay.total)
-    return fail(LCSA_ERR_CAPACITY, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes,
-                lay.total);
+  if (check_ws) {
+    if (reinterpret_cast<uintptr_t>(workspace) % 256)
+      return fail(LCSA_ERR_ALIGN, "%s: workspace is not 256-byte aligned", fn);
+    if (workspace_bytes < lay.total)
+      return fail(LCSA_ERR_CAPACITY, "%s: workspace of %zu bytes, %zu needed", fn,
+                  workspace_bytes, lay.total);
+  } else if (lay.total > workspace_bytes) {
+    return fail(LCSA_ERR_CAPACITY,
+                "%s: this chunk needs %zu bytes of scratch; the library's scratch holds %zu "
+                "(use lcsa_block_sparse_attn_bwd with a caller workspace)",
+                fn, lay.total, workspace_bytes);
+  }
   if (g->frames == 0) return ok();
+  if (!check_ws && !(workspace = noalloc_scratch(fn))) return LCSA_ERR_DEVICE;
   char* ws = (char*)workspace;
   BwdArgs a{};
   a.q = q;
@@ -391,6 +440,25 @@ lcsa_status lcsa_block_sparse_attn_bwd(const lcsa_geom* g, const void* q, const 
   a.kmax = kmax;
   a.scale = scale == 0.f ? 1.f / std::sqrt((float)g->head_dim) : scale;
   return device_status(launch_attn_bwd(a, (hipStream_t)stream), fn);
+}
+
+lcsa_status lcsa_block_sparse_attn_bwd(const lcsa_geom* g, const void* q, const void* k,
+                                       const void* v, const void* out, const void* dout,
+                                       const float* lse, const int32_t* sel_idx,
+                                       const int32_t* sel_cnt, int32_t kmax, float scale,
+                                       void* dq, void* dk, void* dv, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  return attn_bwd(g, q, k, v, out, dout, lse, sel_idx, sel_cnt, kmax, scale, dq, dk, dv,
+                  workspace, workspace_bytes, stream, "lcsa_block_sparse_attn_bwd", true);
+}
+
+lcsa_status lcsa_block_sparse_attn_bwd_noalloc(const lcsa_geom* g, const void* q, const void* k,
+                                               const void* v, const void* out, const void* dout,
+                                               const float* lse, const int32_t* sel_idx,
+                                               const int32_t* sel_cnt, int32_t kmax, float scale,
+                                               void* dq, void* dk, void* dv, void* stream) {
+  return attn_bwd(g, q, k, v, out, dout, lse, sel_idx, sel_cnt, kmax, scale, dq, dk, dv, nullptr,
+                  kNoAllocScratchBytes, stream, "lcsa_block_sparse_attn_bwd_noalloc", false);
 }
 
 lcsa_status lcsa_segment_max_list(const lcsa_geom* gq, const int32_t* frame_seg,

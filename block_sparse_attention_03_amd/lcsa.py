@@ -92,6 +92,9 @@ def load_library(path: str = LIB_PATH):
         "lcsa_block_sparse_attn_bwd": [G, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                        c_void_p, c_void_p, c_void_p, c_int32, c_float, c_void_p,
                                        c_void_p, c_void_p, c_void_p, ctypes.c_size_t, c_void_p],
+        "lcsa_block_sparse_attn_bwd_noalloc": [G, c_void_p, c_void_p, c_void_p, c_void_p,
+                                               c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
+                                               c_float, c_void_p, c_void_p, c_void_p, c_void_p],
         "lcsa_max_candidates": [G, c_int64, C, P, POINTER(c_int32)],
         "lcsa_local_lists": [G, c_int64, C, P, c_int32, c_void_p, c_void_p, c_void_p],
         "lcsa_segment_max_list": [G, POINTER(c_int32), POINTER(c_int32)],
@@ -278,6 +281,18 @@ def lcsa_block_sparse_attn_bwd(geom: Geom, q, k, v, out, dout, lse, sel_idx, sel
                                           _ptr(dout), _ptr(lse), _ptr(sel_idx), _ptr(sel_cnt),
                                           kmax, c_float(scale), _ptr(dq), _ptr(dk), _ptr(dv),
                                           _ptr(workspace), nbytes, _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 48 << 20  # LCSA_NOALLOC_SCRATCH_BYTES
+
+
+def lcsa_block_sparse_attn_bwd_noalloc(geom: Geom, q, k, v, out, dout, lse, sel_idx, sel_cnt,
+                                       kmax: int, dq, dk, dv, scale: float = 0.0, stream=None):
+    lib = load_library()
+    _check(lib.lcsa_block_sparse_attn_bwd_noalloc(ctypes.byref(geom), _ptr(q), _ptr(k), _ptr(v),
+                                                  _ptr(out), _ptr(dout), _ptr(lse), _ptr(sel_idx),
+                                                  _ptr(sel_cnt), kmax, c_float(scale), _ptr(dq),
+                                                  _ptr(dk), _ptr(dv), _stream(stream)))
 
 
 def _frame_seg(frame_seg):

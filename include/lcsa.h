@@ -31,8 +31,9 @@
  *
  * Conventions shared by every entry point:
  *   - All buffers are allocated and owned by the caller. The library never
- *     allocates or frees memory and keeps no global state except the
- *     thread-local text of the last error.
+ *     allocates or frees memory. Its only state is the thread-local text of
+ *     the last error and, for lcsa_block_sparse_attn_bwd_noalloc alone, a
+ *     fixed scratch array on each GPU (see there).
  *   - Device pointers must be 16-byte aligned (LCSA_ERR_ALIGN otherwise).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Device work is enqueued asynchronously; nothing synchronises.
@@ -351,6 +352,25 @@ lcsa_status lcsa_block_sparse_attn_bwd(const lcsa_geom* g, const void* q, const 
                                        const int32_t* sel_cnt, int32_t kmax, float scale,
                                        void* dq, void* dk, void* dv, void* workspace,
                                        size_t workspace_bytes, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * lcsa_block_sparse_attn_bwd with its workspace taken from a scratch array
+ * the library holds on each GPU for the life of the process
+ * (LCSA_NOALLOC_SCRATCH_BYTES per GPU), instead of a caller buffer. Same
+ * arguments, layouts, results and errors otherwise; a chunk whose workspace
+ * (lcsa_attn_bwd_workspace_size) exceeds the scratch is LCSA_ERR_CAPACITY,
+ * before any device work. The call allocates and frees nothing. Every call
+ * on one GPU shares that GPU's scratch: calls that overlap on one GPU (on
+ * concurrent streams, or from several threads) race and must be serialised
+ * by the caller. The scratch keeps the last call's contents; each call
+ * writes every byte it reads before reading it. */
+#define LCSA_NOALLOC_SCRATCH_BYTES ((size_t)48 << 20)
+lcsa_status lcsa_block_sparse_attn_bwd_noalloc(const lcsa_geom* g, const void* q, const void* k,
+                                               const void* v, const void* out, const void* dout,
+                                               const float* lse, const int32_t* sel_idx,
+                                               const int32_t* sel_cnt, int32_t kmax, float scale,
+                                               void* dq, void* dk, void* dv, void* stream);
 
 /* Text of the last error on this thread ("" after success). */
 const char* lcsa_last_error(void);

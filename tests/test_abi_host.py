@@ -345,3 +345,27 @@ def test_partition_requires_the_newest_tbs_in_order(lib):
     assert L.lcsa_kv_cache_append(c2, 1, 4) == 0
     expect(4, L.lcsa_partition_pool, one, ok, ok, ok, ok, ok, c2, 3, 0)
     expect(4, L.lcsa_partition_pool, two, ok, ok, ok, ok, ok, c2, 0, 0)
+
+
+def test_noalloc_backward_validation_before_any_device_call(lib):
+    """lcsa_block_sparse_attn_bwd_noalloc refuses a chunk whose workspace
+    exceeds the library's fixed scratch, and bad arguments, before any HIP
+    call (so these run without a GPU)."""
+    P = _P(FAKE)
+    big = L.make_geom(1, 12, 128, 24, 96, 160, L.LCSA_BF16)
+    assert L.lcsa_attn_bwd_workspace_size(big) > L.NOALLOC_SCRATCH_BYTES
+    msg = expect(6, L.lcsa_block_sparse_attn_bwd_noalloc, big, P, P, P, P, P, P, P, P, 4, P, P, P,
+                 stream=0)
+    assert "scratch" in msg
+    g = L.make_geom(1, 2, 128, 4, 16, 24, L.LCSA_BF16)
+    expect(1, L.lcsa_block_sparse_attn_bwd_noalloc, g, None, P, P, P, P, P, P, P, 4, P, P, P,
+           stream=0)
+    expect(3, L.lcsa_block_sparse_attn_bwd_noalloc, L.make_geom(1, 2, 128, 4, 16, 24, L.LCSA_F32),
+           P, P, P, P, P, P, P, P, 4, P, P, P, stream=0)
+    expect(6, L.lcsa_block_sparse_attn_bwd_noalloc, g, P, P, P, P, P, P, P, P, 0, P, P, P,
+           stream=0)
+    expect(5, L.lcsa_block_sparse_attn_bwd_noalloc, g, P, P, P, P, P, P, P, _P(FAKE + 4), 4, P, P,
+           P, stream=0)
+    # an empty chunk is a no-op (no scratch lookup, no device call)
+    L.lcsa_block_sparse_attn_bwd_noalloc(L.make_geom(1, 2, 128, 0, 16, 24, L.LCSA_BF16), P, P, P, P,
+                                         P, P, P, P, 4, P, P, P, stream=0)
