@@ -38,6 +38,19 @@ __device__ inline int xcd_task(int n_tasks) {
   return t < n_tasks ? t : -1;
 }
 
+// The view's ring slots, copied to LDS at kernel start. The keys of one
+// wave can lie in different temporal blocks, and a per-lane index into the
+// kernel-argument array compiles to a vector load from argument memory
+// followed by a wait on every outstanding load (which serialised the key
+// prefetch); a ds_read of this table costs neither. Needs a barrier before
+// the first read.
+__device__ inline void stage_slots(const RingView& v, int32_t* tab) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < LCSA_MAX_SLOTS; ++i)
+    if (tid == i) tab[i] = v.slot[i];
+}
+
 // Quotient of a small non-negative int by a divisor d >= 1 through an fp32
 // reciprocal, exact for n < 2^22: (n + 0.5) / d lies at least 0.5 / d from
 // an integer, and the two correctly rounded fp32 steps (1/d, then the
@@ -298,6 +311,8 @@ __global__ __launch_bounds__(64 * NW) void draft_mask_kernel(DraftArgs a) {
 
   const size_t bh = (size_t)b * a.NH + h;
   const int row0 = tq * nS + by * nbx + bx0;
+  __shared__ int32_t slot_tab[LCSA_MAX_SLOTS];
+  stage_slots(a.view, slot_tab);
   for (int i = tid; i < D * GX; i += 64 * NW) {
     const int d = i / GX, g = i % GX;
     qs[i] = g < ng ? a.q_pool[(bh * nq + row0 + g) * D + d] : 0.0;
@@ -310,7 +325,7 @@ __global__ __launch_bounds__(64 * NW) void draft_mask_kernel(DraftArgs a) {
     const int r2 = div_nux(u), ux = u - r2 * nux;
     const int p = div_ny(r2), yy = r2 - p * ny;
     const int x = uxlo + ux, y = ylo + yy;
-    const double* kp = a.kpool_ring + (bh * a.n_slots + a.view.slot[p]) * (size_t)D * nS +
+    const double* kp = a.kpool_ring + (bh * a.n_slots + slot_tab[p]) * (size_t)D * nS +
                        (size_t)y * nbx + x;
     double acc[GX];
 #pragma unroll
@@ -396,6 +411,8 @@ __global__ __launch_bounds__(64 * kTileWaves, 4) void draft_tile_kernel(DraftArg
   const int nuy = uyhi - uylo + 1, nux = uxhi - uxlo + 1;
   const int U = nvis * nuy * nux;
 
+  __shared__ int32_t slot_tab[LCSA_MAX_SLOTS];
+  stage_slots(a.view, slot_tab);
   // A operand: row rr of the tile is query block (by0 + rr/4, bx0 + rr%4),
   // staged d-major ([D][16]) so that the 16 rows of one k read 128
   // contiguous bytes (conflict-free); padding rows of an edge tile are 0
@@ -434,7 +451,7 @@ __global__ __launch_bounds__(64 * kTileWaves, 4) void draft_tile_kernel(DraftArg
     p = div_nuy(r2);
     y = uylo + r2 - p * nuy;
     x = uxlo + ux;
-    return a.kpool_ring + (bh * a.n_slots + a.view.slot[p]) * (size_t)D * nS + (size_t)y * nbx + x;
+    return a.kpool_ring + (bh * a.n_slots + slot_tab[p]) * (size_t)D * nS + (size_t)y * nbx + x;
   };
   // One half tile (16 of the 32 k-steps) of key loads in flight at a time;
   // the other resident workgroup covers their latency.
@@ -479,6 +496,514 @@ __global__ __launch_bounds__(64 * kTileWaves, 4) void draft_tile_kernel(DraftArg
     select_row(a, sc + (size_t)ro * a.row_stride, bh * nq + (size_t)tq * nS + qy * nbx + qx, nvis,
                ylo, yhi - ylo + 1, xlo, xhi, n_keys, hist, lane, sqrt((double)D));
   }
+}
+
+// ---- whole-grid windows ----------------------------------------------------
+// When the window covers the whole grid (FlashVSR+ global layers, small
+// grids under an 11x11 window), every query row of a temporal block has the
+// same candidates: all key blocks of the visible TBs, in id order. A
+// workgroup scores 16 consecutive rows of one TB against all of them on the
+// fp64 matrix cores (A = pooled queries held in registers, B = 16 keys of
+// the d-major pooled ring per product), so the pooled keys leave L2 once per
+// 16 rows. The scores are kept in LDS as float32 (16 rows of up to 2,304
+// candidates fit), and the selection stays exact on the float64 scores:
+// rounding to float32 is monotone, so a candidate whose float32 score is
+// above the k-th one has a larger float64 score as well, and only a tie of
+// float32 values at the k-th place can hide an order; the tied candidates'
+// float64 scores are then recomputed (one wave-wide dot product each) and
+// the same selection runs on them.
+constexpr int kDenseWaves = 8;               // 16 rows: two per wave in the selection
+constexpr int kDenseMaxCand = 2304;          // candidates per row held in LDS
+constexpr int kDenseMinCand = 1024;          // below this the row-group path is faster
+constexpr int kHistStride = 264;             // per-wave histogram / list, 8 spare entries
+
+// Order-preserving maps of float32 / float64 to unsigned integers.
+__device__ inline uint32_t ordered_key(float v) {
+  const uint32_t u = __float_as_uint(v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ inline uint64_t ordered_key(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  return (u >> 63) ? ~u : (u | (1ull << 63));
+}
+
+template <int CTRL, int ROWS>
+__device__ inline uint32_t dpp_keep32(uint32_t v) {  // lanes outside ROWS keep their value
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROWS, 0xF, false);
+}
+
+// Full-wave min / max of unsigned keys and floats (the same DPP steps as the
+// float64 reductions above; the result is read from lane 63).
+__device__ inline uint32_t wave_min_u(uint32_t v) {
+  v = min(v, dpp_keep32<0xB1, 0xF>(v));
+  v = min(v, dpp_keep32<0x4E, 0xF>(v));
+  v = min(v, dpp_keep32<0x141, 0xF>(v));
+  v = min(v, dpp_keep32<0x140, 0xF>(v));
+  v = min(v, dpp_keep32<0x142, 0xA>(v));
+  v = min(v, dpp_keep32<0x143, 0xC>(v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+__device__ inline uint32_t wave_max_u(uint32_t v) {
+  v = max(v, dpp_keep32<0xB1, 0xF>(v));
+  v = max(v, dpp_keep32<0x4E, 0xF>(v));
+  v = max(v, dpp_keep32<0x141, 0xF>(v));
+  v = max(v, dpp_keep32<0x140, 0xF>(v));
+  v = max(v, dpp_keep32<0x142, 0xA>(v));
+  v = max(v, dpp_keep32<0x143, 0xC>(v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+__device__ inline int wave_sum_i(int v) {
+  return __builtin_amdgcn_readlane((int)wave_prefix_sum_dpp((uint32_t)v), 63);
+}
+
+// Exact top-kr over the keys ks[lane + 64 m] (in LDS) of the slots m set in
+// `in`, restricted to [klo, khi]. On return the keys above khi are taken,
+// and of those in [klo, khi] (n_in of them) the first kr in candidate order;
+// either kr == n_in (all taken) or klo == khi (one value). Radix steps of 8
+// bits starting below the highest bit where the range's smallest and
+// largest keys differ, so the first histogram already spreads over the
+// occupied range; every step fixes at least 8 more bits.
+__device__ void narrow_range(const uint32_t* ks, int n, uint64_t in, uint32_t& klo, uint32_t& khi,
+                             int& kr, int& n_in, uint32_t* hist, int lane) {
+  n_in = 0;
+  for (int level = 0; level < 6; ++level) {
+    uint32_t mn = ~0u, mx = 0u;
+    int cnt = 0;
+    for (int m = 0; 64 * m < n; ++m) {
+      const uint32_t kv = ks[lane + 64 * m];
+      if (((in >> m) & 1u) && kv >= klo && kv <= khi) {
+        mn = min(mn, kv);
+        mx = max(mx, kv);
+        ++cnt;
+      }
+    }
+    mn = wave_min_u(mn);
+    mx = wave_max_u(mx);
+    cnt = wave_sum_i(cnt);
+    n_in = cnt;
+    if (cnt == 0) return;
+    klo = mn;
+    khi = mx;
+    if (cnt <= kr) {
+      kr = cnt;
+      return;
+    }
+    if (mn == mx) return;
+    const int top = 32 - __builtin_clz(mn ^ mx);
+    const int shift = top > 8 ? top - 8 : 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) hist[lane * 4 + q] = 0u;
+    wave_sync();
+    for (int m = 0; 64 * m < n; ++m) {
+      const uint32_t kv = ks[lane + 64 * m];
+      if (((in >> m) & 1u) && kv >= klo && kv <= khi)
+        atomicAdd(&hist[255 - (int)((kv >> shift) & 255u)], 1u);  // position 0: top digit
+    }
+    wave_sync();
+    uint32_t hb[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) hb[q] = hist[lane * 4 + q];
+    const uint32_t tot = hb[0] + hb[1] + hb[2] + hb[3];
+    uint32_t ab = wave_prefix_sum_dpp(tot) - tot;  // keys in higher digits
+    int found = -1;
+    uint32_t fa = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (found < 0 && ab < (uint32_t)kr && ab + hb[q] >= (uint32_t)kr) {
+        found = 255 - (lane * 4 + q);
+        fa = ab;
+      }
+      ab += hb[q];
+    }
+    const uint64_t bal = __ballot(found >= 0);
+    wave_sync();
+    if (bal == 0) return;  // unreachable: 1 <= kr < cnt
+    const int src = __ffsll((long long)bal) - 1;
+    const uint32_t digit = (uint32_t)__builtin_amdgcn_readlane(found, src);
+    kr -= __builtin_amdgcn_readlane((int)fa, src);
+    const uint32_t above = shift + 8 >= 32 ? 0u : (~0u << (shift + 8));
+    klo = (mn & above) | (digit << shift);
+    khi = klo | ((1u << shift) - 1u);
+  }
+}
+
+// float64 score of candidate c (key id) against the pooled query qrow, in
+// one fixed summation order.
+template <int D>
+__device__ inline double dense_score64(const DraftArgs& a, const int32_t* slot_tab,
+                                       const double* qrow, size_t bh, int nS,
+                                       const SmallDiv& div_ns, int c) {
+  const int p = div_ns(c), sp = c - p * nS;
+  const double* kp = a.kpool_ring + (bh * a.n_slots + slot_tab[p]) * (size_t)D * nS + sp;
+  double w = 0.0;
+#pragma unroll 4
+  for (int d = 0; d < D; ++d) w = fma(qrow[d], kp[(size_t)d * nS], w);
+  return w;
+}
+
+// One wave, general form: top-k and the sorted index list of query row `row`
+// from its n float32 scores in LDS (candidate index = key id), which the
+// selection overwrites with its 32-bit keys. It runs in stages: the float32 score,
+// then, only for candidates tied at the k-th place, the high and the low
+// half of the float64 score (recomputed from the pooled query qrow and the
+// pooled ring); candidates still tied after that are exact ties and go to
+// the lower id.
+template <int D>
+__device__ void select_dense_staged(const DraftArgs& a, const int32_t* slot_tab, float* s, int n,
+                                    size_t row, size_t bh, int nS, int64_t n_keys,
+                                    const double* qrow, uint32_t* hist, int lane) {
+  const int k = topk_dev(a, n, n_keys);
+  int32_t* out = a.sel_idx + row * a.kmax;
+  uint32_t* ks = reinterpret_cast<uint32_t*>(s);
+  uint64_t live = 0;  // bit m: slot m is still undecided (non-NaN candidate)
+  for (int m = 0; 64 * m < n; ++m) {
+    const int c = lane + 64 * m;
+    if (c < n) {
+      const float v = s[c];
+      ks[c] = ordered_key(v);
+      if (!__builtin_isnan(v)) live |= 1ull << m;
+    }
+  }
+  uint64_t taken = 0;  // bit m: slot m is selected
+  int kr = k;
+  const SmallDiv div_ns(nS);
+  for (int stage = 0; stage < 3 && kr > 0; ++stage) {
+    if (stage > 0) {  // the next finer key of the tied candidates
+      for (int m = 0; 64 * m < n; ++m) {
+        if ((live >> m) & 1u) {
+          const int c = lane + 64 * m;
+          const double w = dense_score64<D>(a, slot_tab, qrow, bh, nS, div_ns, c);
+          const uint64_t k64 = ordered_key(w);
+          ks[c] = stage == 1 ? (uint32_t)(k64 >> 32) : (uint32_t)k64;
+          if (__builtin_isnan(w)) live &= ~(1ull << m);
+        }
+      }
+    }
+    wave_sync();
+    uint32_t lo = 0, hi = ~0u;
+    int n_in = 0;
+    narrow_range(ks, n, live, lo, hi, kr, n_in, hist, lane);
+    uint64_t in_range = 0;
+    for (int m = 0; 64 * m < n; ++m) {
+      if ((live >> m) & 1u) {
+        const uint32_t kv = ks[lane + 64 * m];
+        if (kv > hi) taken |= 1ull << m;
+        else if (kv >= lo) in_range |= 1ull << m;
+      }
+    }
+    live = in_range;
+    if (n_in <= kr) {  // the whole range is kept
+      taken |= live;
+      live = 0;
+      kr = 0;
+    }
+  }
+  // Emit in ascending candidate order: the taken ones, then the first kr of
+  // the exact ties left in `live`.
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int eq_before = 0, sel_before = 0;
+  if (k > 0) {
+    for (int m = 0; 64 * m < n; ++m) {
+      const bool gt = (taken >> m) & 1u;
+      const bool eq = (live >> m) & 1u;
+      const uint64_t beq = __ballot(eq);
+      const int r = eq_before + __popcll(beq & lt_mask);
+      const bool want = gt || (eq && r < kr);
+      const int pos = sel_before + __popcll(__ballot(want) & lt_mask);
+      const bool sel = want && pos < k;  // never more than k
+      const uint64_t bsel = __ballot(sel);
+      if (sel) out[pos] = lane + 64 * m;
+      eq_before += __popcll(beq);
+      sel_before += __popcll(bsel);
+    }
+  }
+  for (int pos = sel_before + lane; pos < a.kmax; pos += 64) out[pos] = -1;
+  if (lane == 0) a.sel_cnt[row] = sel_before;
+}
+
+__device__ inline float wave_min_f32(float v) {
+  v = fminf(v, __uint_as_float(dpp_keep32<0xB1, 0xF>(__float_as_uint(v))));
+  v = fminf(v, __uint_as_float(dpp_keep32<0x4E, 0xF>(__float_as_uint(v))));
+  v = fminf(v, __uint_as_float(dpp_keep32<0x141, 0xF>(__float_as_uint(v))));
+  v = fminf(v, __uint_as_float(dpp_keep32<0x140, 0xF>(__float_as_uint(v))));
+  v = fminf(v, __uint_as_float(dpp_keep32<0x142, 0xA>(__float_as_uint(v))));
+  v = fminf(v, __uint_as_float(dpp_keep32<0x143, 0xC>(__float_as_uint(v))));
+  return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 63));
+}
+__device__ inline float wave_max_f32(float v) {
+  v = fmaxf(v, __uint_as_float(dpp_keep32<0xB1, 0xF>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_keep32<0x4E, 0xF>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_keep32<0x141, 0xF>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_keep32<0x140, 0xF>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_keep32<0x142, 0xA>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_keep32<0x143, 0xC>(__float_as_uint(v))));
+  return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 63));
+}
+
+constexpr int kDenseM = (kDenseMaxCand + 63) / 64;  // scores per lane in registers
+constexpr int kBoundaryMax = 256;                   // boundary-bin members ranked pairwise
+
+// One wave, usual case: the row's float32 scores in registers, one 256-bin
+// histogram over [min, max] (bins are a monotone function of the value),
+// every candidate in a bin above the k-th one's bin taken, and the members
+// of that boundary bin ranked pairwise (score descending, id ascending).
+// Falls back to select_dense_staged when the boundary bin is large or a
+// float32 tie straddles the k-th place (then the float64 scores decide).
+template <int D>
+__device__ void select_dense(const DraftArgs& a, const int32_t* slot_tab, float* s, int n,
+                             size_t row, size_t bh, int nS, int64_t n_keys, const double* qrow,
+                             uint32_t* hist, int lane) {
+  constexpr int M = kDenseM;
+  const int k = topk_dev(a, n, n_keys);
+  int32_t* out = a.sel_idx + row * a.kmax;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  float v[M];
+  uint64_t valid = 0;
+  float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const int c = lane + 64 * m;
+    v[m] = c < n ? s[c] : 0.f;
+    if (c < n && !__builtin_isnan(v[m])) {
+      valid |= 1ull << m;
+      mn = fminf(mn, v[m]);
+      mx = fmaxf(mx, v[m]);
+    }
+  }
+  mn = wave_min_f32(mn);
+  mx = wave_max_f32(mx);
+  const int n_valid = wave_sum_i(__popcll(valid));
+  bool general = false;
+  uint64_t taken = 0;
+  if (k > 0 && k < n_valid) {
+    const float scale = 256.f / (mx - mn);
+    general = !(mx > mn) || !(scale < INFINITY);  // one value, or a range beyond float32
+    int bstar = 0, kr = 0, cb = 0;
+    if (!general) {
+      auto bin_of = [&](float x) {
+        const int b = (int)((x - mn) * scale);
+        return b < 0 ? 0 : (b > 255 ? 255 : b);
+      };
+#pragma unroll
+      for (int q = 0; q < 4; ++q) hist[lane * 4 + q] = 0u;
+      wave_sync();
+      // position 0: the top bin; slots without a candidate count into
+      // spare entries past the histogram (no branch per slot)
+#pragma unroll
+      for (int m = 0; m < M; ++m)
+        atomicAdd(&hist[((valid >> m) & 1u) ? 255 - bin_of(v[m]) : 256 + (lane & 7)], 1u);
+      wave_sync();
+      uint32_t hb[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) hb[q] = hist[lane * 4 + q];
+      const uint32_t tot = hb[0] + hb[1] + hb[2] + hb[3];
+      uint32_t ab = wave_prefix_sum_dpp(tot) - tot;
+      int found = -1;
+      uint32_t fa = 0, fc = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (found < 0 && ab < (uint32_t)k && ab + hb[q] >= (uint32_t)k) {
+          found = 255 - (lane * 4 + q);
+          fa = ab;
+          fc = hb[q];
+        }
+        ab += hb[q];
+      }
+      const uint64_t bal = __ballot(found >= 0);
+      wave_sync();  // histogram read before it becomes the id list
+      const int src = bal ? __ffsll((long long)bal) - 1 : 0;
+      bstar = __builtin_amdgcn_readlane(found, src);
+      kr = k - __builtin_amdgcn_readlane((int)fa, src);
+      cb = __builtin_amdgcn_readlane((int)fc, src);
+      general = bal == 0 || cb > kBoundaryMax;
+      if (!general) {
+        // the boundary bin's members, in candidate order: scores over the
+        // row's LDS scores (held in registers now), ids over the histogram
+        uint32_t* ids = hist;
+        int base = 0;
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          const bool onv = (valid >> m) & 1u;
+          const int bn = bin_of(v[m]);
+          if (onv && bn > bstar) taken |= 1ull << m;
+          const bool inb = onv && bn == bstar;
+          const uint64_t bb = __ballot(inb);
+          // members go to their list position, the others to spare entries
+          // (past the row's candidates, past the list)
+          const int idx = base + __popcll(bb & lt_mask);
+          s[inb ? idx : n + (lane & 7)] = v[m];
+          ids[inb ? idx : 256 + (lane & 7)] = (uint32_t)(lane + 64 * m);
+          base += __popcll(bb);
+        }
+        wave_sync();
+        // rank of each member: larger scores, then equal scores of lower id
+        bool straddle = false;
+        for (int i = lane; i < cb; i += 64) {
+          const float vi = s[i];
+          const uint32_t ci = ids[i] & 0x7fffffffu;
+          int gt = 0, eq_lo = 0, eq = 0;
+          for (int j = 0; j < cb; ++j) {  // ids of earlier rounds may carry the taken flag
+            const float vj = s[j];
+            gt += vj > vi;
+            eq += vj == vi;
+            eq_lo += (vj == vi) & ((ids[j] & 0x7fffffffu) < ci);
+          }
+          // a float32 tie group [gt, gt + eq) cut by the k-th place
+          straddle |= gt < kr && gt + eq > kr;
+          if (gt + eq_lo < kr) ids[i] = ci | 0x80000000u;  // taken
+        }
+        general = __ballot(straddle) != 0;
+        wave_sync();
+        if (!general) {
+          base = 0;
+#pragma unroll
+          for (int m = 0; m < M; ++m) {
+            const bool inb = ((valid >> m) & 1u) && bin_of(v[m]) == bstar;
+            const uint64_t bb = __ballot(inb);
+            if (inb && (ids[base + __popcll(bb & lt_mask)] & 0x80000000u)) taken |= 1ull << m;
+            base += __popcll(bb);
+          }
+        }
+        wave_sync();
+      }
+    }
+    if (general) {
+      // restore the row's scores and settle it in stages
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const int c = lane + 64 * m;
+        if (c < n) s[c] = v[m];
+      }
+      wave_sync();
+      select_dense_staged<D>(a, slot_tab, s, n, row, bh, nS, n_keys, qrow, hist, lane);
+      return;
+    }
+  } else if (k > 0) {
+    taken = valid;  // every candidate kept
+  }
+  // emit in ascending candidate order
+  int sel_before = 0;
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const bool want = (taken >> m) & 1u;
+    const uint64_t bw = __ballot(want);
+    const int pos = sel_before + __popcll(bw & lt_mask);
+    if (want && pos < k) out[pos] = lane + 64 * m;
+    sel_before += __popcll(bw);
+  }
+  sel_before = sel_before < k ? sel_before : k;
+  for (int pos = sel_before + lane; pos < a.kmax; pos += 64) out[pos] = -1;
+  if (lane == 0) a.sel_cnt[row] = sel_before;
+}
+
+template <int D>
+__global__ __launch_bounds__(64 * kDenseWaves, 1) void draft_dense_kernel(DraftArgs a) {
+  constexpr int KS = D / 4;  // k-steps of one 16 x 16 x 4 product chain
+  extern __shared__ float dsm[];
+  const int rs = a.row_stride;  // >= candidates, = 16 (mod 64): conflict-free score writes
+  float* sc = dsm;              // [16][rs]
+  uint32_t* hist_all = reinterpret_cast<uint32_t*>(dsm + 16 * (size_t)rs);  // [waves][264]
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int nS = a.nby * a.nbx;
+  const int ngr = (nS + 15) / 16;
+  int task = xcd_task(a.B * a.NH * a.ntb_q * ngr);
+  if (task < 0) return;
+  const int gr = task % ngr;
+  task /= ngr;
+  const int tq = task % a.ntb_q;
+  task /= a.ntb_q;
+  const int h = task % a.NH;
+  const int b = task / a.NH;
+  const size_t bh = (size_t)b * a.NH + h;
+  const int64_t qtb = a.q_first_abs_tb + tq;
+  int nvis = 0;
+  for (int p = 0; p < a.view.n; ++p)
+    if (a.view.abs_tb[p] <= qtb) nvis = p + 1;
+  const int n = nvis * nS;
+  const int64_t n_keys = (int64_t)a.view.n * nS;
+  const int nq = a.ntb_q * nS;
+  const int s0 = 16 * gr;
+  const int nrows = min(16, nS - s0);
+  const size_t row0 = bh * nq + (size_t)tq * nS + s0;
+
+  // lane (r, dq) holds A[r][4 s2 + dq] and B[4 s2 + dq][r] of k-step s2 and
+  // outputs D[4 j + dq][r]: query row 4 j + dq against key 16 t + r
+  const int r = lane & 15, dq = lane >> 4;
+  double qa[KS];
+#pragma unroll
+  for (int s2 = 0; s2 < KS; ++s2)
+    qa[s2] = r < nrows ? a.q_pool[(row0 + r) * D + 4 * s2 + dq] : 0.0;
+
+  __shared__ int32_t slot_tab[LCSA_MAX_SLOTS];
+  stage_slots(a.view, slot_tab);
+  __syncthreads();
+  const SmallDiv div_ns(nS);
+  const int ntiles = (n + 15) / 16;
+  // key u of tile t; u >= n reads key 0 (a valid address) and is never stored
+  auto key_col = [&](int t) {
+    int u = 16 * t + r;
+    u = u < n ? u : 0;
+    const int p = div_ns(u), sp = u - p * nS;
+    return a.kpool_ring + (bh * a.n_slots + slot_tab[p]) * (size_t)D * nS + sp +
+           (size_t)dq * nS;
+  };
+  // Two register buffers of B in turn: the next tile's keys are in flight
+  // while this tile's products run.
+  auto load_tile = [&](int t, double (&b)[KS]) {
+    if (t < ntiles) {
+      const double* kp = key_col(t);
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2) b[s2] = kp[(size_t)4 * s2 * nS];
+    }
+  };
+  auto score_tile = [&](int t, const double (&b)[KS]) {
+    if (t < ntiles) {
+      f64x4 acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int s2 = 0; s2 < KS; s2 += 2) {
+        acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[s2], b[s2], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[s2 + 1], b[s2 + 1], acc1, 0, 0, 0);
+      }
+      const int u = 16 * t + r;
+      if (u < n) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          sc[(size_t)(4 * j + dq) * rs + u] = (float)(acc0[j] + acc1[j]);
+      }
+    }
+  };
+  double b0[KS], b1[KS];
+  load_tile(wave, b0);
+  for (int t = wave; t < ntiles; t += 2 * kDenseWaves) {
+    load_tile(t + kDenseWaves, b1);
+    score_tile(t, b0);
+    load_tile(t + 2 * kDenseWaves, b0);
+    score_tile(t + kDenseWaves, b1);
+  }
+  __syncthreads();
+
+  for (int ro = wave; ro < nrows; ro += kDenseWaves)
+    select_dense<D>(a, slot_tab, sc + (size_t)ro * rs, n, row0 + ro, bh, nS, n_keys,
+                    a.q_pool + (row0 + ro) * D, hist_all + wave * kHistStride, lane);
+}
+
+template <int D>
+hipError_t launch_dense(DraftArgs a, hipStream_t s) {
+  const int nS = a.nby * a.nbx;
+  const long long n_max = (long long)a.view.n * nS;
+  a.row_stride = (int32_t)((n_max + 63) / 64 * 64 + 16);
+  const long long tasks = (long long)a.B * a.NH * a.ntb_q * ((nS + 15) / 16);
+  const long long wgs = 8 * ((tasks + 7) / 8);
+  const size_t shmem = 16 * (size_t)a.row_stride * sizeof(float) + kDenseWaves * kHistStride * 4;
+  if (shmem > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute((const void*)draft_dense_kernel<D>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(draft_dense_kernel<D>, dim3((unsigned)wgs), dim3(64 * kDenseWaves), shmem, s,
+                     a);
+  return hipGetLastError();
 }
 
 template <int D>
@@ -545,6 +1070,19 @@ hipError_t launch_draft_mask(const DraftArgs& a, hipStream_t s) {
   // same candidates and few tiles; there the row-group path's many small
   // workgroups fill the chip better (768x1408 step: 24 vs 33 us; a 12-TB
   // chunk of the same grid has 864 tiles and keeps the tile path).
+  // A window covering the whole grid gives every row of a temporal block
+  // all visible keys: one dense score matrix per TB, scored 16 rows at a
+  // time. It pays from about a thousand candidates per row (FlashVSR+ global
+  // layer at 4K, 2,040: 434 -> 244 us), where the row groups' re-reads of
+  // the pooled keys dominate; below that the row-group path's many small
+  // workgroups win (768x1408 step, 264 candidates: 25 vs 44 us). The draft's
+  // float64 probabilities come from the paths below.
+  const bool whole_grid = a.border == 0
+                              ? (a.nby <= a.local_range && a.nbx <= a.local_range)
+                              : (a.local_range / 2 >= a.nby - 1 && a.local_range / 2 >= a.nbx - 1);
+  const long long n_max = (long long)a.view.n * a.nby * a.nbx;
+  if (!a.probs && whole_grid && n_max >= kDenseMinCand && n_max <= kDenseMaxCand)
+    return a.D == 64 ? launch_dense<64>(a, s) : launch_dense<128>(a, s);
   const bool window_inside = a.local_range < a.nby || a.local_range < a.nbx;
   const long long tiles =
       (long long)a.B * a.NH * a.ntb_q * ((a.nby + 3) / 4) * ((a.nbx + 3) / 4);

@@ -225,3 +225,140 @@ def test_corrupted_index_fails_the_check(dev):
     assert_close(got, o_good, w.dtype)
     with pytest.raises(AssertionError):
         assert_close(got, o_bad, w.dtype)
+
+
+# ------------------------------------------------------- whole-grid windows
+# A window covering the whole grid gives every row of a temporal block the
+# same candidates. Without the probabilities output, rows of up to about a
+# thousand candidates take the row-group path; larger ones (FlashVSR+ global
+# layers) the dense path: 16 rows per workgroup on the fp64 matrix cores,
+# float32 scores in LDS, a tie at the k-th place settled on recomputed
+# float64 scores. Every row's selection is checked in each case.
+
+@pytest.mark.parametrize("case", [
+    dict(local_range=99),                                     # 2 query TBs, ragged 5x7 grid
+    dict(local_range=99, border=1),
+    dict(local_range=99, head_dim=64),
+    dict(local_range=99, batch=2, heads=3),
+    dict(local_range=99, ratio=(1, 1)),                       # k = every candidate
+    dict(local_range=99, topk_fixed=1),
+    dict(local_range=99, ratio=(1, 5), ratio_base=1, frames=6),
+    dict(local_range=99, dtype="f32"),
+    dict(height=8, width=8, frames=6, topk_fixed=2, local_range=99),  # 1x1 block grid
+])
+def test_whole_grid_draft_all_rows(dev, case):
+    w = small(**case)
+    st = Stream(w, dev)
+    g, ref = st.step(want_probs=False)
+    stats = compare_step(w, g, ref)
+    say(f"whole grid {case}: {stats}")
+
+
+def dense(**kw) -> Workload:
+    """12 x 16 blocks per TB and 6 TBs in view: 1,152 candidates per row."""
+    base = dict(height=96, width=128, frames=2, cache_frames=10, cap_tb=5, local_range=99,
+                ratio=(1, 16))
+    base.update(kw)
+    return small(**base)
+
+
+@pytest.mark.parametrize("case", [
+    dict(),
+    dict(border=1),
+    dict(head_dim=64),
+    dict(ratio=(1, 1)),                                       # k = every candidate
+    dict(topk_fixed=1),
+    dict(frames=4, cache_frames=8),                           # 2 query TBs: 1,152 and 960
+])
+def test_dense_draft_path(dev, case):
+    """Selections on every row, outputs on sampled rows."""
+    w = dense(**case)
+    st = Stream(w, dev)
+    rows = sample_rows(w, 4)
+    g, ref = st.step(rows=rows, want_probs=False)
+    stats = compare_step(w, g, ref, rows=rows)
+    say(f"dense draft {case}: {stats}")
+
+
+def test_dense_draft_equal_scores_take_lowest_ids(dev):
+    """q = 0: every score is 0, so every candidate is tied in float32 and in
+    float64 and the k lowest ids are kept."""
+    w = dense(ratio=(1, 3))
+    st = Stream(w, dev, zero_q=True)
+    rows = sample_rows(w, 2)
+    g, ref = st.step(rows=rows, want_probs=False)
+    for h in range(w.heads):
+        for i in range(w.nq):
+            k = int(ref.kcount[i])
+            cand = np.nonzero(np.isfinite(ref.scores[0, h, i]))[0][:k]
+            assert list(g["sel_idx"][0, h, i, :k]) == list(cand)
+    compare_step(w, g, ref, rows=rows)
+
+
+def test_dense_draft_float32_ties_resolved_in_float64(dev):
+    """Scores 1 + j * 2^-27 (exact in float64): groups of 16 consecutive j
+    round to one float32 value and share the high half of their float64
+    key, so the k-th place falls inside a float32 tie and is settled by the
+    low half of the float64 score; a few blocks share j exactly at the
+    boundary and go to the lower id. Selections must equal the oracle's
+    exactly (no tie allowance)."""
+    NH, D, H, W = 2, 64, 144, 160
+    nby, nbx = H // 8, W // 8
+    nS = nby * nbx
+    n = 3 * nS                                   # 3 TBs of candidates, 1,080 keys
+    rng = np.random.default_rng(5)
+    k_tok = np.zeros((1, 6, H, W, NH, D))
+    k_tok[..., 0] = 1.0                          # pooled channel 0 = 1
+    q_tok = np.zeros((1, 2, H, W, NH, D))
+    q_tok[..., 0:3] = 1.0
+    p = O.SelectParams(local_range=99, ratio_num=1, ratio_den=3)
+    k = O.topk_count(n, n, p)                    # 360
+    for h in range(NH):
+        j = rng.permutation(n)
+        boundary = n - k                         # the k-th largest j
+        dup = rng.choice(np.nonzero(j < boundary - 20)[0], size=3, replace=False)
+        j[dup] = boundary                        # exact float64 ties at the k-th place
+        for key in range(n):
+            tb, s = divmod(key, nS)
+            by, bx = divmod(s, nbx)
+            # one token of the block carries j = 256 a + b as a * 2^-12 and
+            # b * 2^-20 (each exact in bf16): its block means add to j * 2^-27
+            a_, b_ = divmod(int(j[key]), 256)
+            k_tok[0, 2 * tb, 8 * by, 8 * bx, h, 1] = a_ * 2.0 ** -12
+            k_tok[0, 2 * tb, 8 * by, 8 * bx, h, 2] = b_ * 2.0 ** -20
+    v_tok = rng.standard_normal((1, 6, H, W, NH, D))
+    bits = {n_: synth.round_bf16_bits(x) for n_, x in (("q", q_tok), ("k", k_tok), ("v", v_tok))}
+    for n_, x in (("q", q_tok), ("k", k_tok)):
+        assert np.array_equal(synth.bf16_bits_to_f64(bits[n_]), x)
+    dv = {n_: to_dev(b, "bf16", dev) for n_, b in bits.items()}
+
+    cache = L.KVCache(1, NH, D, H, W, torch.bfloat16, 3, device=dev)
+    g4 = L.make_geom(1, NH, D, 4, H, W, L.LCSA_BF16)
+    L.lcsa_partition_pool(g4, None, dv["k"][:, :4].contiguous(), dv["v"][:, :4].contiguous(), None,
+                          None, cache.c, cache.append(2, 0))
+    g2 = L.make_geom(1, NH, D, 2, H, W, L.LCSA_BF16)
+    bufs = L.StepBuffers(g2, k, device=dev)
+    L.lcsa_partition_pool(g2, dv["q"], dv["k"][:, 4:].contiguous(), dv["v"][:, 4:].contiguous(), None,
+                          bufs.q_pool, cache.c, cache.append(1, 2))
+    L.lcsa_draft_mask(g2, bufs.q_pool, 2, cache.c, L.make_params(local_range=99, ratio=(1, 3)), k,
+                      bufs.sel_idx, bufs.sel_cnt)
+    torch.cuda.synchronize()
+    sel = bufs.sel_idx.cpu().numpy()
+    cnt = bufs.sel_cnt.cpu().numpy()
+
+    pq = O.pool(O.partition(q_tok))[0]         # [NH][nS][D]
+    pk = O.pool(O.partition(k_tok))[0]         # [NH][3 nS][D]
+    allowed = O.allowed_mask([2], [0, 1, 2], nby, nbx, p)
+    for h in range(NH):
+        s = O.draft_scores(pq[h], pk[h], allowed)
+        ref_sel, ks = O.select_topk(s, p)
+        assert set(int(x) for x in ks) == {k}
+        # the construction: at the k-th place the raw scores tie in float32
+        # over distinct float64 values, and exactly as well
+        raw = np.sort(pq[h, 0] @ pk[h].T)[::-1]
+        assert np.float32(raw[k - 5]) == np.float32(raw[k - 1]) and raw[k - 5] > raw[k - 1]
+        assert raw[k - 1] == raw[k]
+        for i in range(nS):
+            assert cnt[0, h, i] == k
+            assert list(sel[0, h, i, :k]) == list(ref_sel[i]), (h, i)
+    say(f"float32 ties settled in float64: {NH} heads x {nS} rows, k {k} of {n}")

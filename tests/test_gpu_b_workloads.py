@@ -73,14 +73,18 @@ def test_tiny_fp32_all_rows(dev):
     say(f"tiny: {stats}")
 
 
-def test_cold_start_768x1408_every_row(dev):
+@pytest.mark.parametrize("want_probs", [True, False], ids=["with-probs", "whole-grid-path"])
+def test_cold_start_768x1408_every_row(dev, want_probs):
+    """The 11x11 window covers the 6x11 block grid. With the probabilities
+    output the draft scores row groups on the vector ALU; without it, the
+    whole-grid path (16 rows per workgroup on the fp64 matrix cores)."""
     w = WORKLOADS["cold_768x1408"]
     st = Stream(w, dev)
-    g, ref = st.step()
+    g, ref = st.step(want_probs=want_probs)
     assert sorted(set(int(x) for x in ref.kcount)) == [13, 26, 39]
     stats = compare_step(w, g, ref)
     assert stats["rows"] == w.heads * w.nq
-    say(f"cold 768x1408, every row of 12 heads: {stats}")
+    say(f"cold 768x1408 ({'probs' if want_probs else 'no probs'}), every row of 12 heads: {stats}")
 
 
 def test_streaming_step_768x1408_every_row(dev):
