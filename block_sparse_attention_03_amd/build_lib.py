@@ -46,8 +46,17 @@ def _run(cmd):
 EXTRA = {"sparse_attn.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 
 
+def _clear_stale_objects() -> None:
+    """Remove build objects whose source is no longer part of the library."""
+    keep = {s + ".o" for s in HIP_SOURCES + CXX_SOURCES}
+    for name in os.listdir(BUILD):
+        if name.endswith(".o") and name not in keep:
+            os.remove(os.path.join(BUILD, name))
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
+    _clear_stale_objects()
     jobs = []
     for s in HIP_SOURCES:
         obj = os.path.join(BUILD, s + ".o")

@@ -949,37 +949,37 @@ __global__ __launch_bounds__(64 * kDenseWaves, 1) void draft_dense_kernel(DraftA
            (size_t)dq * nS;
   };
   // Two register buffers of B in turn: the next tile's keys are in flight
-  // while this tile's products run.
+  // while this tile's products run. The loads are unconditional (a tile past
+  // the last reads key 0 and is never stored): a load under a branch leaves
+  // the compiler's wait counts conservative, and each product would then
+  // wait for the next tile's loads issued just before it.
   auto load_tile = [&](int t, double (&b)[KS]) {
-    if (t < ntiles) {
-      const double* kp = key_col(t);
+    const double* kp = key_col(t);
 #pragma unroll
-      for (int s2 = 0; s2 < KS; ++s2) b[s2] = kp[(size_t)4 * s2 * nS];
-    }
+    for (int s2 = 0; s2 < KS; ++s2) b[s2] = kp[(size_t)4 * s2 * nS];
   };
   auto score_tile = [&](int t, const double (&b)[KS]) {
-    if (t < ntiles) {
-      f64x4 acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = {0.0, 0.0, 0.0, 0.0};
+    f64x4 acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-      for (int s2 = 0; s2 < KS; s2 += 2) {
-        acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[s2], b[s2], acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[s2 + 1], b[s2 + 1], acc1, 0, 0, 0);
-      }
-      const int u = 16 * t + r;
-      if (u < n) {
+    for (int s2 = 0; s2 < KS; s2 += 2) {
+      acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[s2], b[s2], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[s2 + 1], b[s2 + 1], acc1, 0, 0, 0);
+    }
+    const int u = 16 * t + r;
+    if (t < ntiles && u < n) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          sc[(size_t)(4 * j + dq) * rs + u] = (float)(acc0[j] + acc1[j]);
-      }
+      for (int j = 0; j < 4; ++j) sc[(size_t)(4 * j + dq) * rs + u] = (float)(acc0[j] + acc1[j]);
     }
   };
   double b0[KS], b1[KS];
-  load_tile(wave, b0);
-  for (int t = wave; t < ntiles; t += 2 * kDenseWaves) {
-    load_tile(t + kDenseWaves, b1);
-    score_tile(t, b0);
-    load_tile(t + 2 * kDenseWaves, b0);
-    score_tile(t + kDenseWaves, b1);
+  if (wave < ntiles) {  // uniform per wave
+    load_tile(wave, b0);
+    for (int t = wave; t < ntiles; t += 2 * kDenseWaves) {
+      load_tile(t + kDenseWaves, b1);
+      score_tile(t, b0);
+      load_tile(t + 2 * kDenseWaves, b0);
+      score_tile(t + kDenseWaves, b1);
+    }
   }
   __syncthreads();
 
