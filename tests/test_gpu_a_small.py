@@ -295,13 +295,16 @@ def test_dense_draft_equal_scores_take_lowest_ids(dev):
     compare_step(w, g, ref, rows=rows)
 
 
-def test_dense_draft_float32_ties_resolved_in_float64(dev):
+@pytest.mark.parametrize("outliers", [False, True], ids=["tie", "tie-in-a-full-bin"])
+def test_dense_draft_float32_ties_resolved_in_float64(dev, outliers):
     """Scores 1 + j * 2^-27 (exact in float64): groups of 16 consecutive j
     round to one float32 value and share the high half of their float64
     key, so the k-th place falls inside a float32 tie and is settled by the
     low half of the float64 score; a few blocks share j exactly at the
-    boundary and go to the lower id. Selections must equal the oracle's
-    exactly (no tie allowance)."""
+    boundary and go to the lower id. With `outliers`, two blocks score about
+    +8.8 and -5, so every other score falls into one of the 256 histogram
+    bins (far more than the pairwise rank takes) and the staged selection
+    decides. Selections must equal the oracle's exactly (no tie allowance)."""
     NH, D, H, W = 2, 64, 144, 160
     nby, nbx = H // 8, W // 8
     nS = nby * nbx
@@ -310,12 +313,13 @@ def test_dense_draft_float32_ties_resolved_in_float64(dev):
     k_tok = np.zeros((1, 6, H, W, NH, D))
     k_tok[..., 0] = 1.0                          # pooled channel 0 = 1
     q_tok = np.zeros((1, 2, H, W, NH, D))
-    q_tok[..., 0:3] = 1.0
+    q_tok[..., 0:4 if outliers else 3] = 1.0
     p = O.SelectParams(local_range=99, ratio_num=1, ratio_den=3)
     k = O.topk_count(n, n, p)                    # 360
     for h in range(NH):
         j = rng.permutation(n)
-        boundary = n - k                         # the k-th largest j
+        # the k-th largest j (one place lower with the +8 outlier on top)
+        boundary = n - k + (1 if outliers else 0)
         dup = rng.choice(np.nonzero(j < boundary - 20)[0], size=3, replace=False)
         j[dup] = boundary                        # exact float64 ties at the k-th place
         for key in range(n):
@@ -326,6 +330,12 @@ def test_dense_draft_float32_ties_resolved_in_float64(dev):
             a_, b_ = divmod(int(j[key]), 256)
             k_tok[0, 2 * tb, 8 * by, 8 * bx, h, 1] = a_ * 2.0 ** -12
             k_tok[0, 2 * tb, 8 * by, 8 * bx, h, 2] = b_ * 2.0 ** -20
+        if outliers:  # channel 3: +1000 / -768 in one token of two blocks far below the top
+            lo_keys = np.nonzero(j < boundary - 40)[0][:2]
+            for key, val in zip(lo_keys, (1000.0, -768.0)):
+                tb, s_ = divmod(int(key), nS)
+                by, bx = divmod(s_, nbx)
+                k_tok[0, 2 * tb, 8 * by, 8 * bx, h, 3] = val
     v_tok = rng.standard_normal((1, 6, H, W, NH, D))
     bits = {n_: synth.round_bf16_bits(x) for n_, x in (("q", q_tok), ("k", k_tok), ("v", v_tok))}
     for n_, x in (("q", q_tok), ("k", k_tok)):
@@ -358,6 +368,12 @@ def test_dense_draft_float32_ties_resolved_in_float64(dev):
         raw = np.sort(pq[h, 0] @ pk[h].T)[::-1]
         assert np.float32(raw[k - 5]) == np.float32(raw[k - 1]) and raw[k - 5] > raw[k - 1]
         assert raw[k - 1] == raw[k]
+        if outliers:
+            assert raw[0] > 7 and raw[-1] < -4.9 and raw[1] < 1.001
+            # one 256-bin histogram over [-5, 8.8]: bins of ~0.054, every score
+            # in [1, 1 + 2^-16) in one bin
+            width = (raw[0] - raw[-1]) / 256
+            assert int((raw[1] - raw[-1]) / width) == int((raw[-2] - raw[-1]) / width)
         for i in range(nS):
             assert cnt[0, h, i] == k
             assert list(sel[0, h, i, :k]) == list(ref_sel[i]), (h, i)
