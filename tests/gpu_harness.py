@@ -164,20 +164,24 @@ def compare_step(w, g, ref, rows="all", check_probs=True):
     lg, lw = np.stack(lse_g), np.stack(lse_w)
     fin = np.isfinite(lw)
     assert np.array_equal(np.isfinite(lg), fin)
+    lse_err = lse_tol = None
     if fin.any():
-        # lse bound: rounding each probability (bf16 on the matrix-core path)
-        # moves ln(sum) by at most that unit roundoff; a float32 logit of D
-        # exact products is within gamma_D * |q| |k| * scale of the exact one
-        # (u = 2^-23 on the matrix cores: the bound for truncating as well as
-        # round-to-nearest accumulation; 2^-24 for the fp32 path's IEEE fma)
-        # and lse is 1-Lipschitz in the logits; float32 rounding of the
-        # result adds a few ulps of |lse|.
+        # lse bound: rounding each probability (bf16 on the matrix-core
+        # path, unit roundoff 2^-8: an 8-bit significand) moves ln(sum) by at
+        # most ln(1 + u) < u; a float32 logit of D exact products is within
+        # gamma_D * |q| |k| * scale of the exact one (the matrix cores add a
+        # 16-product step to the accumulator with one round-to-nearest-even,
+        # so D roundings of unit 2^-24 overcount theirs, as for IEEE fma) and
+        # lse is 1-Lipschitz in the logits; float32 rounding of the result
+        # adds a few ulps of |lse|.
         D = w.head_dim
-        u = 2.0 ** -23 if w.dtype == "bf16" else 2.0 ** -24
+        u = 2.0 ** -24
         gamma = D * u / (1 - D * u)
         qn = np.sqrt((ref.q_blocks ** 2).sum(-1)).max()
         kn = np.sqrt((kb ** 2).sum(-1)).max()
-        tol = ((2.0 ** -9 if w.dtype == "bf16" else 1e-5) + gamma * qn * kn / math.sqrt(D)
+        tol = ((2.0 ** -8 if w.dtype == "bf16" else 1e-5) + gamma * qn * kn / math.sqrt(D)
                + 8 * 2.0 ** -24 * max(1.0, float(np.abs(lw[fin]).max())))
-        assert np.abs(lg[fin] - lw[fin]).max() <= tol, (np.abs(lg[fin] - lw[fin]).max(), tol)
-    return {"tied": tied, "max_abs": amax, "rel_l2": rel, "rows": len(rows)}
+        lse_err, lse_tol = float(np.abs(lg[fin] - lw[fin]).max()), float(tol)
+        assert lse_err <= tol, (lse_err, tol)
+    return {"tied": tied, "max_abs": amax, "rel_l2": rel, "rows": len(rows),
+            "lse_err": lse_err, "lse_tol": lse_tol}

@@ -9,10 +9,11 @@ and at the full 768x1280 training shape the dq of sampled query blocks and
 the dk / dv of sampled key blocks (the oracle then computes every row that
 selects them).
 
-Tolerance: P and dS enter the matrix cores as bf16 (2^-9 relative each),
-and delta = rowsum(dout * O) uses the bf16 forward output. dk and dv are
-sums of such terms, so their rel-L2 error is a small multiple of 2^-9:
-bound 1e-2. dq = scale * dS K, and every row of dS sums to zero, so dq is a
+Tolerance: P and dS enter the matrix cores as bf16 (at most 2^-8 relative
+each: the unit roundoff of an 8-bit significand), and delta =
+rowsum(dout * O) uses the bf16 forward output. dk and dv are sums of such
+terms whose independent roundings average out, so their rel-L2 error stays
+a fraction of 2^-8: bound 1e-2. dq = scale * dS K, and every row of dS sums to zero, so dq is a
 difference of terms several times larger than itself while the rounding
 errors scale with the terms: bound rel-L2 3e-2 for dq. All three:
 max-abs <= 2e-2 * max(1, max |ref|).
