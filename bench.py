@@ -44,6 +44,9 @@ def parse():
                     help="have the partition write the query blocks (q_blk) and the attention "
                          "read q from them, instead of reading q in token layout (measured "
                          "slower: q_blk is an extra write and read of the whole of q)")
+    ap.add_argument("--no-draft-workspace", action="store_true",
+                    help="give the draft no workspace: its whole-grid windows then run the "
+                         "fused scoring and selection kernel instead of the split pair")
     ap.add_argument("--cpu-sample-heads", type=int, default=12)
     ap.add_argument("--cpu-sample-steps", type=int, default=4)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -154,6 +157,11 @@ def main():
                 self.kmax = L.lcsa_max_topk(geom, tb_first, probe, self.params)
             self.bufs = L.StepBuffers(geom, self.kmax, device=dev, with_lse=sp.backward,
                                       with_q_blk=args.q_blocks)
+            # the draft's workspace (its split path at the whole-grid windows
+            # of about a thousand candidates and more; 0 bytes elsewhere)
+            nb = 0 if (self.seg or sp.lists == "local" or args.no_draft_workspace) else \
+                L.lcsa_draft_workspace_size(geom, self.cache.c, self.params)
+            self.dws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
             self.keep = sp.cap_tb if sp.cache_frames else 0  # cold chunks: empty after each step
             if sp.backward:  # training shape: the keys are the chunk's own blocks
                 assert sp.cache_frames == 0 and not self.seg
@@ -180,7 +188,7 @@ def main():
                                    stream)
             else:
                 L.lcsa_draft_mask(geom, b.q_pool, tb, c.c, self.params, self.kmax, b.sel_idx,
-                                  b.sel_cnt, None, stream)
+                                  b.sel_cnt, None, stream, workspace=self.dws)
             if ev is not None:
                 ev[0].record(stream)
             if self.seg and b.q_blk is not None:

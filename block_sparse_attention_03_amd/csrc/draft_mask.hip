@@ -749,21 +749,22 @@ constexpr int kBoundaryMax = 256;                   // boundary-bin members rank
 // of that boundary bin ranked pairwise (score descending, id ascending).
 // Falls back to select_dense_staged when the boundary bin is large or a
 // float32 tie straddles the k-th place (then the float64 scores decide).
+// v[m]: the score of candidate lane + 64 m (any value past n); s: this
+// wave's LDS row of at least n + 8 floats, scratch for the boundary list and
+// the staged selection.
 template <int D>
-__device__ void select_dense(const DraftArgs& a, const int32_t* slot_tab, float* s, int n,
-                             size_t row, size_t bh, int nS, int64_t n_keys, const double* qrow,
-                             uint32_t* hist, int lane) {
+__device__ void select_dense(const DraftArgs& a, const int32_t* slot_tab, float* s,
+                             const float (&v)[kDenseM], int n, size_t row, size_t bh, int nS,
+                             int64_t n_keys, const double* qrow, uint32_t* hist, int lane) {
   constexpr int M = kDenseM;
   const int k = topk_dev(a, n, n_keys);
   int32_t* out = a.sel_idx + row * a.kmax;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  float v[M];
   uint64_t valid = 0;
   float mn = INFINITY, mx = -INFINITY;
 #pragma unroll
   for (int m = 0; m < M; ++m) {
     const int c = lane + 64 * m;
-    v[m] = c < n ? s[c] : 0.f;
     if (c < n && !__builtin_isnan(v[m])) {
       valid |= 1ull << m;
       mn = fminf(mn, v[m]);
@@ -896,6 +897,172 @@ __device__ void select_dense(const DraftArgs& a, const int32_t* slot_tab, float*
   if (lane == 0) a.sel_cnt[row] = sel_before;
 }
 
+// One wave, split path: the same selection as select_dense, over the row's
+// float32 scores in the workspace (src, ws_stride floats). Lane l holds the
+// candidates [l M, l M + M) (M = ws_stride / 64: a multiple of four, at
+// most kDenseM), so a per-lane count and one prefix sum over the lanes give
+// every list position in candidate order: the boundary bin's members and
+// the emitted ids go straight to their places, with no pass of ballots over
+// the slots.
+template <int D>
+__device__ void select_split(const DraftArgs& a, const int32_t* slot_tab, const float* src,
+                             float* s, int n, size_t row, size_t bh, int nS, int64_t n_keys,
+                             const double* qrow, uint32_t* hist, int lane) {
+  constexpr int MX = kDenseM;
+  const int M = a.ws_stride >> 6;
+  const int cbase = lane * M;
+  const int k = topk_dev(a, n, n_keys);
+  int32_t* out = a.sel_idx + row * a.kmax;
+  // every load issued before the first wait; a slot past this lane's M
+  // reads the row's first four scores and is never used
+  float v[MX];
+#pragma unroll
+  for (int i = 0; i < MX / 4; ++i) {
+    const float4 x = *reinterpret_cast<const float4*>(src + (4 * i < M ? cbase + 4 * i : 0));
+    v[4 * i] = x.x;
+    v[4 * i + 1] = x.y;
+    v[4 * i + 2] = x.z;
+    v[4 * i + 3] = x.w;
+  }
+  uint64_t valid = 0;
+  float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+  for (int m = 0; m < MX; ++m) {
+    if (m < M && cbase + m < n && !__builtin_isnan(v[m])) {
+      valid |= 1ull << m;
+      mn = fminf(mn, v[m]);
+      mx = fmaxf(mx, v[m]);
+    }
+  }
+  mn = wave_min_f32(mn);
+  mx = wave_max_f32(mx);
+  const int n_valid = wave_sum_i(__popcll(valid));
+  uint64_t taken = 0;
+  if (k > 0 && k < n_valid) {
+    const float scale = 256.f / (mx - mn);
+    bool general = !(mx > mn) || !(scale < INFINITY);  // one value, or a range beyond float32
+    if (!general) {
+      auto bin_of = [&](float x) {
+        const int b = (int)((x - mn) * scale);
+        return b < 0 ? 0 : (b > 255 ? 255 : b);
+      };
+#pragma unroll
+      for (int q = 0; q < 4; ++q) hist[lane * 4 + q] = 0u;
+      wave_sync();
+      // position 0: the top bin; slots without a candidate count into spare entries
+#pragma unroll
+      for (int m = 0; m < MX; ++m)
+        atomicAdd(&hist[((valid >> m) & 1u) ? 255 - bin_of(v[m]) : 256 + (lane & 7)], 1u);
+      wave_sync();
+      uint32_t hb[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) hb[q] = hist[lane * 4 + q];
+      const uint32_t tot = hb[0] + hb[1] + hb[2] + hb[3];
+      uint32_t ab = wave_prefix_sum_dpp(tot) - tot;
+      int found = -1;
+      uint32_t fa = 0, fc = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (found < 0 && ab < (uint32_t)k && ab + hb[q] >= (uint32_t)k) {
+          found = 255 - (lane * 4 + q);
+          fa = ab;
+          fc = hb[q];
+        }
+        ab += hb[q];
+      }
+      const uint64_t bal = __ballot(found >= 0);
+      wave_sync();  // histogram read before it becomes the id list
+      const int srcl = bal ? __ffsll((long long)bal) - 1 : 0;
+      const int bstar = __builtin_amdgcn_readlane(found, srcl);
+      const int kr = k - __builtin_amdgcn_readlane((int)fa, srcl);
+      const int cb = __builtin_amdgcn_readlane((int)fc, srcl);
+      general = bal == 0 || cb > kBoundaryMax;
+      if (!general) {
+        uint64_t member = 0;
+#pragma unroll
+        for (int m = 0; m < MX; ++m) {
+          if ((valid >> m) & 1u) {
+            const int bn = bin_of(v[m]);
+            if (bn > bstar) taken |= 1ull << m;
+            else if (bn == bstar) member |= 1ull << m;
+          }
+        }
+        if (cb == kr) {  // the whole boundary bin is kept
+          taken |= member;
+        } else {
+          // the members, in candidate order: scores over this wave's LDS
+          // row, ids over the histogram; each lane's run starts at its
+          // exclusive prefix of the member counts
+          uint32_t* ids = hist;
+          const int pm = __popcll(member);
+          const int mbase = (int)wave_prefix_sum_dpp((uint32_t)pm) - pm;
+          int pos = mbase;
+#pragma unroll
+          for (int m = 0; m < MX; ++m) {
+            if ((member >> m) & 1u) {
+              s[pos] = v[m];
+              ids[pos] = (uint32_t)(cbase + m);
+              ++pos;
+            }
+          }
+          wave_sync();
+          // rank of each member: larger scores, then equal scores of lower id
+          bool straddle = false;
+          for (int i = lane; i < cb; i += 64) {
+            const float vi = s[i];
+            const uint32_t ci = ids[i] & 0x7fffffffu;
+            int gt = 0, eq_lo = 0, eq = 0;
+            for (int j = 0; j < cb; ++j) {  // ids of earlier rounds may carry the taken flag
+              const float vj = s[j];
+              gt += vj > vi;
+              eq += vj == vi;
+              eq_lo += (vj == vi) & ((ids[j] & 0x7fffffffu) < ci);
+            }
+            // a float32 tie group [gt, gt + eq) cut by the k-th place
+            straddle |= gt < kr && gt + eq > kr;
+            if (gt + eq_lo < kr) ids[i] = ci | 0x80000000u;  // taken
+          }
+          general = __ballot(straddle) != 0;
+          wave_sync();
+          if (!general) {
+            pos = mbase;
+#pragma unroll
+            for (int m = 0; m < MX; ++m) {
+              if ((member >> m) & 1u) {
+                if (ids[pos] & 0x80000000u) taken |= 1ull << m;
+                ++pos;
+              }
+            }
+          }
+          wave_sync();
+        }
+      }
+    }
+    if (general) {
+      // the row's scores into this wave's LDS row, settled in stages
+#pragma unroll
+      for (int m = 0; m < MX; ++m)
+        if (m < M && cbase + m < n) s[cbase + m] = v[m];
+      wave_sync();
+      select_dense_staged<D>(a, slot_tab, s, n, row, bh, nS, n_keys, qrow, hist, lane);
+      return;
+    }
+  } else if (k > 0) {
+    taken = valid;  // every candidate kept
+  }
+  // emit in ascending candidate order: this lane's run starts at its
+  // exclusive prefix of the taken counts
+  const int pt = __popcll(taken);
+  const int incl = (int)wave_prefix_sum_dpp((uint32_t)pt);
+  const int total = __builtin_amdgcn_readlane(incl, 63);
+  int pos = incl - pt;
+  for (uint64_t t = taken; t; t &= t - 1, ++pos)
+    if (pos < k) out[pos] = cbase + __builtin_ctzll(t);
+  const int cnt = total < k ? total : k;
+  for (int p = cnt + lane; p < a.kmax; p += 64) out[p] = -1;
+  if (lane == 0) a.sel_cnt[row] = cnt;
+}
+
 template <int D>
 __global__ __launch_bounds__(64 * kDenseWaves, 1) void draft_dense_kernel(DraftArgs a) {
   constexpr int KS = D / 4;  // k-steps of one 16 x 16 x 4 product chain
@@ -983,9 +1150,17 @@ __global__ __launch_bounds__(64 * kDenseWaves, 1) void draft_dense_kernel(DraftA
   }
   __syncthreads();
 
-  for (int ro = wave; ro < nrows; ro += kDenseWaves)
-    select_dense<D>(a, slot_tab, sc + (size_t)ro * rs, n, row0 + ro, bh, nS, n_keys,
+  for (int ro = wave; ro < nrows; ro += kDenseWaves) {
+    float* srow = sc + (size_t)ro * rs;
+    float v[kDenseM];
+#pragma unroll
+    for (int m = 0; m < kDenseM; ++m) {
+      const int c = lane + 64 * m;
+      v[m] = srow[c < n ? c : 0];
+    }
+    select_dense<D>(a, slot_tab, srow, v, n, row0 + ro, bh, nS, n_keys,
                     a.q_pool + (row0 + ro) * D, hist_all + wave * kHistStride, lane);
+  }
 }
 
 template <int D>
@@ -1003,6 +1178,168 @@ hipError_t launch_dense(DraftArgs a, hipStream_t s) {
   }
   hipLaunchKernelGGL(draft_dense_kernel<D>, dim3((unsigned)wgs), dim3(64 * kDenseWaves), shmem, s,
                      a);
+  return hipGetLastError();
+}
+
+// Split form of the dense path, for callers that pass a workspace: the
+// scores go to device memory and two kernels replace the fused one.
+// Scoring: a workgroup takes 64 rows of one temporal block (16 per wave,
+// held in registers as the A operand) against a chunk of 256 candidates;
+// each 16-key tile of the pooled ring is loaded once into LDS and read by
+// all four waves, so the pooled keys leave L2 once per 64 rows. The
+// products run in the fused kernel's order, so the float32 scores are the
+// same values. Selection: one wave per row over the whole chip, where the
+// fused kernel's one workgroup per CU left part of the chip idle in its
+// last round.
+constexpr int kScoreTiles = 16;                       // 16-key tiles per scoring workgroup
+constexpr int kSelWaves = 4;                          // rows per selection workgroup
+
+// Workspace row stride: whole groups of four scores per lane (64 lanes).
+inline int split_row_stride(long long n_max) { return (int)(((n_max + 255) / 256) * 256); }
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void draft_score_kernel(DraftArgs a) {
+  constexpr int KS = D / 4;      // k-steps of one 16 x 16 x 4 product chain
+  constexpr int PER = D / 16;    // doubles one thread stages per tile
+  // tile layout for the B fragments: (d, key r) at ((d / 8 * 4 + d % 4) * 16 + r) * 2 + d / 4 % 2,
+  // so lane (r, dq) reads k-steps 2 sp and 2 sp + 1 as one 16-byte pair
+  __shared__ __attribute__((aligned(16))) double kt[2][16 * D];
+  __shared__ int32_t slot_tab[LCSA_MAX_SLOTS];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int nS = a.nby * a.nbx;
+  const int ngr = (nS + 63) / 64;
+  const int n_max = a.view.n * nS;
+  const int nch = (n_max + 16 * kScoreTiles - 1) / (16 * kScoreTiles);
+  int task = xcd_task(a.B * a.NH * a.ntb_q * ngr * nch);
+  if (task < 0) return;
+  const int ch = task % nch;
+  task /= nch;
+  const int gr = task % ngr;
+  task /= ngr;
+  const int tq = task % a.ntb_q;
+  task /= a.ntb_q;
+  const size_t bh = (size_t)task;  // b * NH + h
+  const int64_t qtb = a.q_first_abs_tb + tq;
+  int nvis = 0;
+  for (int p = 0; p < a.view.n; ++p)
+    if (a.view.abs_tb[p] <= qtb) nvis = p + 1;
+  const int n = nvis * nS;
+  const int c0 = ch * 16 * kScoreTiles;
+  if (c0 >= n) return;  // uniform: the chunk lies past this TB's candidates
+  const int ntl = min(kScoreTiles, (n - c0 + 15) / 16);
+  const int nq = a.ntb_q * nS;
+  const int s0 = 64 * gr + 16 * wave;
+  const int nrows = nS - s0;  // rows of this wave: min(16, nrows), none if <= 0
+  const size_t row0 = bh * nq + (size_t)tq * nS + s0;
+
+  stage_slots(a.view, slot_tab);
+  const int r = lane & 15, dq = lane >> 4;
+  double qa[KS];
+#pragma unroll
+  for (int s2 = 0; s2 < KS; ++s2)
+    qa[s2] = r < nrows ? a.q_pool[(row0 + r) * D + 4 * s2 + dq] : 0.0;
+  __syncthreads();
+
+  // staging: thread (kr, dg) loads key c0 + 16 t + kr at d = dg + 16 e; a
+  // key past the candidates reads key 0 (a valid address), never stored
+  const int kr = tid & 15, dg = tid >> 4;
+  const SmallDiv div_ns(nS);
+  double pre[PER];
+  auto load_tile = [&](int t) {
+    int u = c0 + 16 * t + kr;
+    u = u < n ? u : 0;
+    const int p = div_ns(u), sp = u - p * nS;
+    const double* kp = a.kpool_ring + (bh * a.n_slots + slot_tab[p]) * (size_t)D * nS + sp;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) pre[e] = kp[(size_t)(dg + 16 * e) * nS];
+  };
+  auto stage_tile = [&](int buf) {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int d = dg + 16 * e;
+      kt[buf][(((d >> 3) * 4 + (d & 3)) * 16 + kr) * 2 + ((d >> 2) & 1)] = pre[e];
+    }
+  };
+
+  float* ws = a.scores;
+  const int rs = a.ws_stride;
+  load_tile(0);
+  stage_tile(0);
+  load_tile(1);
+  __syncthreads();
+  for (int t = 0; t < ntl; ++t) {
+    const double* kb = kt[t & 1];
+    f64x4 acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int sp = 0; sp < KS / 2; ++sp) {
+      const double2 bb = *reinterpret_cast<const double2*>(kb + ((sp * 4 + dq) * 16 + r) * 2);
+      acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[2 * sp], bb.x, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[2 * sp + 1], bb.y, acc1, 0, 0, 0);
+    }
+    const int u = c0 + 16 * t + r;
+    if (u < n) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (4 * j + dq < nrows) ws[(row0 + 4 * j + dq) * rs + u] = (float)(acc0[j] + acc1[j]);
+    }
+    if (t + 1 < ntl) {  // uniform
+      stage_tile((t + 1) & 1);  // read by every wave in iteration t - 1, before the last barrier
+      load_tile(t + 2);
+    }
+    __syncthreads();
+  }
+}
+
+// One wave per row: the split selection over its float32 scores in the
+// workspace (this wave's LDS row is its scratch).
+template <int D>
+__global__ __launch_bounds__(64 * kSelWaves) void draft_select_kernel(DraftArgs a) {
+  extern __shared__ float xsm[];
+  __shared__ int32_t slot_tab[LCSA_MAX_SLOTS];
+  stage_slots(a.view, slot_tab);
+  __syncthreads();
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nS = a.nby * a.nbx;
+  const int nq = a.ntb_q * nS;
+  const long long rows = (long long)a.B * a.NH * nq;
+  const long long row = (long long)blockIdx.x * kSelWaves + wave;
+  if (row >= rows) return;
+  const size_t bh = (size_t)(row / nq);
+  const int tq = (int)(row % nq) / nS;
+  const int64_t qtb = a.q_first_abs_tb + tq;
+  int nvis = 0;
+  for (int p = 0; p < a.view.n; ++p)
+    if (a.view.abs_tb[p] <= qtb) nvis = p + 1;
+  const int n = nvis * nS;
+  const int64_t n_keys = (int64_t)a.view.n * nS;
+  const int ls = a.ws_stride + 16;  // LDS row: the candidates and 8 spare entries
+  float* s = xsm + (size_t)wave * (ls + kHistStride);
+  uint32_t* hist = reinterpret_cast<uint32_t*>(s + ls);
+  select_split<D>(a, slot_tab, a.scores + (size_t)row * a.ws_stride, s, n, (size_t)row, bh, nS,
+                  n_keys, a.q_pool + (size_t)row * D, hist, lane);
+}
+
+template <int D>
+hipError_t launch_split(DraftArgs a, hipStream_t s) {
+  const int nS = a.nby * a.nbx;
+  const long long n_max = (long long)a.view.n * nS;
+  a.ws_stride = split_row_stride(n_max);
+  const long long ngr = (nS + 63) / 64;
+  const long long nch = (n_max + 16 * kScoreTiles - 1) / (16 * kScoreTiles);
+  const long long tasks = (long long)a.B * a.NH * a.ntb_q * ngr * nch;
+  hipLaunchKernelGGL(draft_score_kernel<D>, dim3((unsigned)(8 * ((tasks + 7) / 8))), dim3(256), 0, s,
+                     a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long long rows = (long long)a.B * a.NH * a.ntb_q * nS;
+  const size_t shmem = (size_t)kSelWaves * (a.ws_stride + 16 + kHistStride) * sizeof(float);
+  if (shmem > 64 * 1024) {
+    e = hipFuncSetAttribute((const void*)draft_select_kernel<D>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(draft_select_kernel<D>, dim3((unsigned)((rows + kSelWaves - 1) / kSelWaves)),
+                     dim3(64 * kSelWaves), shmem, s, a);
   return hipGetLastError();
 }
 
@@ -1063,6 +1400,22 @@ hipError_t launch_d(const DraftArgs& a, hipStream_t s) {
 
 }  // namespace
 
+// Whether a call takes the dense path: a window covering the whole grid and
+// between kDenseMinCand and kDenseMaxCand candidates, without probabilities.
+static bool takes_dense(const DraftArgs& a) {
+  const bool whole_grid = a.border == 0
+                              ? (a.nby <= a.local_range && a.nbx <= a.local_range)
+                              : (a.local_range / 2 >= a.nby - 1 && a.local_range / 2 >= a.nbx - 1);
+  const long long n_max = (long long)a.view.n * a.nby * a.nbx;
+  return !a.probs && whole_grid && n_max >= kDenseMinCand && n_max <= kDenseMaxCand;
+}
+
+size_t draft_workspace_bytes(const DraftArgs& a) {
+  if (!takes_dense(a)) return 0;
+  const long long nS = (long long)a.nby * a.nbx;
+  return (size_t)a.B * a.NH * a.ntb_q * nS * split_row_stride(a.view.n * nS) * sizeof(float);
+}
+
 hipError_t launch_draft_mask(const DraftArgs& a, hipStream_t s) {
   // The tile path pays where 4 x 4 neighbouring rows share most of a window
   // that is smaller than the grid, or where its tiles alone fill the chip.
@@ -1077,12 +1430,10 @@ hipError_t launch_draft_mask(const DraftArgs& a, hipStream_t s) {
   // the pooled keys dominate; below that the row-group path's many small
   // workgroups win (768x1408 step, 264 candidates: 25 vs 44 us). The draft's
   // float64 probabilities come from the paths below.
-  const bool whole_grid = a.border == 0
-                              ? (a.nby <= a.local_range && a.nbx <= a.local_range)
-                              : (a.local_range / 2 >= a.nby - 1 && a.local_range / 2 >= a.nbx - 1);
-  const long long n_max = (long long)a.view.n * a.nby * a.nbx;
-  if (!a.probs && whole_grid && n_max >= kDenseMinCand && n_max <= kDenseMaxCand)
+  if (takes_dense(a)) {
+    if (a.scores) return a.D == 64 ? launch_split<64>(a, s) : launch_split<128>(a, s);
     return a.D == 64 ? launch_dense<64>(a, s) : launch_dense<128>(a, s);
+  }
   const bool window_inside = a.local_range < a.nby || a.local_range < a.nbx;
   const long long tiles =
       (long long)a.B * a.NH * a.ntb_q * ((a.nby + 3) / 4) * ((a.nbx + 3) / 4);

@@ -222,10 +222,37 @@ lcsa_status lcsa_partition_pool(const lcsa_geom* g, const void* q, const void* k
   return device_status(launch_partition_pool(a, (hipStream_t)stream), fn);
 }
 
+lcsa_status lcsa_draft_workspace_size(const lcsa_geom* gq, const lcsa_kv_cache* cache,
+                                      const lcsa_select_params* params, size_t* bytes_out) {
+  lcsa_status st;
+  if ((st = check_geom(gq, "lcsa_draft_workspace_size")) || (st = check_params(params)) ||
+      (st = check_cache(cache)) || (st = check_matches_cache(gq, cache)))
+    return st;
+  if (!bytes_out) return fail(LCSA_ERR_NULL, "bytes_out is NULL");
+  DraftArgs a{};
+  a.B = gq->batch;
+  a.NH = gq->heads;
+  a.D = gq->head_dim;
+  a.ntb_q = gq->frames / 2;
+  a.nby = gq->height / 8;
+  a.nbx = gq->width / 8;
+  a.local_range = params->local_range;
+  a.border = params->border;
+  size_t most = 0;  // over every occupancy of the cache
+  for (int32_t nv = 1; nv <= cache->n_slots; ++nv) {
+    a.view.n = nv;
+    const size_t b = draft_workspace_bytes(a);
+    most = b > most ? b : most;
+  }
+  *bytes_out = most;
+  return ok();
+}
+
 lcsa_status lcsa_draft_mask(const lcsa_geom* gq, const double* q_pool, int64_t q_first_abs_tb,
                             const lcsa_kv_cache* cache, const lcsa_select_params* params,
                             int32_t kmax, int32_t* sel_idx, int32_t* sel_cnt, double* probs,
-                            size_t probs_bytes, void* stream) {
+                            size_t probs_bytes, void* workspace, size_t workspace_bytes,
+                            void* stream) {
   lcsa_status st;
   if ((st = check_geom(gq, "lcsa_draft_mask")) || (st = check_params(params)) ||
       (st = check_cache(cache)) || (st = check_matches_cache(gq, cache)) ||
@@ -304,6 +331,15 @@ lcsa_status lcsa_draft_mask(const lcsa_geom* gq, const double* q_pool, int64_t q
   while (gx > 2 && rows_per_col * ((a.nbx + gx - 1) / gx) < 512) gx /= 2;
   while (gx > 1 && (int64_t)gx * a.row_stride * 8 > 64 * 1024) gx /= 2;
   a.gx = gx;
+  if (workspace) {
+    if (reinterpret_cast<uintptr_t>(workspace) % 256)
+      return fail(LCSA_ERR_ALIGN, "lcsa_draft_mask: workspace is not 256-byte aligned");
+    const size_t need = draft_workspace_bytes(a);
+    if (need > workspace_bytes)
+      return fail(LCSA_ERR_CAPACITY, "lcsa_draft_mask: workspace of %zu bytes; %zu needed",
+                  workspace_bytes, need);
+    if (need) a.scores = static_cast<float*>(workspace);
+  }
   return device_status(launch_draft_mask(a, (hipStream_t)stream), "lcsa_draft_mask");
 }
 

@@ -45,6 +45,8 @@ struct DraftArgs {
   int64_t ratio_num, ratio_den;      // reduced fraction incl. resolution scale
   int32_t row_stride;                // LDS scores per row (>= max candidates)
   int32_t gx;                        // query rows (consecutive bx) per workgroup
+  float* scores;                     // split dense path: [B][NH][nq][ws_stride] float32, or null
+  int32_t ws_stride;                 // scores per workspace row (set by the launcher)
 };
 
 struct AttnArgs {
@@ -105,6 +107,9 @@ struct BwdArgs {
 
 hipError_t launch_partition_pool(const PartitionArgs& a, hipStream_t s);
 hipError_t launch_draft_mask(const DraftArgs& a, hipStream_t s);
+// Workspace bytes lcsa_draft_mask's split dense path needs for a (0 when
+// the call takes another path).
+size_t draft_workspace_bytes(const DraftArgs& a);
 hipError_t launch_block_sparse_attn(const AttnArgs& a, int32_t dtype, bool segment, hipStream_t s);
 hipError_t launch_segment_lists(const SegListArgs& a, hipStream_t s);
 hipError_t launch_local_lists(const LocalListArgs& a, hipStream_t s);

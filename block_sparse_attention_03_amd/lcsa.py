@@ -83,7 +83,8 @@ def load_library(path: str = LIB_PATH):
         "lcsa_partition_pool": [G, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, C,
                                 c_int32, c_void_p],
         "lcsa_draft_mask": [G, c_void_p, c_int64, C, P, c_int32, c_void_p, c_void_p, c_void_p,
-                            ctypes.c_size_t, c_void_p],
+                            ctypes.c_size_t, c_void_p, ctypes.c_size_t, c_void_p],
+        "lcsa_draft_workspace_size": [G, C, P, POINTER(ctypes.c_size_t)],
         "lcsa_block_sparse_attn": [G, c_void_p, C, c_void_p, c_void_p, c_int32, c_float,
                                    c_void_p, c_void_p, c_void_p],
         "lcsa_block_sparse_attn_tok": [G, c_void_p, C, c_void_p, c_void_p, c_int32, c_float,
@@ -224,13 +225,23 @@ def lcsa_partition_pool(geom: Geom, q, k, v, q_blk, q_pool, cache: KvCacheStruct
 
 def lcsa_draft_mask(geom: Geom, q_pool, q_first_abs_tb: int, cache: KvCacheStruct,
                     params: SelectParams, kmax: int, sel_idx, sel_cnt, probs=None, stream=None,
-                    probs_bytes=None):
-    """probs_bytes defaults to the probs tensor's own size."""
+                    probs_bytes=None, workspace=None, workspace_bytes=None):
+    """probs_bytes and workspace_bytes default to the tensors' own sizes."""
     lib = load_library()
     pb = _nbytes(probs) if probs_bytes is None else probs_bytes
+    wb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
     _check(lib.lcsa_draft_mask(ctypes.byref(geom), _ptr(q_pool), q_first_abs_tb,
                                ctypes.byref(cache), ctypes.byref(params), kmax, _ptr(sel_idx),
-                               _ptr(sel_cnt), _ptr(probs), pb, _stream(stream)))
+                               _ptr(sel_cnt), _ptr(probs), pb, _ptr(workspace), wb,
+                               _stream(stream)))
+
+
+def lcsa_draft_workspace_size(geom: Geom, cache: KvCacheStruct, params: SelectParams) -> int:
+    lib = load_library()
+    n = ctypes.c_size_t(0)
+    _check(lib.lcsa_draft_workspace_size(ctypes.byref(geom), ctypes.byref(cache),
+                                         ctypes.byref(params), ctypes.byref(n)))
+    return n.value
 
 
 def lcsa_block_sparse_attn(geom: Geom, q_blk, cache: KvCacheStruct, sel_idx, sel_cnt, kmax: int,
@@ -401,13 +412,14 @@ class StepBuffers:
 def run_step(geom: Geom, q, k, v, cache: KVCache, first_abs_tb: int, params: SelectParams,
              bufs: StepBuffers | None = None, keep_tb: int | None = None, stream=None,
              want_probs=False, want_lse=False, scale: float = 0.0, local: bool = False,
-             q_blocks: bool = False):
+             q_blocks: bool = False, draft_workspace=None):
     """One LCSA invocation through the C-ABI: append, partition+pool, draft
     (or, with local=True, the FlashVSR+ local lists: every allowed key
     block), attention, evict. The attention reads q in token layout, so the
     partition writes only q's block means; q_blocks=True instead writes the
-    query blocks to bufs.q_blk and reads them from there. Returns the
-    StepBuffers holding the results."""
+    query blocks to bufs.q_blk and reads them from there. draft_workspace
+    (a device tensor of lcsa_draft_workspace_size bytes, or None) goes to the
+    draft. Returns the StepBuffers holding the results."""
     n_tb = geom.frames // 2
     first_slot = cache.append(n_tb, first_abs_tb)
     if local:
@@ -428,7 +440,8 @@ def run_step(geom: Geom, q, k, v, cache: KVCache, first_abs_tb: int, params: Sel
                          bufs.sel_cnt, stream)
     else:
         lcsa_draft_mask(geom, bufs.q_pool, first_abs_tb, cache.c, params, bufs.kmax,
-                        bufs.sel_idx, bufs.sel_cnt, bufs.probs, stream)
+                        bufs.sel_idx, bufs.sel_cnt, bufs.probs, stream,
+                        workspace=draft_workspace)
     if q_blocks:
         lcsa_block_sparse_attn(geom, q_blk, cache.c, bufs.sel_idx, bufs.sel_cnt, bufs.kmax,
                                bufs.out, bufs.lse, scale, stream)

@@ -216,12 +216,29 @@ lcsa_status lcsa_partition_pool(const lcsa_geom* g, const void* q, const void* k
  * a smaller buffer is LCSA_ERR_CAPACITY); keep the k candidates of largest
  * score, equal scores ordered by lower logical id. sel_idx receives the kept
  * logical ids in ascending order, padded with -1 up to kmax; sel_cnt the
- * count. kmax >= lcsa_max_topk() (LCSA_ERR_CAPACITY otherwise). */
+ * count. kmax >= lcsa_max_topk() (LCSA_ERR_CAPACITY otherwise).
+ * workspace (nullable): device memory, 256-byte aligned (LCSA_ERR_ALIGN),
+ * of workspace_bytes bytes. With a window covering the whole grid and about
+ * a thousand to 2,304 candidates per row (and probs NULL), the call then
+ * writes each row's float32 scores there and selects from them with one
+ * wave per row, instead of one fused kernel; the selections are the same.
+ * It needs lcsa_draft_workspace_size() bytes (LCSA_ERR_CAPACITY if
+ * smaller); other calls leave it untouched. The caller owns it; calls that
+ * share one workspace must be ordered on one stream. */
 lcsa_status lcsa_draft_mask(const lcsa_geom* gq, const double* q_pool,
                             int64_t q_first_abs_tb, const lcsa_kv_cache* cache,
                             const lcsa_select_params* params, int32_t kmax,
                             int32_t* sel_idx, int32_t* sel_cnt, double* probs,
-                            size_t probs_bytes, void* stream);
+                            size_t probs_bytes, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/* Bytes of workspace lcsa_draft_mask can use for a chunk of geometry gq and
+ * the draft rule params, at any occupancy of `cache` (the float32 scores of
+ * every query block against the cache's key blocks; [HW] 2.2 step 3 scores
+ * every block pair of the coarse map). 0 when no occupancy takes the split
+ * path. */
+lcsa_status lcsa_draft_workspace_size(const lcsa_geom* gq, const lcsa_kv_cache* cache,
+                                      const lcsa_select_params* params, size_t* bytes_out);
 
 /* Step 5 ([FN] Key design 2: full 128x128 attention with the original Q, K,
  * V on the selected block pairs only; [HW] 2.2: unselected blocks are

@@ -47,7 +47,8 @@ def lib_params(w) -> L.SelectParams:
 class Stream:
     """Runs the same stream of chunks on the GPU and in the oracle."""
 
-    def __init__(self, w, device, seed=None, zero_q=False, q_scale=None, q_blocks=False):
+    def __init__(self, w, device, seed=None, zero_q=False, q_scale=None, q_blocks=False,
+                 draft_ws=False):
         import torch
         self.w = w
         self.q_scale = q_scale  # a power of two: exact in bf16, the same on both sides
@@ -75,6 +76,12 @@ class Stream:
                                   self.gcache.c, first)
             O.prime_cache(self.ocache, d["k"][1], d["v"][1], 0)
             self.next_frame = w.cache_frames
+        # draft_ws: give the draft a workspace (its split path where it applies)
+        self.dws = None
+        if draft_ws:
+            nb = L.lcsa_draft_workspace_size(self.geom, self.gcache.c, self.lp)
+            assert nb > 0, "this workload never takes the draft's split path"
+            self.dws = torch.empty(nb, dtype=torch.uint8, device=device)
 
     def step(self, rows="all", want_probs=True):
         """One chunk: returns (gpu results dict, oracle StepResult)."""
@@ -98,7 +105,7 @@ class Stream:
         local = w.lists == "local"
         bufs = L.run_step(self.geom, q, k, v, self.gcache, tb0, self.lp, keep_tb=w.cap_tb,
                           want_probs=want_probs and not local, want_lse=True, local=local,
-                          q_blocks=self.q_blocks)
+                          q_blocks=self.q_blocks, draft_workspace=self.dws)
         torch.cuda.synchronize()
         g = {"sel_idx": bufs.sel_idx.cpu().numpy(), "sel_cnt": bufs.sel_cnt.cpu().numpy(),
              "out": bufs.out, "lse": bufs.lse.cpu().numpy(),

@@ -220,6 +220,32 @@ def test_empty_chunk_is_a_no_op(lib):
     assert L.lcsa_last_error() == ""
 
 
+def test_draft_workspace_size_and_validation(lib):
+    """The draft's workspace: sized for the split path at the cache's fullest
+    occupancy (0 where no occupancy takes it), and refused when misaligned
+    (LCSA_ERR_ALIGN) or too small (LCSA_ERR_CAPACITY) before any device call."""
+    c = fake_cache(17, 30, 2, 128, L.LCSA_BF16, 4)  # the 4K grid: 510 blocks per TB
+    geom = L.make_geom(1, 2, 128, 2, 136, 240, L.LCSA_BF16)
+    glob = L.make_params(local_range=255, ratio=(1, 5))
+    nb = L.lcsa_draft_workspace_size(geom, c, glob)
+    assert nb == 2 * 510 * 2048 * 4  # 2 heads x 510 rows x 2,040 candidates padded to 2,048
+    assert L.lcsa_draft_workspace_size(geom, c, L.make_params(local_range=11)) == 0
+    small = fake_cache(6, 11, 2, 128, L.LCSA_BF16, 4)  # 264 candidates at most: other paths
+    assert L.lcsa_draft_workspace_size(L.make_geom(1, 2, 128, 2, 48, 88, L.LCSA_BF16), small,
+                                       glob) == 0
+    assert lib.lcsa_draft_workspace_size(ctypes.byref(geom), ctypes.byref(c), ctypes.byref(glob),
+                                         None) == 1
+    L.lcsa_kv_cache_append(c, 4, 0)
+    ok = _P(FAKE)
+    kmax = L.lcsa_max_topk(geom, 3, c, glob)
+    msg = expect(5, L.lcsa_draft_mask, geom, ok, 3, c, glob, kmax, ok, ok, None, 0,
+                 workspace=_P(FAKE + 8), workspace_bytes=nb)
+    assert "workspace" in msg
+    msg = expect(6, L.lcsa_draft_mask, geom, ok, 3, c, glob, kmax, ok, ok, None, 0,
+                 workspace=ok, workspace_bytes=nb - 1)
+    assert "workspace" in msg
+
+
 def test_too_many_candidates_is_refused(lib):
     # 16 TBs of a 17x30 grid with an unbounded window: 8160 candidates > 4096
     c = fake_cache(17, 30, 1, 128, L.LCSA_BF16, 16)

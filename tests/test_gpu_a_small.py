@@ -270,21 +270,24 @@ def dense(**kw) -> Workload:
     dict(topk_fixed=1),
     dict(frames=4, cache_frames=8),                           # 2 query TBs: 1,152 and 960
 ])
-def test_dense_draft_path(dev, case):
-    """Selections on every row, outputs on sampled rows."""
+@pytest.mark.parametrize("split", [False, True], ids=["fused", "split"])
+def test_dense_draft_path(dev, case, split):
+    """Selections on every row, outputs on sampled rows; split: with a draft
+    workspace (scores in device memory, selection one wave per row)."""
     w = dense(**case)
-    st = Stream(w, dev)
+    st = Stream(w, dev, draft_ws=split)
     rows = sample_rows(w, 4)
     g, ref = st.step(rows=rows, want_probs=False)
     stats = compare_step(w, g, ref, rows=rows)
-    say(f"dense draft {case}: {stats}")
+    say(f"dense draft {case} {'split' if split else 'fused'}: {stats}")
 
 
-def test_dense_draft_equal_scores_take_lowest_ids(dev):
+@pytest.mark.parametrize("split", [False, True], ids=["fused", "split"])
+def test_dense_draft_equal_scores_take_lowest_ids(dev, split):
     """q = 0: every score is 0, so every candidate is tied in float32 and in
     float64 and the k lowest ids are kept."""
     w = dense(ratio=(1, 3))
-    st = Stream(w, dev, zero_q=True)
+    st = Stream(w, dev, zero_q=True, draft_ws=split)
     rows = sample_rows(w, 2)
     g, ref = st.step(rows=rows, want_probs=False)
     for h in range(w.heads):
@@ -295,8 +298,9 @@ def test_dense_draft_equal_scores_take_lowest_ids(dev):
     compare_step(w, g, ref, rows=rows)
 
 
+@pytest.mark.parametrize("split", [False, True], ids=["fused", "split"])
 @pytest.mark.parametrize("outliers", [False, True], ids=["tie", "tie-in-a-full-bin"])
-def test_dense_draft_float32_ties_resolved_in_float64(dev, outliers):
+def test_dense_draft_float32_ties_resolved_in_float64(dev, outliers, split):
     """Scores 1 + j * 2^-27 (exact in float64): groups of 16 consecutive j
     round to one float32 value and share the high half of their float64
     key, so the k-th place falls inside a float32 tie and is settled by the
@@ -304,7 +308,8 @@ def test_dense_draft_float32_ties_resolved_in_float64(dev, outliers):
     boundary and go to the lower id. With `outliers`, two blocks score about
     +8.8 and -5, so every other score falls into one of the 256 histogram
     bins (far more than the pairwise rank takes) and the staged selection
-    decides. Selections must equal the oracle's exactly (no tie allowance)."""
+    decides. Selections must equal the oracle's exactly (no tie allowance),
+    with and without a draft workspace."""
     NH, D, H, W = 2, 64, 144, 160
     nby, nbx = H // 8, W // 8
     nS = nby * nbx
@@ -350,8 +355,11 @@ def test_dense_draft_float32_ties_resolved_in_float64(dev, outliers):
     bufs = L.StepBuffers(g2, k, device=dev)
     L.lcsa_partition_pool(g2, dv["q"], dv["k"][:, 4:].contiguous(), dv["v"][:, 4:].contiguous(), None,
                           bufs.q_pool, cache.c, cache.append(1, 2))
-    L.lcsa_draft_mask(g2, bufs.q_pool, 2, cache.c, L.make_params(local_range=99, ratio=(1, 3)), k,
-                      bufs.sel_idx, bufs.sel_cnt)
+    lp = L.make_params(local_range=99, ratio=(1, 3))
+    ws = (torch.empty(L.lcsa_draft_workspace_size(g2, cache.c, lp), dtype=torch.uint8, device=dev)
+          if split else None)
+    L.lcsa_draft_mask(g2, bufs.q_pool, 2, cache.c, lp, k, bufs.sel_idx, bufs.sel_cnt,
+                      workspace=ws)
     torch.cuda.synchronize()
     sel = bufs.sel_idx.cpu().numpy()
     cnt = bufs.sel_cnt.cpu().numpy()

@@ -65,11 +65,14 @@ def test_local_layer_4k(dev):
         say(f"local 4K step {n}: {stats}")
 
 
-def test_global_layer_4k(dev):
+@pytest.mark.parametrize("split", [False, True], ids=["fused", "split"])
+def test_global_layer_4k(dev, split):
+    """Selections on every row, outputs on sampled rows; with and without a
+    draft workspace (split scoring and selection kernels, or the fused one)."""
     w = WORKLOADS["hybrid_global_4k"]
-    st = Stream(w, dev)
+    st = Stream(w, dev, draft_ws=split)
     rows = sample_rows(w, 3)
     g, ref = st.step(rows=rows, want_probs=False)
     assert set(int(x) for x in ref.kcount) == {48}   # floor(2040 / 5 * 768*1280 / (2176*3840))
     stats = compare_step(w, g, ref, rows=rows, check_probs=False)
-    say(f"global 4K: {stats}")
+    say(f"global 4K ({'split' if split else 'fused'}): {stats}")
