@@ -1202,8 +1202,13 @@ __global__ __launch_bounds__(256, 2) void draft_score_kernel(DraftArgs a) {
   constexpr int KS = D / 4;      // k-steps of one 16 x 16 x 4 product chain
   constexpr int PER = D / 16;    // doubles one thread stages per tile
   // tile layout for the B fragments: (d, key r) at ((d / 8 * 4 + d % 4) * 16 + r) * 2 + d / 4 % 2,
-  // so lane (r, dq) reads k-steps 2 sp and 2 sp + 1 as one 16-byte pair
-  __shared__ __attribute__((aligned(16))) double kt[2][16 * D];
+  // so lane (r, dq) reads k-steps 2 sp and 2 sp + 1 as one 16-byte pair.
+  // Before the tiles, the same memory stages the pooled queries: 32 rows at
+  // a time, D + 2 doubles per row (the A fragment reads of 16 rows then fall
+  // into distinct banks)
+  constexpr int QS = D + 2;
+  constexpr int LDS_D = 2 * 16 * D > 32 * QS ? 2 * 16 * D : 32 * QS;
+  __shared__ __attribute__((aligned(16))) double lds_d[LDS_D];
   __shared__ int32_t slot_tab[LCSA_MAX_SLOTS];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int nS = a.nby * a.nbx;
@@ -1234,11 +1239,38 @@ __global__ __launch_bounds__(256, 2) void draft_score_kernel(DraftArgs a) {
 
   stage_slots(a.view, slot_tab);
   const int r = lane & 15, dq = lane >> 4;
+  // pooled queries: two passes of 32 rows, each row's D doubles read as
+  // consecutive 16-byte pieces (rows past the TB's last block read as 0)
+  const int tid2 = 2 * tid;
+  const size_t grow0 = bh * nq + (size_t)tq * nS + 64 * gr;  // the workgroup's first row
+  constexpr int QL = 32 * D / 512;                           // 16-byte loads per thread per pass
+  double2 qx[2][QL];
+#pragma unroll
+  for (int ps = 0; ps < 2; ++ps)
+#pragma unroll
+    for (int i = 0; i < QL; ++i) {
+      const int f = tid2 + 512 * i, rr = 32 * ps + f / D;
+      qx[ps][i] = 64 * gr + rr < nS
+                      ? *reinterpret_cast<const double2*>(a.q_pool + (grow0 + rr) * D + f % D)
+                      : make_double2(0.0, 0.0);
+    }
   double qa[KS];
 #pragma unroll
-  for (int s2 = 0; s2 < KS; ++s2)
-    qa[s2] = r < nrows ? a.q_pool[(row0 + r) * D + 4 * s2 + dq] : 0.0;
-  __syncthreads();
+  for (int ps = 0; ps < 2; ++ps) {
+#pragma unroll
+    for (int i = 0; i < QL; ++i) {
+      const int f = tid2 + 512 * i;
+      *reinterpret_cast<double2*>(lds_d + (f / D) * QS + f % D) = qx[ps][i];
+    }
+    __syncthreads();
+    if ((wave >> 1) == ps) {  // uniform per wave
+      const double* qr = lds_d + (16 * (wave & 1) + r) * QS + dq;
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2) qa[s2] = qr[4 * s2];
+    }
+    __syncthreads();
+  }
+  double (*kt)[16 * D] = reinterpret_cast<double (*)[16 * D]>(lds_d);
 
   // staging: thread (kr, dg) loads key c0 + 16 t + kr at d = dg + 16 e; a
   // key past the candidates reads key 0 (a valid address), never stored
