@@ -131,6 +131,138 @@ __device__ inline uint32_t wave_prefix_sum_dpp(uint32_t x) {
   return (uint32_t)v;
 }
 
+// Register form of select_row, for rows of at most kRegCand candidates when
+// no probabilities are asked for. Lane l holds the candidates
+// [l M, l M + M) (M = ceil(n / 64)) of the row's float64 scores in
+// registers, so each refinement level is one pass over registers rather
+// than over LDS, and the kept ids go to their places through prefix sums of
+// per-lane counts (candidate order = ascending logical id), with no ballot
+// per 64 candidates. Same result as select_row: the k largest scores,
+// equal scores taken lowest index first.
+constexpr int kRegM = 8;
+constexpr int kRegCand = 64 * kRegM;
+
+__device__ void select_row_regs(const DraftArgs& a, const double* s, size_t row, int nvis,
+                                int ylo, int ny, int gxlo, int gxhi, int64_t n_keys,
+                                uint32_t* hist, int lane) {
+  const int nbx = a.nbx, nS = a.nby * nbx;
+  const int nx = gxhi - gxlo + 1;
+  const int n = nvis * ny * nx;
+  const int k = topk_dev(a, n, n_keys);
+  int32_t* out = a.sel_idx + row * a.kmax;
+  const int M = (n + 63) >> 6;
+  const int cbase = lane * M;
+  double v[kRegM];
+  uint32_t valid = 0;
+  double lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+  for (int m = 0; m < kRegM; ++m) {
+    const bool in_row = m < M && cbase + m < n;
+    v[m] = s[in_row ? cbase + m : 0];
+    if (in_row && v[m] == v[m]) {  // NaN scores are never kept
+      valid |= 1u << m;
+      lo = fmin(lo, v[m]);
+      hi = fmax(hi, v[m]);
+    }
+  }
+  lo = wave_min_dpp(lo);
+  hi = wave_max_dpp(hi);
+  const int n_valid = __builtin_amdgcn_readlane((int)wave_prefix_sum_dpp(__popc(valid)), 63);
+  uint32_t taken = 0, in = 0;  // in: undecided candidates, all in [lo, hi]
+  int kr = 0;
+  if (k >= n_valid) {
+    taken = valid;
+  } else if (k > 0) {
+    in = valid;
+    kr = k;
+    for (int level = 0; level <= n && lo < hi; ++level) {
+      const double scale = 256.0 / (hi - lo);
+      auto bin_of = [&](double x) {
+        const int b = (int)((x - lo) * scale);
+        return b < 0 ? 0 : (b > 255 ? 255 : b);
+      };
+#pragma unroll
+      for (int q = 0; q < 4; ++q) hist[lane * 4 + q] = 0u;
+      wave_sync();
+#pragma unroll
+      for (int m = 0; m < kRegM; ++m)
+        if ((in >> m) & 1u) atomicAdd(&hist[255 - bin_of(v[m])], 1u);  // position 0: top bin
+      wave_sync();
+      uint32_t hb[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) hb[q] = hist[lane * 4 + q];
+      const uint32_t tot = hb[0] + hb[1] + hb[2] + hb[3];
+      uint32_t ab = wave_prefix_sum_dpp(tot) - tot;  // candidates in higher bins
+      int found = -1;
+      uint32_t fa = 0, fc = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (found < 0 && ab < (uint32_t)kr && ab + hb[q] >= (uint32_t)kr) {
+          found = 255 - (lane * 4 + q);
+          fa = ab;
+          fc = hb[q];
+        }
+        ab += hb[q];
+      }
+      const uint64_t bal = __ballot(found >= 0);
+      wave_sync();
+      if (bal == 0) break;  // unreachable: 1 <= kr < candidates in range
+      const int src = __ffsll((long long)bal) - 1;
+      const int bin = __builtin_amdgcn_readlane(found, src);
+      kr -= __builtin_amdgcn_readlane((int)fa, src);
+      const int cb = __builtin_amdgcn_readlane((int)fc, src);
+      // above the bin: kept; below: dropped; in it: the new range
+      double nlo = INFINITY, nhi = -INFINITY;
+#pragma unroll
+      for (int m = 0; m < kRegM; ++m) {
+        if ((in >> m) & 1u) {
+          const int bn = bin_of(v[m]);
+          if (bn > bin) {
+            taken |= 1u << m;
+            in &= ~(1u << m);
+          } else if (bn < bin) {
+            in &= ~(1u << m);
+          } else {
+            nlo = fmin(nlo, v[m]);
+            nhi = fmax(nhi, v[m]);
+          }
+        }
+      }
+      lo = wave_min_dpp(nlo);
+      hi = wave_max_dpp(nhi);
+      if (cb == kr) {  // the whole bin is kept
+        taken |= in;
+        in = 0;
+        kr = 0;
+        break;
+      }
+    }
+    // the undecided candidates now share one value: the first kr of them
+    // in candidate order are kept
+    const int pe = __popc(in);
+    int e = (int)wave_prefix_sum_dpp((uint32_t)pe) - pe;
+    for (uint32_t t = in; t; t &= t - 1, ++e)
+      if (e < kr) taken |= t & (~t + 1u);
+  }
+  // emit in ascending candidate order
+  const int pt = __popc(taken);
+  const int incl = (int)wave_prefix_sum_dpp((uint32_t)pt);
+  const int total = __builtin_amdgcn_readlane(incl, 63);
+  int pos = incl - pt;
+  const SmallDiv div_nx(nx), div_ny(ny);
+  for (uint32_t t = taken; t; t &= t - 1, ++pos) {
+    if (pos < k) {
+      const int c = cbase + __builtin_ctz(t);
+      const int r3 = div_nx(c), xx = c - r3 * nx;
+      const int p = div_ny(r3), yy = r3 - p * ny;
+      out[pos] = p * nS + (ylo + yy) * nbx + gxlo + xx;
+    }
+  }
+  const int cnt = total < k ? total : k;
+  for (int q = cnt + lane; q < a.kmax; q += 64) out[q] = -1;
+  if (lane == 0) a.sel_cnt[row] = cnt;
+}
+
 // One wave: softmax (optional probs), exact top-k and the sorted index list
 // of query row `row`, whose candidates are scores s[0 .. n) enumerated as
 // c = (p*ny + (y - ylo))*nx + (x - xlo) over visible TBs p < nvis.
@@ -149,6 +281,10 @@ __device__ void select_row(const DraftArgs& a, const double* s, size_t row, int 
   const int yhi = ylo + ny - 1;
   const int nx = gxhi - gxlo + 1;
   const int n = nvis * ny * nx;
+  if (!a.probs && n <= kRegCand) {
+    select_row_regs(a, s, row, nvis, ylo, ny, gxlo, gxhi, n_keys, hist, lane);
+    return;
+  }
   const int k = topk_dev(a, n, n_keys);
   int32_t* out = a.sel_idx + row * a.kmax;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
