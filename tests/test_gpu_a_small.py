@@ -269,6 +269,7 @@ def dense(**kw) -> Workload:
     dict(ratio=(1, 1)),                                       # k = every candidate
     dict(topk_fixed=1),
     dict(frames=4, cache_frames=8),                           # 2 query TBs: 1,152 and 960
+    dict(batch=2, heads=3, width=120),                        # 12 x 15 blocks: partial row groups
 ])
 @pytest.mark.parametrize("split", [False, True], ids=["fused", "split"])
 def test_dense_draft_path(dev, case, split):
