@@ -24,14 +24,17 @@
  *                          write k/v blocks straight into the ring slots
  *                          (q's blocks only when q_blk is given)
  *   lcsa_draft_mask        masked draft scores, row softmax, per-row top-k
+ *                          (with an optional workspace of
+ *                          lcsa_draft_workspace_size bytes for whole-grid
+ *                          windows)
  *   lcsa_block_sparse_attn exact attention over the selected block pairs,
  *                          q read from q_blk (lcsa_block_sparse_attn_tok: q
  *                          read in token layout, so q_blk is never written)
  *   lcsa_kv_cache_evict    drop the oldest temporal blocks beyond capacity
  *
  * Conventions shared by every entry point:
- *   - All buffers are allocated and owned by the caller. The library never
- *     allocates or frees memory. Its only state is the thread-local text of
+ *   - All buffers are allocated and owned by the caller, workspaces
+ *     included. The library never allocates or frees memory. Its only state is the thread-local text of
  *     the last error and, for lcsa_block_sparse_attn_bwd_noalloc alone, a
  *     fixed scratch array on each GPU (see there).
  *   - Device pointers must be 16-byte aligned (LCSA_ERR_ALIGN otherwise).
