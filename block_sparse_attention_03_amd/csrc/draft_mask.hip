@@ -1596,8 +1596,10 @@ hipError_t launch_draft_mask(const DraftArgs& a, hipStream_t s) {
   // time. It pays from about a thousand candidates per row (FlashVSR+ global
   // layer at 4K, 2,040: 434 -> 244 us), where the row groups' re-reads of
   // the pooled keys dominate; below that the row-group path's many small
-  // workgroups win (768x1408 step, 264 candidates: 25 vs 44 us). The draft's
-  // float64 probabilities come from the paths below.
+  // workgroups win (768x1408 step, 264 candidates: 25 vs 44 us). With a
+  // workspace the dense path runs as the split pair instead (scores in device
+  // memory, one wave per row for the selection: 4K global layer 204-231 ->
+  // 134-140 us). The draft's float64 probabilities come from the paths below.
   if (takes_dense(a)) {
     if (a.scores) return a.D == 64 ? launch_split<64>(a, s) : launch_split<128>(a, s);
     return a.D == 64 ? launch_dense<64>(a, s) : launch_dense<128>(a, s);
