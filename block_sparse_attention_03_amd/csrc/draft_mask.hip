@@ -879,6 +879,80 @@ __device__ inline float wave_max_f32(float v) {
 constexpr int kDenseM = (kDenseMaxCand + 63) / 64;  // scores per lane in registers
 constexpr int kBoundaryMax = 256;                   // boundary-bin members ranked pairwise
 
+// Bin of x among 256 equal bins over [mn, mn + 256 / scale]: a monotone map
+// of the value, so every score in a higher bin is larger.
+__device__ __forceinline__ int bin256(float x, float mn, float scale) {
+  const int b = (int)((x - mn) * scale);
+  return b < 0 ? 0 : (b > 255 ? 255 : b);
+}
+
+// One wave: the 256-bin histogram of the scores v[m] of the slots set in
+// `valid` (position 0 is the top bin; slots without a candidate count into
+// spare entries past the histogram, so there is no branch per slot), and
+// the bin holding the k-th largest score: bstar, the candidates still to
+// take inside it (kr) and its size (cb). False when no bin holds it (only
+// with NaN scores). The histogram's memory is free again on return.
+template <int M>
+__device__ __forceinline__ bool boundary_bin(const float (&v)[M], uint64_t valid, float mn,
+                                             float scale, int k, uint32_t* hist, int lane,
+                                             int& bstar, int& kr, int& cb) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) hist[lane * 4 + q] = 0u;
+  wave_sync();
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+    atomicAdd(&hist[((valid >> m) & 1u) ? 255 - bin256(v[m], mn, scale) : 256 + (lane & 7)], 1u);
+  wave_sync();
+  uint32_t hb[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) hb[q] = hist[lane * 4 + q];
+  const uint32_t tot = hb[0] + hb[1] + hb[2] + hb[3];
+  uint32_t ab = wave_prefix_sum_dpp(tot) - tot;  // candidates in higher bins
+  int found = -1;
+  uint32_t fa = 0, fc = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (found < 0 && ab < (uint32_t)k && ab + hb[q] >= (uint32_t)k) {
+      found = 255 - (lane * 4 + q);
+      fa = ab;
+      fc = hb[q];
+    }
+    ab += hb[q];
+  }
+  const uint64_t bal = __ballot(found >= 0);
+  wave_sync();  // every lane has read the histogram
+  const int src = bal ? __ffsll((long long)bal) - 1 : 0;
+  bstar = __builtin_amdgcn_readlane(found, src);
+  kr = k - __builtin_amdgcn_readlane((int)fa, src);
+  cb = __builtin_amdgcn_readlane((int)fc, src);
+  return bal != 0;
+}
+
+// One wave: the cb boundary-bin members, scores s[i] and candidate ids
+// ids[i] (ascending), ranked by larger score, then equal score of lower id;
+// the members ranked below kr get the taken flag (top bit of ids[i]). True
+// when a float32 tie group straddles the kr-th place (then the float64
+// scores must decide).
+__device__ __forceinline__ bool rank_members(const float* s, uint32_t* ids, int cb, int kr,
+                                             int lane) {
+  bool straddle = false;
+  for (int i = lane; i < cb; i += 64) {
+    const float vi = s[i];
+    const uint32_t ci = ids[i] & 0x7fffffffu;
+    int gt = 0, eq_lo = 0, eq = 0;
+    for (int j = 0; j < cb; ++j) {  // ids of earlier rounds may carry the taken flag
+      const float vj = s[j];
+      gt += vj > vi;
+      eq += vj == vi;
+      eq_lo += (vj == vi) & ((ids[j] & 0x7fffffffu) < ci);
+    }
+    // a float32 tie group [gt, gt + eq) cut by the k-th place
+    straddle |= gt < kr && gt + eq > kr;
+    if (gt + eq_lo < kr) ids[i] = ci | 0x80000000u;  // taken
+  }
+  return __ballot(straddle) != 0;
+}
+
 // One wave, usual case: the row's float32 scores in registers, one 256-bin
 // histogram over [min, max] (bins are a monotone function of the value),
 // every candidate in a bin above the k-th one's bin taken, and the members
@@ -917,42 +991,9 @@ __device__ void select_dense(const DraftArgs& a, const int32_t* slot_tab, float*
     general = !(mx > mn) || !(scale < INFINITY);  // one value, or a range beyond float32
     int bstar = 0, kr = 0, cb = 0;
     if (!general) {
-      auto bin_of = [&](float x) {
-        const int b = (int)((x - mn) * scale);
-        return b < 0 ? 0 : (b > 255 ? 255 : b);
-      };
-#pragma unroll
-      for (int q = 0; q < 4; ++q) hist[lane * 4 + q] = 0u;
-      wave_sync();
-      // position 0: the top bin; slots without a candidate count into
-      // spare entries past the histogram (no branch per slot)
-#pragma unroll
-      for (int m = 0; m < M; ++m)
-        atomicAdd(&hist[((valid >> m) & 1u) ? 255 - bin_of(v[m]) : 256 + (lane & 7)], 1u);
-      wave_sync();
-      uint32_t hb[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) hb[q] = hist[lane * 4 + q];
-      const uint32_t tot = hb[0] + hb[1] + hb[2] + hb[3];
-      uint32_t ab = wave_prefix_sum_dpp(tot) - tot;
-      int found = -1;
-      uint32_t fa = 0, fc = 0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (found < 0 && ab < (uint32_t)k && ab + hb[q] >= (uint32_t)k) {
-          found = 255 - (lane * 4 + q);
-          fa = ab;
-          fc = hb[q];
-        }
-        ab += hb[q];
-      }
-      const uint64_t bal = __ballot(found >= 0);
-      wave_sync();  // histogram read before it becomes the id list
-      const int src = bal ? __ffsll((long long)bal) - 1 : 0;
-      bstar = __builtin_amdgcn_readlane(found, src);
-      kr = k - __builtin_amdgcn_readlane((int)fa, src);
-      cb = __builtin_amdgcn_readlane((int)fc, src);
-      general = bal == 0 || cb > kBoundaryMax;
+      auto bin_of = [&](float x) { return bin256(x, mn, scale); };
+      general = !boundary_bin<M>(v, valid, mn, scale, k, hist, lane, bstar, kr, cb) ||
+                cb > kBoundaryMax;
       if (!general) {
         // the boundary bin's members, in candidate order: scores over the
         // row's LDS scores (held in registers now), ids over the histogram
@@ -973,23 +1014,7 @@ __device__ void select_dense(const DraftArgs& a, const int32_t* slot_tab, float*
           base += __popcll(bb);
         }
         wave_sync();
-        // rank of each member: larger scores, then equal scores of lower id
-        bool straddle = false;
-        for (int i = lane; i < cb; i += 64) {
-          const float vi = s[i];
-          const uint32_t ci = ids[i] & 0x7fffffffu;
-          int gt = 0, eq_lo = 0, eq = 0;
-          for (int j = 0; j < cb; ++j) {  // ids of earlier rounds may carry the taken flag
-            const float vj = s[j];
-            gt += vj > vi;
-            eq += vj == vi;
-            eq_lo += (vj == vi) & ((ids[j] & 0x7fffffffu) < ci);
-          }
-          // a float32 tie group [gt, gt + eq) cut by the k-th place
-          straddle |= gt < kr && gt + eq > kr;
-          if (gt + eq_lo < kr) ids[i] = ci | 0x80000000u;  // taken
-        }
-        general = __ballot(straddle) != 0;
+        general = rank_members(s, ids, cb, kr, lane);
         wave_sync();
         if (!general) {
           base = 0;
@@ -1078,41 +1103,10 @@ __device__ void select_split(const DraftArgs& a, const int32_t* slot_tab, const 
     const float scale = 256.f / (mx - mn);
     bool general = !(mx > mn) || !(scale < INFINITY);  // one value, or a range beyond float32
     if (!general) {
-      auto bin_of = [&](float x) {
-        const int b = (int)((x - mn) * scale);
-        return b < 0 ? 0 : (b > 255 ? 255 : b);
-      };
-#pragma unroll
-      for (int q = 0; q < 4; ++q) hist[lane * 4 + q] = 0u;
-      wave_sync();
-      // position 0: the top bin; slots without a candidate count into spare entries
-#pragma unroll
-      for (int m = 0; m < MX; ++m)
-        atomicAdd(&hist[((valid >> m) & 1u) ? 255 - bin_of(v[m]) : 256 + (lane & 7)], 1u);
-      wave_sync();
-      uint32_t hb[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) hb[q] = hist[lane * 4 + q];
-      const uint32_t tot = hb[0] + hb[1] + hb[2] + hb[3];
-      uint32_t ab = wave_prefix_sum_dpp(tot) - tot;
-      int found = -1;
-      uint32_t fa = 0, fc = 0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (found < 0 && ab < (uint32_t)k && ab + hb[q] >= (uint32_t)k) {
-          found = 255 - (lane * 4 + q);
-          fa = ab;
-          fc = hb[q];
-        }
-        ab += hb[q];
-      }
-      const uint64_t bal = __ballot(found >= 0);
-      wave_sync();  // histogram read before it becomes the id list
-      const int srcl = bal ? __ffsll((long long)bal) - 1 : 0;
-      const int bstar = __builtin_amdgcn_readlane(found, srcl);
-      const int kr = k - __builtin_amdgcn_readlane((int)fa, srcl);
-      const int cb = __builtin_amdgcn_readlane((int)fc, srcl);
-      general = bal == 0 || cb > kBoundaryMax;
+      auto bin_of = [&](float x) { return bin256(x, mn, scale); };
+      int bstar = 0, kr = 0, cb = 0;
+      general = !boundary_bin<MX>(v, valid, mn, scale, k, hist, lane, bstar, kr, cb) ||
+                cb > kBoundaryMax;
       if (!general) {
         uint64_t member = 0;
 #pragma unroll
@@ -1142,23 +1136,7 @@ __device__ void select_split(const DraftArgs& a, const int32_t* slot_tab, const 
             }
           }
           wave_sync();
-          // rank of each member: larger scores, then equal scores of lower id
-          bool straddle = false;
-          for (int i = lane; i < cb; i += 64) {
-            const float vi = s[i];
-            const uint32_t ci = ids[i] & 0x7fffffffu;
-            int gt = 0, eq_lo = 0, eq = 0;
-            for (int j = 0; j < cb; ++j) {  // ids of earlier rounds may carry the taken flag
-              const float vj = s[j];
-              gt += vj > vi;
-              eq += vj == vi;
-              eq_lo += (vj == vi) & ((ids[j] & 0x7fffffffu) < ci);
-            }
-            // a float32 tie group [gt, gt + eq) cut by the k-th place
-            straddle |= gt < kr && gt + eq > kr;
-            if (gt + eq_lo < kr) ids[i] = ci | 0x80000000u;  // taken
-          }
-          general = __ballot(straddle) != 0;
+          general = rank_members(s, ids, cb, kr, lane);
           wave_sync();
           if (!general) {
             pos = mbase;
