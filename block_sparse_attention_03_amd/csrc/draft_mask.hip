@@ -9,398 +9,33 @@
 // the current and past temporal blocks; Key design 3: two border rules.
 //
 // No dense mask exists: candidates are enumerated from block coordinates.
-// Two scoring layouts share one selection routine:
+// The scoring layouts (kernels below) share the selections of
+// draft_select.h:
 //  * tile path (up to 768 candidates per row, e.g. the 11x11 window): a
 //    workgroup scores a 4x4 tile of query blocks against the union of their
 //    windows on the fp64 matrix cores;
-//  * row-group path (larger windows): a workgroup scores `gx` query rows of
-//    one block row with the vector ALU, each pooled key fetched once.
-// Scores land in LDS at each row's candidate index; then one wave per row
-// takes the softmax and selects exactly k candidates (value-range bucket
-// select, ties to the lower logical id). Scores are float64 so the
-// selection is decided on values equal to the exact ones up to summation
-// order. Rows are ranked on the raw dot products: dividing by sqrt(D) is
-// monotone and leaves the order as it is, so the division is only applied
-// to the softmax written to probs.
+//  * row-group path (larger windows, small whole-grid windows, and any call
+//    that asks for the probabilities): a workgroup scores `gx` query rows of
+//    one block row with the vector ALU, each pooled key fetched once;
+//  * dense path (a window covering the grid, 1,024 to 2,304 candidates):
+//    16 rows of a temporal block against every visible key on the fp64
+//    matrix cores, scores kept in LDS as float32; with a workspace, the split
+//    pair instead (64-row scoring workgroups writing float32 scores to device
+//    memory, then one wave per row selecting).
+// Scores land at each row's candidate index; then one wave per row takes the
+// softmax (when asked for) and selects exactly k candidates, ties to the
+// lower logical id. The window paths keep float64 scores, so the selection
+// is decided on values equal to the exact ones up to summation order; the
+// dense paths rank float32 scores and settle a float32 tie at the k-th place
+// on recomputed float64 scores. Rows are ranked on the raw dot products:
+// dividing by sqrt(D) is monotone and leaves the order as it is, so the
+// division is only applied to the softmax written to probs.
+#include "draft_select.h"
 #include "lcsa_kernels.h"
 #include "lcsa_window.h"
 
 namespace lcsa {
 namespace {
-
-// XCD-contiguous task order: workgroups are dealt to the 8 XCDs in turn, so
-// XCD x takes tasks [x*per, (x+1)*per) and neighbouring query tiles, whose
-// windows share pooled keys, hit the same L2. Launch 8*per workgroups;
-// returns -1 for the padding ones.
-__device__ inline int xcd_task(int n_tasks) {
-  const int per = (n_tasks + 7) / 8;
-  const int t = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
-  return t < n_tasks ? t : -1;
-}
-
-// The view's ring slots, copied to LDS at kernel start. The keys of one
-// wave can lie in different temporal blocks, and a per-lane index into the
-// kernel-argument array compiles to a vector load from argument memory
-// followed by a wait on every outstanding load (which serialised the key
-// prefetch); a ds_read of this table costs neither. Needs a barrier before
-// the first read.
-__device__ inline void stage_slots(const RingView& v, int32_t* tab) {
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < LCSA_MAX_SLOTS; ++i)
-    if (tid == i) tab[i] = v.slot[i];
-}
-
-// Quotient of a small non-negative int by a divisor d >= 1 through an fp32
-// reciprocal, exact for n < 2^22: (n + 0.5) / d lies at least 0.5 / d from
-// an integer, and the two correctly rounded fp32 steps (1/d, then the
-// product) move it by less than (n + 0.5) * 2^-23 / d < 0.5 / d.
-struct SmallDiv {
-  float inv;
-  __device__ explicit SmallDiv(int d) : inv(1.0f / (float)d) {}
-  __device__ int operator()(int n) const { return (int)(((float)n + 0.5f) * inv); }
-};
-
-__device__ inline void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-__device__ inline double wave_sum_f64(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-
-__device__ inline int32_t topk_dev(const DraftArgs& a, int64_t n_allowed, int64_t n_keys) {
-  if (n_allowed <= 0) return 0;
-  if (a.topk_fixed > 0) return (int32_t)(a.topk_fixed < n_allowed ? a.topk_fixed : n_allowed);
-  const int64_t base = a.ratio_base == 0 ? n_allowed : n_keys;
-  // the host reduced num/den and checked num < 2^32, so base * num < 2^56
-  const uint64_t kk = ((uint64_t)base * (uint64_t)a.ratio_num) / (uint64_t)a.ratio_den;
-  const int64_t k = kk > (uint64_t)n_allowed ? n_allowed : (int64_t)kk;
-  return (int32_t)(k < 1 ? 1 : k);
-}
-
-// ---- DPP wave primitives (gfx9 row operations: no LDS round trip) --------
-template <int CTRL, int ROWS>
-__device__ inline double dpp_keep(double v) {  // lanes outside ROWS keep their value
-  const int lo = __double2loint(v), hi = __double2hiint(v);
-  return __hiloint2double(__builtin_amdgcn_update_dpp(hi, hi, CTRL, ROWS, 0xF, false),
-                          __builtin_amdgcn_update_dpp(lo, lo, CTRL, ROWS, 0xF, false));
-}
-
-__device__ inline double lane63_f64(double v) {
-  return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), 63),
-                          __builtin_amdgcn_readlane(__double2loint(v), 63));
-}
-
-// quad_perm [1,0,3,2], [2,3,0,1], row_half_mirror, row_mirror, row_bcast:15,
-// row_bcast:31: the full-wave result ends in lane 63.
-__device__ inline double wave_max_dpp(double v) {
-  v = fmax(v, dpp_keep<0xB1, 0xF>(v));
-  v = fmax(v, dpp_keep<0x4E, 0xF>(v));
-  v = fmax(v, dpp_keep<0x141, 0xF>(v));
-  v = fmax(v, dpp_keep<0x140, 0xF>(v));
-  v = fmax(v, dpp_keep<0x142, 0xA>(v));
-  v = fmax(v, dpp_keep<0x143, 0xC>(v));
-  return lane63_f64(v);
-}
-
-__device__ inline double wave_min_dpp(double v) {
-  v = fmin(v, dpp_keep<0xB1, 0xF>(v));
-  v = fmin(v, dpp_keep<0x4E, 0xF>(v));
-  v = fmin(v, dpp_keep<0x141, 0xF>(v));
-  v = fmin(v, dpp_keep<0x140, 0xF>(v));
-  v = fmin(v, dpp_keep<0x142, 0xA>(v));
-  v = fmin(v, dpp_keep<0x143, 0xC>(v));
-  return lane63_f64(v);
-}
-
-// Inclusive prefix sum over lanes 0..63 (row_shr 1,2,4,8 with zero fill,
-// then row_bcast:15 / :31 to carry across rows).
-__device__ inline uint32_t wave_prefix_sum_dpp(uint32_t x) {
-  int v = (int)x;
-  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);
-  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);
-  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);
-  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);
-  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);
-  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);
-  return (uint32_t)v;
-}
-
-// Register form of select_row, for rows of at most kRegCand candidates when
-// no probabilities are asked for. Lane l holds the candidates
-// [l M, l M + M) (M = ceil(n / 64)) of the row's float64 scores in
-// registers, so each refinement level is one pass over registers rather
-// than over LDS, and the kept ids go to their places through prefix sums of
-// per-lane counts (candidate order = ascending logical id), with no ballot
-// per 64 candidates. Same result as select_row: the k largest scores,
-// equal scores taken lowest index first.
-constexpr int kRegM = 8;
-constexpr int kRegCand = 64 * kRegM;
-
-__device__ void select_row_regs(const DraftArgs& a, const double* s, size_t row, int nvis,
-                                int ylo, int ny, int gxlo, int gxhi, int64_t n_keys,
-                                uint32_t* hist, int lane) {
-  const int nbx = a.nbx, nS = a.nby * nbx;
-  const int nx = gxhi - gxlo + 1;
-  const int n = nvis * ny * nx;
-  const int k = topk_dev(a, n, n_keys);
-  int32_t* out = a.sel_idx + row * a.kmax;
-  const int M = (n + 63) >> 6;
-  const int cbase = lane * M;
-  double v[kRegM];
-  uint32_t valid = 0;
-  double lo = INFINITY, hi = -INFINITY;
-#pragma unroll
-  for (int m = 0; m < kRegM; ++m) {
-    const bool in_row = m < M && cbase + m < n;
-    v[m] = s[in_row ? cbase + m : 0];
-    if (in_row && v[m] == v[m]) {  // NaN scores are never kept
-      valid |= 1u << m;
-      lo = fmin(lo, v[m]);
-      hi = fmax(hi, v[m]);
-    }
-  }
-  lo = wave_min_dpp(lo);
-  hi = wave_max_dpp(hi);
-  const int n_valid = __builtin_amdgcn_readlane((int)wave_prefix_sum_dpp(__popc(valid)), 63);
-  uint32_t taken = 0, in = 0;  // in: undecided candidates, all in [lo, hi]
-  int kr = 0;
-  if (k >= n_valid) {
-    taken = valid;
-  } else if (k > 0) {
-    in = valid;
-    kr = k;
-    for (int level = 0; level <= n && lo < hi; ++level) {
-      const double scale = 256.0 / (hi - lo);
-      auto bin_of = [&](double x) {
-        const int b = (int)((x - lo) * scale);
-        return b < 0 ? 0 : (b > 255 ? 255 : b);
-      };
-#pragma unroll
-      for (int q = 0; q < 4; ++q) hist[lane * 4 + q] = 0u;
-      wave_sync();
-#pragma unroll
-      for (int m = 0; m < kRegM; ++m)
-        if ((in >> m) & 1u) atomicAdd(&hist[255 - bin_of(v[m])], 1u);  // position 0: top bin
-      wave_sync();
-      uint32_t hb[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) hb[q] = hist[lane * 4 + q];
-      const uint32_t tot = hb[0] + hb[1] + hb[2] + hb[3];
-      uint32_t ab = wave_prefix_sum_dpp(tot) - tot;  // candidates in higher bins
-      int found = -1;
-      uint32_t fa = 0, fc = 0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (found < 0 && ab < (uint32_t)kr && ab + hb[q] >= (uint32_t)kr) {
-          found = 255 - (lane * 4 + q);
-          fa = ab;
-          fc = hb[q];
-        }
-        ab += hb[q];
-      }
-      const uint64_t bal = __ballot(found >= 0);
-      wave_sync();
-      if (bal == 0) break;  // unreachable: 1 <= kr < candidates in range
-      const int src = __ffsll((long long)bal) - 1;
-      const int bin = __builtin_amdgcn_readlane(found, src);
-      kr -= __builtin_amdgcn_readlane((int)fa, src);
-      const int cb = __builtin_amdgcn_readlane((int)fc, src);
-      // above the bin: kept; below: dropped; in it: the new range
-      double nlo = INFINITY, nhi = -INFINITY;
-#pragma unroll
-      for (int m = 0; m < kRegM; ++m) {
-        if ((in >> m) & 1u) {
-          const int bn = bin_of(v[m]);
-          if (bn > bin) {
-            taken |= 1u << m;
-            in &= ~(1u << m);
-          } else if (bn < bin) {
-            in &= ~(1u << m);
-          } else {
-            nlo = fmin(nlo, v[m]);
-            nhi = fmax(nhi, v[m]);
-          }
-        }
-      }
-      lo = wave_min_dpp(nlo);
-      hi = wave_max_dpp(nhi);
-      if (cb == kr) {  // the whole bin is kept
-        taken |= in;
-        in = 0;
-        kr = 0;
-        break;
-      }
-    }
-    // the undecided candidates now share one value: the first kr of them
-    // in candidate order are kept
-    const int pe = __popc(in);
-    int e = (int)wave_prefix_sum_dpp((uint32_t)pe) - pe;
-    for (uint32_t t = in; t; t &= t - 1, ++e)
-      if (e < kr) taken |= t & (~t + 1u);
-  }
-  // emit in ascending candidate order
-  const int pt = __popc(taken);
-  const int incl = (int)wave_prefix_sum_dpp((uint32_t)pt);
-  const int total = __builtin_amdgcn_readlane(incl, 63);
-  int pos = incl - pt;
-  const SmallDiv div_nx(nx), div_ny(ny);
-  for (uint32_t t = taken; t; t &= t - 1, ++pos) {
-    if (pos < k) {
-      const int c = cbase + __builtin_ctz(t);
-      const int r3 = div_nx(c), xx = c - r3 * nx;
-      const int p = div_ny(r3), yy = r3 - p * ny;
-      out[pos] = p * nS + (ylo + yy) * nbx + gxlo + xx;
-    }
-  }
-  const int cnt = total < k ? total : k;
-  for (int q = cnt + lane; q < a.kmax; q += 64) out[q] = -1;
-  if (lane == 0) a.sel_cnt[row] = cnt;
-}
-
-// One wave: softmax (optional probs), exact top-k and the sorted index list
-// of query row `row`, whose candidates are scores s[0 .. n) enumerated as
-// c = (p*ny + (y - ylo))*nx + (x - xlo) over visible TBs p < nvis.
-//
-// Exact top-k by value-range bucketing: the candidates in [lo, hi] are
-// binned into 256 equal-width bins (a monotone map of the value, so every
-// key in a higher bin is larger than every key in a lower one); the bin
-// holding the k-th largest becomes the new [lo, hi] (its own min and max)
-// and is refined again, until it is kept whole or holds one value, whose
-// copies are then taken lowest index first. Each level removes at least
-// one distinct value, so the loop ends; smooth score rows need 1-2 levels.
-__device__ void select_row(const DraftArgs& a, const double* s, size_t row, int nvis, int ylo,
-                           int ny, int gxlo, int gxhi, int64_t n_keys, uint32_t* hist, int lane,
-                           double sqrt_d) {
-  const int nby = a.nby, nbx = a.nbx, nS = nby * nbx;
-  const int yhi = ylo + ny - 1;
-  const int nx = gxhi - gxlo + 1;
-  const int n = nvis * ny * nx;
-  if (!a.probs && n <= kRegCand) {
-    select_row_regs(a, s, row, nvis, ylo, ny, gxlo, gxhi, n_keys, hist, lane);
-    return;
-  }
-  const int k = topk_dev(a, n, n_keys);
-  int32_t* out = a.sel_idx + row * a.kmax;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-
-  double lo = INFINITY, hi = -INFINITY;
-  for (int c = lane; c < n; c += 64) {
-    lo = fmin(lo, s[c]);
-    hi = fmax(hi, s[c]);
-  }
-  lo = wave_min_dpp(lo);
-  hi = wave_max_dpp(hi);
-
-  if (a.probs) {
-    double* pr = a.probs + row * n_keys;
-    double z = 0.0;
-    for (int c = lane; c < n; c += 64) z += exp((s[c] - hi) / sqrt_d);
-    z = wave_sum_f64(z);
-    for (int64_t j = lane; j < n_keys; j += 64) {
-      const int p = (int)(j / nS), rem = (int)(j % nS);
-      const int y = rem / nbx, x = rem % nbx;
-      double val = 0.0;
-      if (p < nvis && y >= ylo && y <= yhi && x >= gxlo && x <= gxhi)
-        val = exp((s[(p * ny + (y - ylo)) * nx + (x - gxlo)] - hi) / sqrt_d) / z;
-      pr[j] = val;
-    }
-  }
-
-  int kr = k;
-  if (k >= n) {  // every candidate kept: the range already covers them all
-    kr = n;
-  } else if (k > 0) {
-    for (int level = 0; level <= n && lo < hi; ++level) {
-      const double scale = 256.0 / (hi - lo);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) hist[lane * 4 + q] = 0u;
-      wave_sync();
-      for (int c = lane; c < n; c += 64) {
-        const double v = s[c];
-        if (v >= lo && v <= hi) {
-          int bn = (int)((v - lo) * scale);
-          bn = bn < 0 ? 0 : (bn > 255 ? 255 : bn);
-          atomicAdd(&hist[255 - bn], 1u);  // reversed: position 0 is the top bin
-        }
-      }
-      wave_sync();
-      uint32_t hb[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) hb[q] = hist[lane * 4 + q];
-      const uint32_t tot = hb[0] + hb[1] + hb[2] + hb[3];
-      uint32_t ab = wave_prefix_sum_dpp(tot) - tot;  // candidates in higher bins
-      int found = -1;
-      uint32_t fa = 0, fc = 0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (found < 0 && ab < (uint32_t)kr && ab + hb[q] >= (uint32_t)kr) {
-          found = 255 - (lane * 4 + q);
-          fa = ab;
-          fc = hb[q];
-        }
-        ab += hb[q];
-      }
-      const uint64_t bal = __ballot(found >= 0);
-      wave_sync();
-      if (bal == 0) break;  // only with NaN scores; the emit below stays in bounds
-      const int src = __ffsll((long long)bal) - 1;
-      const int bin = __builtin_amdgcn_readlane(found, src);
-      const int ca = __builtin_amdgcn_readlane((int)fa, src);
-      const int cb = __builtin_amdgcn_readlane((int)fc, src);
-      kr -= ca;
-      double nlo = INFINITY, nhi = -INFINITY;
-      for (int c = lane; c < n; c += 64) {
-        const double v = s[c];
-        if (v >= lo && v <= hi) {
-          int bn = (int)((v - lo) * scale);
-          bn = bn < 0 ? 0 : (bn > 255 ? 255 : bn);
-          if (bn == bin) {
-            nlo = fmin(nlo, v);
-            nhi = fmax(nhi, v);
-          }
-        }
-      }
-      lo = wave_min_dpp(nlo);
-      hi = wave_max_dpp(nhi);
-      if (cb == kr) break;  // the whole bin is kept
-    }
-  }
-  // Emit in ascending candidate order (= ascending logical id): values above
-  // the final range, then the first kr values inside it.
-  int eq_before = 0, sel_before = 0;
-  const SmallDiv div_nx(nx), div_ny(ny);
-  if (k > 0) {
-    for (int base = 0; base < n; base += 64) {
-      const int c = base + lane;
-      const bool valid = c < n;
-      const double v = valid ? s[c] : 0.0;
-      const bool gt = valid && v > hi;
-      const bool eq = valid && v >= lo && v <= hi;
-      const uint64_t beq = __ballot(eq);
-      const int r = eq_before + __popcll(beq & lt_mask);
-      const bool want = gt || (eq && r < kr);
-      const int pos = sel_before + __popcll(__ballot(want) & lt_mask);
-      const bool sel = want && pos < k;  // never more than k (only NaN scores could ask)
-      const uint64_t bsel = __ballot(sel);
-      if (sel) {
-        const int r3 = div_nx(c), xx = c - r3 * nx;
-        const int p = div_ny(r3), yy = r3 - p * ny;
-        out[pos] = p * nS + (ylo + yy) * nbx + gxlo + xx;
-      }
-      eq_before += __popcll(beq);
-      sel_before += __popcll(bsel);
-    }
-  }
-  for (int pos = sel_before + lane; pos < a.kmax; pos += 64) out[pos] = -1;
-  if (lane == 0) a.sel_cnt[row] = sel_before;
-}
-
 // NW waves per workgroup: one key of the group's union per thread, so a
 // union of up to 64 * NW keys is scored in one round of D loads per thread.
 template <int GX, int D, int NW>
@@ -649,533 +284,7 @@ __global__ __launch_bounds__(64 * kTileWaves, 4) void draft_tile_kernel(DraftArg
 // float64 scores are then recomputed (one wave-wide dot product each) and
 // the same selection runs on them.
 constexpr int kDenseWaves = 8;               // 16 rows: two per wave in the selection
-constexpr int kDenseMaxCand = 2304;          // candidates per row held in LDS
 constexpr int kDenseMinCand = 1024;          // below this the row-group path is faster
-constexpr int kHistStride = 264;             // per-wave histogram / list, 8 spare entries
-
-// Order-preserving maps of float32 / float64 to unsigned integers.
-__device__ inline uint32_t ordered_key(float v) {
-  const uint32_t u = __float_as_uint(v);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ inline uint64_t ordered_key(double v) {
-  const uint64_t u = (uint64_t)__double_as_longlong(v);
-  return (u >> 63) ? ~u : (u | (1ull << 63));
-}
-
-template <int CTRL, int ROWS>
-__device__ inline uint32_t dpp_keep32(uint32_t v) {  // lanes outside ROWS keep their value
-  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROWS, 0xF, false);
-}
-
-// Full-wave min / max of unsigned keys and floats (the same DPP steps as the
-// float64 reductions above; the result is read from lane 63).
-__device__ inline uint32_t wave_min_u(uint32_t v) {
-  v = min(v, dpp_keep32<0xB1, 0xF>(v));
-  v = min(v, dpp_keep32<0x4E, 0xF>(v));
-  v = min(v, dpp_keep32<0x141, 0xF>(v));
-  v = min(v, dpp_keep32<0x140, 0xF>(v));
-  v = min(v, dpp_keep32<0x142, 0xA>(v));
-  v = min(v, dpp_keep32<0x143, 0xC>(v));
-  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
-}
-__device__ inline uint32_t wave_max_u(uint32_t v) {
-  v = max(v, dpp_keep32<0xB1, 0xF>(v));
-  v = max(v, dpp_keep32<0x4E, 0xF>(v));
-  v = max(v, dpp_keep32<0x141, 0xF>(v));
-  v = max(v, dpp_keep32<0x140, 0xF>(v));
-  v = max(v, dpp_keep32<0x142, 0xA>(v));
-  v = max(v, dpp_keep32<0x143, 0xC>(v));
-  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
-}
-__device__ inline int wave_sum_i(int v) {
-  return __builtin_amdgcn_readlane((int)wave_prefix_sum_dpp((uint32_t)v), 63);
-}
-
-// Exact top-kr over the keys ks[lane + 64 m] (in LDS) of the slots m set in
-// `in`, restricted to [klo, khi]. On return the keys above khi are taken,
-// and of those in [klo, khi] (n_in of them) the first kr in candidate order;
-// either kr == n_in (all taken) or klo == khi (one value). Radix steps of 8
-// bits starting below the highest bit where the range's smallest and
-// largest keys differ, so the first histogram already spreads over the
-// occupied range; every step fixes at least 8 more bits.
-__device__ void narrow_range(const uint32_t* ks, int n, uint64_t in, uint32_t& klo, uint32_t& khi,
-                             int& kr, int& n_in, uint32_t* hist, int lane) {
-  n_in = 0;
-  for (int level = 0; level < 6; ++level) {
-    uint32_t mn = ~0u, mx = 0u;
-    int cnt = 0;
-    for (int m = 0; 64 * m < n; ++m) {
-      const uint32_t kv = ks[lane + 64 * m];
-      if (((in >> m) & 1u) && kv >= klo && kv <= khi) {
-        mn = min(mn, kv);
-        mx = max(mx, kv);
-        ++cnt;
-      }
-    }
-    mn = wave_min_u(mn);
-    mx = wave_max_u(mx);
-    cnt = wave_sum_i(cnt);
-    n_in = cnt;
-    if (cnt == 0) return;
-    klo = mn;
-    khi = mx;
-    if (cnt <= kr) {
-      kr = cnt;
-      return;
-    }
-    if (mn == mx) return;
-    const int top = 32 - __builtin_clz(mn ^ mx);
-    const int shift = top > 8 ? top - 8 : 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) hist[lane * 4 + q] = 0u;
-    wave_sync();
-    for (int m = 0; 64 * m < n; ++m) {
-      const uint32_t kv = ks[lane + 64 * m];
-      if (((in >> m) & 1u) && kv >= klo && kv <= khi)
-        atomicAdd(&hist[255 - (int)((kv >> shift) & 255u)], 1u);  // position 0: top digit
-    }
-    wave_sync();
-    uint32_t hb[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) hb[q] = hist[lane * 4 + q];
-    const uint32_t tot = hb[0] + hb[1] + hb[2] + hb[3];
-    uint32_t ab = wave_prefix_sum_dpp(tot) - tot;  // keys in higher digits
-    int found = -1;
-    uint32_t fa = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (found < 0 && ab < (uint32_t)kr && ab + hb[q] >= (uint32_t)kr) {
-        found = 255 - (lane * 4 + q);
-        fa = ab;
-      }
-      ab += hb[q];
-    }
-    const uint64_t bal = __ballot(found >= 0);
-    wave_sync();
-    if (bal == 0) return;  // unreachable: 1 <= kr < cnt
-    const int src = __ffsll((long long)bal) - 1;
-    const uint32_t digit = (uint32_t)__builtin_amdgcn_readlane(found, src);
-    kr -= __builtin_amdgcn_readlane((int)fa, src);
-    const uint32_t above = shift + 8 >= 32 ? 0u : (~0u << (shift + 8));
-    klo = (mn & above) | (digit << shift);
-    khi = klo | ((1u << shift) - 1u);
-  }
-}
-
-// float64 score of candidate c (key id) against the pooled query qrow, in
-// one fixed summation order.
-template <int D>
-__device__ inline double dense_score64(const DraftArgs& a, const int32_t* slot_tab,
-                                       const double* qrow, size_t bh, int nS,
-                                       const SmallDiv& div_ns, int c) {
-  const int p = div_ns(c), sp = c - p * nS;
-  const double* kp = a.kpool_ring + (bh * a.n_slots + slot_tab[p]) * (size_t)D * nS + sp;
-  double w = 0.0;
-#pragma unroll 4
-  for (int d = 0; d < D; ++d) w = fma(qrow[d], kp[(size_t)d * nS], w);
-  return w;
-}
-
-// One wave, general form: top-k and the sorted index list of query row `row`
-// from its n float32 scores in LDS (candidate index = key id), which the
-// selection overwrites with its 32-bit keys. It runs in stages: the float32 score,
-// then, only for candidates tied at the k-th place, the high and the low
-// half of the float64 score (recomputed from the pooled query qrow and the
-// pooled ring); candidates still tied after that are exact ties and go to
-// the lower id.
-template <int D>
-__device__ void select_dense_staged(const DraftArgs& a, const int32_t* slot_tab, float* s, int n,
-                                    size_t row, size_t bh, int nS, int64_t n_keys,
-                                    const double* qrow, uint32_t* hist, int lane) {
-  const int k = topk_dev(a, n, n_keys);
-  int32_t* out = a.sel_idx + row * a.kmax;
-  uint32_t* ks = reinterpret_cast<uint32_t*>(s);
-  uint64_t live = 0;  // bit m: slot m is still undecided (non-NaN candidate)
-  for (int m = 0; 64 * m < n; ++m) {
-    const int c = lane + 64 * m;
-    if (c < n) {
-      const float v = s[c];
-      ks[c] = ordered_key(v);
-      if (!__builtin_isnan(v)) live |= 1ull << m;
-    }
-  }
-  uint64_t taken = 0;  // bit m: slot m is selected
-  int kr = k;
-  const SmallDiv div_ns(nS);
-  for (int stage = 0; stage < 3 && kr > 0; ++stage) {
-    if (stage > 0) {  // the next finer key of the tied candidates
-      for (int m = 0; 64 * m < n; ++m) {
-        if ((live >> m) & 1u) {
-          const int c = lane + 64 * m;
-          const double w = dense_score64<D>(a, slot_tab, qrow, bh, nS, div_ns, c);
-          const uint64_t k64 = ordered_key(w);
-          ks[c] = stage == 1 ? (uint32_t)(k64 >> 32) : (uint32_t)k64;
-          if (__builtin_isnan(w)) live &= ~(1ull << m);
-        }
-      }
-    }
-    wave_sync();
-    uint32_t lo = 0, hi = ~0u;
-    int n_in = 0;
-    narrow_range(ks, n, live, lo, hi, kr, n_in, hist, lane);
-    uint64_t in_range = 0;
-    for (int m = 0; 64 * m < n; ++m) {
-      if ((live >> m) & 1u) {
-        const uint32_t kv = ks[lane + 64 * m];
-        if (kv > hi) taken |= 1ull << m;
-        else if (kv >= lo) in_range |= 1ull << m;
-      }
-    }
-    live = in_range;
-    if (n_in <= kr) {  // the whole range is kept
-      taken |= live;
-      live = 0;
-      kr = 0;
-    }
-  }
-  // Emit in ascending candidate order: the taken ones, then the first kr of
-  // the exact ties left in `live`.
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  int eq_before = 0, sel_before = 0;
-  if (k > 0) {
-    for (int m = 0; 64 * m < n; ++m) {
-      const bool gt = (taken >> m) & 1u;
-      const bool eq = (live >> m) & 1u;
-      const uint64_t beq = __ballot(eq);
-      const int r = eq_before + __popcll(beq & lt_mask);
-      const bool want = gt || (eq && r < kr);
-      const int pos = sel_before + __popcll(__ballot(want) & lt_mask);
-      const bool sel = want && pos < k;  // never more than k
-      const uint64_t bsel = __ballot(sel);
-      if (sel) out[pos] = lane + 64 * m;
-      eq_before += __popcll(beq);
-      sel_before += __popcll(bsel);
-    }
-  }
-  for (int pos = sel_before + lane; pos < a.kmax; pos += 64) out[pos] = -1;
-  if (lane == 0) a.sel_cnt[row] = sel_before;
-}
-
-__device__ inline float wave_min_f32(float v) {
-  v = fminf(v, __uint_as_float(dpp_keep32<0xB1, 0xF>(__float_as_uint(v))));
-  v = fminf(v, __uint_as_float(dpp_keep32<0x4E, 0xF>(__float_as_uint(v))));
-  v = fminf(v, __uint_as_float(dpp_keep32<0x141, 0xF>(__float_as_uint(v))));
-  v = fminf(v, __uint_as_float(dpp_keep32<0x140, 0xF>(__float_as_uint(v))));
-  v = fminf(v, __uint_as_float(dpp_keep32<0x142, 0xA>(__float_as_uint(v))));
-  v = fminf(v, __uint_as_float(dpp_keep32<0x143, 0xC>(__float_as_uint(v))));
-  return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 63));
-}
-__device__ inline float wave_max_f32(float v) {
-  v = fmaxf(v, __uint_as_float(dpp_keep32<0xB1, 0xF>(__float_as_uint(v))));
-  v = fmaxf(v, __uint_as_float(dpp_keep32<0x4E, 0xF>(__float_as_uint(v))));
-  v = fmaxf(v, __uint_as_float(dpp_keep32<0x141, 0xF>(__float_as_uint(v))));
-  v = fmaxf(v, __uint_as_float(dpp_keep32<0x140, 0xF>(__float_as_uint(v))));
-  v = fmaxf(v, __uint_as_float(dpp_keep32<0x142, 0xA>(__float_as_uint(v))));
-  v = fmaxf(v, __uint_as_float(dpp_keep32<0x143, 0xC>(__float_as_uint(v))));
-  return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 63));
-}
-
-constexpr int kDenseM = (kDenseMaxCand + 63) / 64;  // scores per lane in registers
-constexpr int kBoundaryMax = 256;                   // boundary-bin members ranked pairwise
-
-// Bin of x among 256 equal bins over [mn, mn + 256 / scale]: a monotone map
-// of the value, so every score in a higher bin is larger.
-__device__ __forceinline__ int bin256(float x, float mn, float scale) {
-  const int b = (int)((x - mn) * scale);
-  return b < 0 ? 0 : (b > 255 ? 255 : b);
-}
-
-// One wave: the 256-bin histogram of the scores v[m] of the slots set in
-// `valid` (position 0 is the top bin; slots without a candidate count into
-// spare entries past the histogram, so there is no branch per slot), and
-// the bin holding the k-th largest score: bstar, the candidates still to
-// take inside it (kr) and its size (cb). False when no bin holds it (only
-// with NaN scores). The histogram's memory is free again on return.
-template <int M>
-__device__ __forceinline__ bool boundary_bin(const float (&v)[M], uint64_t valid, float mn,
-                                             float scale, int k, uint32_t* hist, int lane,
-                                             int& bstar, int& kr, int& cb) {
-#pragma unroll
-  for (int q = 0; q < 4; ++q) hist[lane * 4 + q] = 0u;
-  wave_sync();
-#pragma unroll
-  for (int m = 0; m < M; ++m)
-    atomicAdd(&hist[((valid >> m) & 1u) ? 255 - bin256(v[m], mn, scale) : 256 + (lane & 7)], 1u);
-  wave_sync();
-  uint32_t hb[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) hb[q] = hist[lane * 4 + q];
-  const uint32_t tot = hb[0] + hb[1] + hb[2] + hb[3];
-  uint32_t ab = wave_prefix_sum_dpp(tot) - tot;  // candidates in higher bins
-  int found = -1;
-  uint32_t fa = 0, fc = 0;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    if (found < 0 && ab < (uint32_t)k && ab + hb[q] >= (uint32_t)k) {
-      found = 255 - (lane * 4 + q);
-      fa = ab;
-      fc = hb[q];
-    }
-    ab += hb[q];
-  }
-  const uint64_t bal = __ballot(found >= 0);
-  wave_sync();  // every lane has read the histogram
-  const int src = bal ? __ffsll((long long)bal) - 1 : 0;
-  bstar = __builtin_amdgcn_readlane(found, src);
-  kr = k - __builtin_amdgcn_readlane((int)fa, src);
-  cb = __builtin_amdgcn_readlane((int)fc, src);
-  return bal != 0;
-}
-
-// One wave: the cb boundary-bin members, scores s[i] and candidate ids
-// ids[i] (ascending), ranked by larger score, then equal score of lower id;
-// the members ranked below kr get the taken flag (top bit of ids[i]). True
-// when a float32 tie group straddles the kr-th place (then the float64
-// scores must decide).
-__device__ __forceinline__ bool rank_members(const float* s, uint32_t* ids, int cb, int kr,
-                                             int lane) {
-  bool straddle = false;
-  for (int i = lane; i < cb; i += 64) {
-    const float vi = s[i];
-    const uint32_t ci = ids[i] & 0x7fffffffu;
-    int gt = 0, eq_lo = 0, eq = 0;
-    for (int j = 0; j < cb; ++j) {  // ids of earlier rounds may carry the taken flag
-      const float vj = s[j];
-      gt += vj > vi;
-      eq += vj == vi;
-      eq_lo += (vj == vi) & ((ids[j] & 0x7fffffffu) < ci);
-    }
-    // a float32 tie group [gt, gt + eq) cut by the k-th place
-    straddle |= gt < kr && gt + eq > kr;
-    if (gt + eq_lo < kr) ids[i] = ci | 0x80000000u;  // taken
-  }
-  return __ballot(straddle) != 0;
-}
-
-// One wave, usual case: the row's float32 scores in registers, one 256-bin
-// histogram over [min, max] (bins are a monotone function of the value),
-// every candidate in a bin above the k-th one's bin taken, and the members
-// of that boundary bin ranked pairwise (score descending, id ascending).
-// Falls back to select_dense_staged when the boundary bin is large or a
-// float32 tie straddles the k-th place (then the float64 scores decide).
-// v[m]: the score of candidate lane + 64 m (any value past n); s: this
-// wave's LDS row of at least n + 8 floats, scratch for the boundary list and
-// the staged selection.
-template <int D>
-__device__ void select_dense(const DraftArgs& a, const int32_t* slot_tab, float* s,
-                             const float (&v)[kDenseM], int n, size_t row, size_t bh, int nS,
-                             int64_t n_keys, const double* qrow, uint32_t* hist, int lane) {
-  constexpr int M = kDenseM;
-  const int k = topk_dev(a, n, n_keys);
-  int32_t* out = a.sel_idx + row * a.kmax;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  uint64_t valid = 0;
-  float mn = INFINITY, mx = -INFINITY;
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const int c = lane + 64 * m;
-    if (c < n && !__builtin_isnan(v[m])) {
-      valid |= 1ull << m;
-      mn = fminf(mn, v[m]);
-      mx = fmaxf(mx, v[m]);
-    }
-  }
-  mn = wave_min_f32(mn);
-  mx = wave_max_f32(mx);
-  const int n_valid = wave_sum_i(__popcll(valid));
-  bool general = false;
-  uint64_t taken = 0;
-  if (k > 0 && k < n_valid) {
-    const float scale = 256.f / (mx - mn);
-    general = !(mx > mn) || !(scale < INFINITY);  // one value, or a range beyond float32
-    int bstar = 0, kr = 0, cb = 0;
-    if (!general) {
-      auto bin_of = [&](float x) { return bin256(x, mn, scale); };
-      general = !boundary_bin<M>(v, valid, mn, scale, k, hist, lane, bstar, kr, cb) ||
-                cb > kBoundaryMax;
-      if (!general) {
-        // the boundary bin's members, in candidate order: scores over the
-        // row's LDS scores (held in registers now), ids over the histogram
-        uint32_t* ids = hist;
-        int base = 0;
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-          const bool onv = (valid >> m) & 1u;
-          const int bn = bin_of(v[m]);
-          if (onv && bn > bstar) taken |= 1ull << m;
-          const bool inb = onv && bn == bstar;
-          const uint64_t bb = __ballot(inb);
-          // members go to their list position, the others to spare entries
-          // (past the row's candidates, past the list)
-          const int idx = base + __popcll(bb & lt_mask);
-          s[inb ? idx : n + (lane & 7)] = v[m];
-          ids[inb ? idx : 256 + (lane & 7)] = (uint32_t)(lane + 64 * m);
-          base += __popcll(bb);
-        }
-        wave_sync();
-        general = rank_members(s, ids, cb, kr, lane);
-        wave_sync();
-        if (!general) {
-          base = 0;
-#pragma unroll
-          for (int m = 0; m < M; ++m) {
-            const bool inb = ((valid >> m) & 1u) && bin_of(v[m]) == bstar;
-            const uint64_t bb = __ballot(inb);
-            if (inb && (ids[base + __popcll(bb & lt_mask)] & 0x80000000u)) taken |= 1ull << m;
-            base += __popcll(bb);
-          }
-        }
-        wave_sync();
-      }
-    }
-    if (general) {
-      // restore the row's scores and settle it in stages
-#pragma unroll
-      for (int m = 0; m < M; ++m) {
-        const int c = lane + 64 * m;
-        if (c < n) s[c] = v[m];
-      }
-      wave_sync();
-      select_dense_staged<D>(a, slot_tab, s, n, row, bh, nS, n_keys, qrow, hist, lane);
-      return;
-    }
-  } else if (k > 0) {
-    taken = valid;  // every candidate kept
-  }
-  // emit in ascending candidate order
-  int sel_before = 0;
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const bool want = (taken >> m) & 1u;
-    const uint64_t bw = __ballot(want);
-    const int pos = sel_before + __popcll(bw & lt_mask);
-    if (want && pos < k) out[pos] = lane + 64 * m;
-    sel_before += __popcll(bw);
-  }
-  sel_before = sel_before < k ? sel_before : k;
-  for (int pos = sel_before + lane; pos < a.kmax; pos += 64) out[pos] = -1;
-  if (lane == 0) a.sel_cnt[row] = sel_before;
-}
-
-// One wave, split path: the same selection as select_dense, over the row's
-// float32 scores in the workspace (src, ws_stride floats). Lane l holds the
-// candidates [l M, l M + M) (M = ws_stride / 64: a multiple of four, at
-// most kDenseM), so a per-lane count and one prefix sum over the lanes give
-// every list position in candidate order: the boundary bin's members and
-// the emitted ids go straight to their places, with no pass of ballots over
-// the slots.
-template <int D>
-__device__ void select_split(const DraftArgs& a, const int32_t* slot_tab, const float* src,
-                             float* s, int n, size_t row, size_t bh, int nS, int64_t n_keys,
-                             const double* qrow, uint32_t* hist, int lane) {
-  constexpr int MX = kDenseM;
-  const int M = a.ws_stride >> 6;
-  const int cbase = lane * M;
-  const int k = topk_dev(a, n, n_keys);
-  int32_t* out = a.sel_idx + row * a.kmax;
-  // every load issued before the first wait; a slot past this lane's M
-  // reads the row's first four scores and is never used
-  float v[MX];
-#pragma unroll
-  for (int i = 0; i < MX / 4; ++i) {
-    const float4 x = *reinterpret_cast<const float4*>(src + (4 * i < M ? cbase + 4 * i : 0));
-    v[4 * i] = x.x;
-    v[4 * i + 1] = x.y;
-    v[4 * i + 2] = x.z;
-    v[4 * i + 3] = x.w;
-  }
-  uint64_t valid = 0;
-  float mn = INFINITY, mx = -INFINITY;
-#pragma unroll
-  for (int m = 0; m < MX; ++m) {
-    if (m < M && cbase + m < n && !__builtin_isnan(v[m])) {
-      valid |= 1ull << m;
-      mn = fminf(mn, v[m]);
-      mx = fmaxf(mx, v[m]);
-    }
-  }
-  mn = wave_min_f32(mn);
-  mx = wave_max_f32(mx);
-  const int n_valid = wave_sum_i(__popcll(valid));
-  uint64_t taken = 0;
-  if (k > 0 && k < n_valid) {
-    const float scale = 256.f / (mx - mn);
-    bool general = !(mx > mn) || !(scale < INFINITY);  // one value, or a range beyond float32
-    if (!general) {
-      auto bin_of = [&](float x) { return bin256(x, mn, scale); };
-      int bstar = 0, kr = 0, cb = 0;
-      general = !boundary_bin<MX>(v, valid, mn, scale, k, hist, lane, bstar, kr, cb) ||
-                cb > kBoundaryMax;
-      if (!general) {
-        uint64_t member = 0;
-#pragma unroll
-        for (int m = 0; m < MX; ++m) {
-          if ((valid >> m) & 1u) {
-            const int bn = bin_of(v[m]);
-            if (bn > bstar) taken |= 1ull << m;
-            else if (bn == bstar) member |= 1ull << m;
-          }
-        }
-        if (cb == kr) {  // the whole boundary bin is kept
-          taken |= member;
-        } else {
-          // the members, in candidate order: scores over this wave's LDS
-          // row, ids over the histogram; each lane's run starts at its
-          // exclusive prefix of the member counts
-          uint32_t* ids = hist;
-          const int pm = __popcll(member);
-          const int mbase = (int)wave_prefix_sum_dpp((uint32_t)pm) - pm;
-          int pos = mbase;
-#pragma unroll
-          for (int m = 0; m < MX; ++m) {
-            if ((member >> m) & 1u) {
-              s[pos] = v[m];
-              ids[pos] = (uint32_t)(cbase + m);
-              ++pos;
-            }
-          }
-          wave_sync();
-          general = rank_members(s, ids, cb, kr, lane);
-          wave_sync();
-          if (!general) {
-            pos = mbase;
-#pragma unroll
-            for (int m = 0; m < MX; ++m) {
-              if ((member >> m) & 1u) {
-                if (ids[pos] & 0x80000000u) taken |= 1ull << m;
-                ++pos;
-              }
-            }
-          }
-          wave_sync();
-        }
-      }
-    }
-    if (general) {
-      // the row's scores into this wave's LDS row, settled in stages
-#pragma unroll
-      for (int m = 0; m < MX; ++m)
-        if (m < M && cbase + m < n) s[cbase + m] = v[m];
-      wave_sync();
-      select_dense_staged<D>(a, slot_tab, s, n, row, bh, nS, n_keys, qrow, hist, lane);
-      return;
-    }
-  } else if (k > 0) {
-    taken = valid;  // every candidate kept
-  }
-  // emit in ascending candidate order: this lane's run starts at its
-  // exclusive prefix of the taken counts
-  const int pt = __popcll(taken);
-  const int incl = (int)wave_prefix_sum_dpp((uint32_t)pt);
-  const int total = __builtin_amdgcn_readlane(incl, 63);
-  int pos = incl - pt;
-  for (uint64_t t = taken; t; t &= t - 1, ++pos)
-    if (pos < k) out[pos] = cbase + __builtin_ctzll(t);
-  const int cnt = total < k ? total : k;
-  for (int p = cnt + lane; p < a.kmax; p += 64) out[p] = -1;
-  if (lane == 0) a.sel_cnt[row] = cnt;
-}
 
 template <int D>
 __global__ __launch_bounds__(64 * kDenseWaves, 1) void draft_dense_kernel(DraftArgs a) {
