@@ -141,10 +141,13 @@ typedef double f64x4 __attribute__((ext_vector_type(4)));
 // (up to 484 candidates per row): one's selection overlaps the other's
 // scoring, and a half tile of key loads in flight per wave suffices.
 constexpr int kTileMaxCand = 768;
-constexpr int kTileWaves = 8;  // 16 rows: two per wave in the selection phase
-
-template <int D>
-__global__ __launch_bounds__(64 * kTileWaves, 4) void draft_tile_kernel(DraftArgs a) {
+// Fewer tiles than CUs (1536x2688 step: 189) leave CUs idle, so there each
+// tile takes 16 waves, one row per wave in the selection phase (draft
+// 39-40 -> 35 us); from one tile per CU on, 8 waves (two rows each) and two
+// workgroups per CU.
+constexpr long long kTileWideBelow = 256;
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW, 4) void draft_tile_kernel(DraftArgs a) {
   extern __shared__ double smem[];
   double* sc = smem;                                  // [16][row_stride] scores
   double* sa = sc + 16 * (size_t)a.row_stride;        // [D][16] pooled queries, d-major
@@ -187,7 +190,7 @@ __global__ __launch_bounds__(64 * kTileWaves, 4) void draft_tile_kernel(DraftArg
   // A operand: row rr of the tile is query block (by0 + rr/4, bx0 + rr%4),
   // staged d-major ([D][16]) so that the 16 rows of one k read 128
   // contiguous bytes (conflict-free); padding rows of an edge tile are 0
-  for (int e = tid; e < 16 * D; e += 64 * kTileWaves) {
+  for (int e = tid; e < 16 * D; e += 64 * NW) {
     const int rr = e % 16, d = e / 16;
     const int qy = by0 + (rr >> 2), qx = bx0 + (rr & 3);
     sa[e] = (qy < nby && qx < nbx)
@@ -227,9 +230,9 @@ __global__ __launch_bounds__(64 * kTileWaves, 4) void draft_tile_kernel(DraftArg
   // One half tile (16 of the 32 k-steps) of key loads in flight at a time;
   // the other resident workgroup covers their latency.
   constexpr int HS = D / 8;  // k-steps per half tile
-  const int ntiles = U > 16 * wave ? (U - 16 * wave + 16 * kTileWaves - 1) / (16 * kTileWaves) : 0;
+  const int ntiles = U > 16 * wave ? (U - 16 * wave + 16 * NW - 1) / (16 * NW) : 0;
   for (int it = 0; it < ntiles; ++it) {
-    const int t = wave + it * kTileWaves;
+    const int t = wave + it * NW;
     const int u = 16 * t + r;
     int p, y, x;
     const double* kp = key_ptr(u, p, y, x);
@@ -258,7 +261,7 @@ __global__ __launch_bounds__(64 * kTileWaves, 4) void draft_tile_kernel(DraftArg
   __syncthreads();  // scores complete; the pooled-query region becomes the histograms
 
   uint32_t* hist = hist_all + wave * 256;
-  for (int ro = wave; ro < 16; ro += kTileWaves) {
+  for (int ro = wave; ro < 16; ro += NW) {
     const int qy = by0 + (ro >> 2), qx = bx0 + (ro & 3);
     if (qy >= nby || qx >= nbx) continue;  // uniform per wave
     int ylo, yhi, xlo, xhi;
@@ -598,21 +601,27 @@ hipError_t launch_split(DraftArgs a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int D>
-hipError_t launch_tile(const DraftArgs& a, hipStream_t s) {
-  const long long tasks = (long long)a.B * a.NH * a.ntb_q * ((a.nby + 3) / 4) * ((a.nbx + 3) / 4);
+template <int D, int NW>
+hipError_t launch_tile_nw(const DraftArgs& a, long long tasks, hipStream_t s) {
   const long long wgs = 8 * ((tasks + 7) / 8);
-  constexpr size_t kAux = (size_t)D * 16 * sizeof(double) > kTileWaves * 256 * 4
+  constexpr size_t kAux = (size_t)D * 16 * sizeof(double) > NW * 256 * 4
                              ? (size_t)D * 16 * sizeof(double)
-                             : kTileWaves * 256 * 4;
+                             : NW * 256 * 4;
   const size_t shmem = 16 * (size_t)a.row_stride * sizeof(double) + kAux;
   if (shmem > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute((const void*)draft_tile_kernel<D>,
+    hipError_t e = hipFuncSetAttribute((const void*)draft_tile_kernel<D, NW>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(draft_tile_kernel<D>, dim3((unsigned)wgs), dim3(64 * kTileWaves), shmem, s, a);
+  hipLaunchKernelGGL((draft_tile_kernel<D, NW>), dim3((unsigned)wgs), dim3(64 * NW), shmem, s, a);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_tile(const DraftArgs& a, hipStream_t s) {
+  const long long tasks = (long long)a.B * a.NH * a.ntb_q * ((a.nby + 3) / 4) * ((a.nbx + 3) / 4);
+  return tasks < kTileWideBelow ? launch_tile_nw<D, 16>(a, tasks, s)
+                                : launch_tile_nw<D, 8>(a, tasks, s);
 }
 
 template <int GX, int D, int NW>
