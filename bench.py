@@ -58,6 +58,8 @@ def parse():
                     help="no GPU work: turn the rocprofv3 output of a --kernel-trace --stats run "
                          "and of --pmc FETCH_SIZE / --pmc WRITE_SIZE runs of this script into "
                          "profiles/<kernels>_<workload>.md and the workload's traffic.json entry")
+    ap.add_argument("--sq2-dir", default=None,
+                    help="with --summarize-profiles: a rocprofv3 --pmc run of SQ_ISSUE_COUNTERS")
     ap.add_argument("--sq-dir", default=None,
                     help="with --summarize-profiles: the output of a rocprofv3 --pmc run of this "
                          "script with the SQ_COUNTERS set (instruction mix, matrix-core busy "
@@ -595,6 +597,14 @@ def _counter_per_dispatch(d, counter):
 SQ_COUNTERS = ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_LDS",
                "SQ_LDS_BANK_CONFLICT", "SQ_WAVES", "SQ_BUSY_CU_CYCLES", "GRBM_GUI_ACTIVE")
 N_SIMDS, N_XCDS = 1024, 8  # MI355X: 256 CUs x 4 SIMDs, 8 XCDs
+# The issue-state counters of a second pass: where the waves' cycles go
+# (waiting on counters and barriers, waiting to issue, issuing VALU or LDS
+# work) and how many of the matrix cores' busy cycles also issued a vector
+# instruction (co-execution). The SQ_WAVE_CYCLES / SQ_WAIT_* / SQ_ACTIVE_*
+# counters are in units of 4 cycles.
+SQ_ISSUE_COUNTERS = ("SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY",
+                     "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_VALU_MFMA_COEXEC_CYCLES",
+                     "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
 
 
 def _per_kernel_counters(d, names):
@@ -651,7 +661,8 @@ def summarize_profiles(args):
                       "f_factor": probe_bytes / (fcopy["FETCH_SIZE"] * 1024.0),
                       "w_factor": probe_bytes / (wcopy["WRITE_SIZE"] * 1024.0)}
     sq = _per_kernel_counters(args.sq_dir, SQ_COUNTERS)[0] if args.sq_dir else None
-    _write_summary(args, stats, bench, cnt, per_kernel, sq)
+    sq2 = _per_kernel_counters(args.sq2_dir, SQ_ISSUE_COUNTERS)[0] if args.sq2_dir else None
+    _write_summary(args, stats, bench, cnt, per_kernel, sq, sq2)
 
 
 def _write_traffic(args, fetch_b, write_b, fa, wa, fc, wc, f_factor, w_factor, nf, nw):
@@ -674,7 +685,7 @@ def _write_traffic(args, fetch_b, write_b, fa, wa, fc, wc, f_factor, w_factor, n
         f.write("\n")
 
 
-def _write_summary(args, stats, bench, cnt, per_kernel=None, sq=None):
+def _write_summary(args, stats, bench, cnt, per_kernel=None, sq=None, sq2=None):
     sw = (f"--steps {bench['steps']} --warmup {bench['warmup']}" if bench else "--steps S --warmup W")
     kernels = sorted({_short(r["Name"]) for r in stats})
     names = sorted({k.split("<")[0].replace("_kernel", "") for k in kernels})
@@ -691,9 +702,12 @@ def _write_summary(args, stats, bench, cnt, per_kernel=None, sq=None):
                if cnt else []),
              *([f"    rocprofv3 --pmc {' '.join(SQ_COUNTERS)} --output-format csv -d SQ_DIR -o pmc "
                 f"-- {cmd_b}"] if sq else []),
+             *([f"    rocprofv3 --pmc {' '.join(SQ_ISSUE_COUNTERS)} --output-format csv -d SQ2_DIR "
+                f"-o pmc -- {cmd_b}"] if sq2 else []),
              f"    python3 bench.py --workload {args.workload} --copy-probe-mib {args.copy_probe_mib} "
              f"--summarize-profiles TRACE_DIR {'FETCH_DIR WRITE_DIR' if cnt else '- -'} "
-             f"{'--sq-dir SQ_DIR ' if sq else ''}--bench-log BENCH_LOG", "",
+             f"{'--sq-dir SQ_DIR ' if sq else ''}{'--sq2-dir SQ2_DIR ' if sq2 else ''}"
+             f"--bench-log BENCH_LOG", "",
              "## Kernel durations (rocprofv3 --stats)", "",
              "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
     for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
@@ -757,6 +771,34 @@ def _write_summary(args, stats, bench, cnt, per_kernel=None, sq=None):
             busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0) / (N_SIMDS * cyc) if cyc else 0.0
             lines.append(f"| {k} | " + " | ".join(f"{c.get(n, 0):.0f}" for n in SQ_COUNTERS) +
                          f" | {ghz:.2f} | {busy:.3f} |")
+        lines.append("")
+    if sq2:
+        lines += ["## Where the wave-cycles go (rocprofv3 --pmc, a second pass)", "",
+                  "Per launch, as fractions of the waves' resident cycles (SQ_WAVE_CYCLES; the "
+                  "SQ_WAVE_CYCLES, SQ_WAIT_* and SQ_ACTIVE_INST_* counters count 4-cycle units): "
+                  "waiting on memory counters or a barrier (SQ_WAIT_ANY), waiting to issue an "
+                  "instruction that is ready (SQ_WAIT_INST_ANY), and issuing any, VALU or LDS "
+                  "instructions (SQ_ACTIVE_INST_*). Co-execution is the share of the matrix cores' "
+                  "busy cycles in which a normal vector instruction issued as well "
+                  "(SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES). The fractions overlap "
+                  "(a wave can wait on a counter while another of its instructions issues).", "",
+                  "| kernel | " + " | ".join(SQ_ISSUE_COUNTERS) + " | waiting | waiting to issue | "
+                  "issuing | VALU | LDS | MFMA busy | co-execution |",
+                  "|---|" + "---|" * (len(SQ_ISSUE_COUNTERS) + 7)]
+        for k in sorted(sq2, key=lambda k: -avg_us.get(k, 0)):
+            c = sq2[k]
+            wc = c.get("SQ_WAVE_CYCLES", 0)
+            cyc = c.get("GRBM_GUI_ACTIVE", 0) / N_XCDS
+            mb = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0)
+
+            def frac(n):
+                return f"{c.get(n, 0) / wc:.3f}" if wc else "-"
+            busy = mb / (N_SIMDS * cyc) if cyc else 0.0
+            coex = c.get("SQ_VALU_MFMA_COEXEC_CYCLES", 0) / mb if mb else 0.0
+            lines.append(f"| {k} | " + " | ".join(f"{c.get(n, 0):.0f}" for n in SQ_ISSUE_COUNTERS) +
+                         f" | {frac('SQ_WAIT_ANY')} | {frac('SQ_WAIT_INST_ANY')} | "
+                         f"{frac('SQ_ACTIVE_INST_ANY')} | {frac('SQ_ACTIVE_INST_VALU')} | "
+                         f"{frac('SQ_ACTIVE_INST_LDS')} | {busy:.3f} | {coex:.3f} |")
         lines.append("")
     with open(out, "w") as f:
         f.write("\n".join(lines))
