@@ -222,6 +222,63 @@ lcsa_status lcsa_partition_pool(const lcsa_geom* g, const void* q, const void* k
   return device_status(launch_partition_pool(a, (hipStream_t)stream), fn);
 }
 
+lcsa_status lcsa_kv_cache_copy(lcsa_kv_cache* dst, const lcsa_kv_cache* src, void* stream) {
+  const char* fn = "lcsa_kv_cache_copy";
+  lcsa_status st;
+  if ((st = check_cache(src)) || (st = check_cache(dst))) return st;
+  if (dst == src) return fail(LCSA_ERR_PARAM, "%s: dst and src are the same cache", fn);
+  if (dst->batch != src->batch || dst->heads != src->heads || dst->head_dim != src->head_dim ||
+      dst->nby != src->nby || dst->nbx != src->nbx || dst->n_slots != src->n_slots)
+    return fail(LCSA_ERR_SHAPE,
+                "%s: dst (B %d, NH %d, D %d, %dx%d blocks, %d slots) and src (B %d, NH %d, "
+                "D %d, %dx%d blocks, %d slots) differ", fn, dst->batch, dst->heads,
+                dst->head_dim, dst->nby, dst->nbx, dst->n_slots, src->batch, src->heads,
+                src->head_dim, src->nby, src->nbx, src->n_slots);
+  if (dst->dtype != src->dtype)
+    return fail(LCSA_ERR_DTYPE, "%s: dst dtype %d, src dtype %d", fn, dst->dtype, src->dtype);
+  if ((st = check_ptr(dst->k_ring, "dst k_ring")) || (st = check_ptr(dst->v_ring, "dst v_ring")) ||
+      (st = check_ptr(dst->kpool_ring, "dst kpool_ring")) ||
+      (st = check_ptr(src->k_ring, "src k_ring")) || (st = check_ptr(src->v_ring, "src v_ring")) ||
+      (st = check_ptr(src->kpool_ring, "src kpool_ring")))
+    return st;
+  // per (batch, head): n_slots slots of nS blocks (rings [B][NH][n_slots]...)
+  const size_t esize = src->dtype == LCSA_BF16 ? 2 : 4;
+  const size_t nS = (size_t)src->nby * src->nbx;
+  const size_t rows = (size_t)src->batch * src->heads;
+  const size_t slot_kv = nS * 128 * src->head_dim * esize;
+  const size_t slot_kp = nS * src->head_dim * sizeof(double);
+  const size_t pitch_kv = slot_kv * src->n_slots, pitch_kp = slot_kp * src->n_slots;
+  const uintptr_t d_ptr[3] = {(uintptr_t)dst->k_ring, (uintptr_t)dst->v_ring,
+                              (uintptr_t)dst->kpool_ring};
+  const uintptr_t s_ptr[3] = {(uintptr_t)src->k_ring, (uintptr_t)src->v_ring,
+                              (uintptr_t)src->kpool_ring};
+  const size_t len[3] = {rows * pitch_kv, rows * pitch_kv, rows * pitch_kp};
+  for (int x = 0; x < 3; ++x)
+    for (int y = 0; y < 3; ++y)
+      if (d_ptr[x] < s_ptr[y] + len[y] && s_ptr[y] < d_ptr[x] + len[x])
+        return fail(LCSA_ERR_PARAM, "%s: a dst ring overlaps a src ring", fn);
+  const hipStream_t s = (hipStream_t)stream;
+  for (int32_t i = 0; i < src->count; ++i) {
+    const size_t slot = (size_t)((src->head + i) % src->n_slots);
+    const size_t skv = slot * slot_kv, skp = slot * slot_kp;
+    hipError_t e = hipMemcpy2DAsync((char*)dst->k_ring + skv, pitch_kv,
+                                    (const char*)src->k_ring + skv, pitch_kv, slot_kv, rows,
+                                    hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess)
+      e = hipMemcpy2DAsync((char*)dst->v_ring + skv, pitch_kv, (const char*)src->v_ring + skv,
+                           pitch_kv, slot_kv, rows, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess)
+      e = hipMemcpy2DAsync((char*)dst->kpool_ring + skp, pitch_kp,
+                           (const char*)src->kpool_ring + skp, pitch_kp, slot_kp, rows,
+                           hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return device_status(e, fn);
+  }
+  dst->head = src->head;
+  dst->count = src->count;
+  for (int32_t i = 0; i < LCSA_MAX_SLOTS; ++i) dst->abs_tb[i] = src->abs_tb[i];
+  return ok();
+}
+
 lcsa_status lcsa_draft_workspace_size(const lcsa_geom* gq, const lcsa_kv_cache* cache,
                                       const lcsa_select_params* params, size_t* bytes_out) {
   lcsa_status st;

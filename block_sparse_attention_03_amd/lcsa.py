@@ -77,6 +77,7 @@ def load_library(path: str = LIB_PATH):
                                ctypes.c_size_t],
         "lcsa_kv_cache_append": [C, c_int32, c_int64, POINTER(c_int32)],
         "lcsa_kv_cache_evict": [C, c_int32],
+        "lcsa_kv_cache_copy": [C, C, c_void_p],
         "lcsa_kv_cache_view": [C, POINTER(c_int32), POINTER(c_int32), POINTER(c_int64)],
         "lcsa_topk_count": [P, c_int32, c_int32, POINTER(c_int32)],
         "lcsa_max_topk": [G, c_int64, C, P, POINTER(c_int32)],
@@ -197,6 +198,11 @@ def lcsa_kv_cache_view(cache: KvCacheStruct):
     tbs = (c_int64 * MAX_SLOTS)()
     _check(lib.lcsa_kv_cache_view(ctypes.byref(cache), ctypes.byref(n), slots, tbs))
     return list(slots[:n.value]), list(tbs[:n.value])
+
+
+def lcsa_kv_cache_copy(dst: KvCacheStruct, src: KvCacheStruct, stream=None):
+    lib = load_library()
+    _check(lib.lcsa_kv_cache_copy(ctypes.byref(dst), ctypes.byref(src), _stream(stream)))
 
 
 def lcsa_topk_count(params: SelectParams, n_allowed: int, n_keys: int) -> int:
@@ -382,6 +388,10 @@ class KVCache:
 
     def view(self):
         return lcsa_kv_cache_view(self.c)
+
+    def copy_from(self, other: "KVCache", stream=None):
+        """Take over other's held blocks and metadata (lcsa_kv_cache_copy)."""
+        lcsa_kv_cache_copy(self.c, other.c, stream)
 
 
 class StepBuffers:

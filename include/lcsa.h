@@ -31,6 +31,8 @@
  *                          q read from q_blk (lcsa_block_sparse_attn_tok: q
  *                          read in token layout, so q_blk is never written)
  *   lcsa_kv_cache_evict    drop the oldest temporal blocks beyond capacity
+ * and, between steps, lcsa_kv_cache_copy saves a stream's ring into a spare
+ * one (a checkpoint) or restores it.
  *
  * Conventions shared by every entry point:
  *   - All buffers are allocated and owned by the caller, workspaces
@@ -172,6 +174,25 @@ lcsa_status lcsa_kv_cache_evict(lcsa_kv_cache* cache, int32_t keep_tb);
  * output array may be NULL. */
 lcsa_status lcsa_kv_cache_view(const lcsa_kv_cache* cache, int32_t* n_out,
                                int32_t* slots, int64_t* abs_tb);
+
+/* Checkpoint and resume of a stream ([HW] 2.3: the ring of cached segments
+ * is the only state a streaming layer carries from one step to the next).
+ * Copies what src holds into dst, slot for slot: for each held temporal
+ * block its K, V^T and pooled-K slots of every (batch, head), then src's
+ * head, count and abs_tb, so that dst continues the stream exactly where
+ * src stood (bitwise: the next steps on dst give the results they would
+ * have given on src). dst keeps its own buffers; slots src does not hold
+ * are left as they were. dst and src must come from lcsa_kv_cache_init
+ * with the same batch, heads, head_dim, grid and n_slots
+ * (LCSA_ERR_SHAPE), and dtype (LCSA_ERR_DTYPE); dst == src, or a dst ring
+ * overlapping any src ring, is LCSA_ERR_PARAM. The device copies are
+ * enqueued on `stream` (device to device, no host staging) and dst's
+ * metadata is updated when the call returns, so work that reads dst or
+ * writes src goes on the same stream after it. A device error is
+ * LCSA_ERR_DEVICE with dst's metadata unchanged (its ring may be partly
+ * written). Save a checkpoint by copying the live cache into a spare one
+ * of the same shape; resume by copying it back. */
+lcsa_status lcsa_kv_cache_copy(lcsa_kv_cache* dst, const lcsa_kv_cache* src, void* stream);
 
 /* ---- selection helpers (host only) ------------------------------------ */
 

@@ -395,3 +395,38 @@ def test_noalloc_backward_validation_before_any_device_call(lib):
     # an empty chunk is a no-op (no scratch lookup, no device call)
     L.lcsa_block_sparse_attn_bwd_noalloc(L.make_geom(1, 2, 128, 0, 16, 24, L.LCSA_BF16), P, P, P, P,
                                          P, P, P, P, 4, P, P, P, stream=0)
+
+
+def test_ring_copy_validates_before_any_device_call(lib):
+    """lcsa_kv_cache_copy, the checkpoint / resume of a stream's ring ([HW]
+    "How FlashVSR works" 2.3: the cache of past segments is the state a
+    stream carries between steps), refuses rings of another shape or dtype,
+    the same cache, and overlapping rings, and leaves dst's metadata as it
+    was. Fake device addresses: every case fails before its first HIP call."""
+    P = lambda a: type("P", (), {"data_ptr": lambda s: a})()
+
+    def cache(base, heads=3, D=128, nby=6, nbx=11, dtype=L.LCSA_BF16, n_slots=4):
+        kv, pool = ring_bytes(nby, nbx, heads, D, dtype, n_slots)
+        c = L.KvCacheStruct()
+        L.lcsa_kv_cache_init(c, 1, heads, D, nby, nbx, dtype, n_slots, P(base), P(base + kv),
+                             P(base + 2 * kv), kv, kv, pool)
+        return c
+
+    span = 1 << 32  # far apart: no ring of one fake cache overlaps the other's
+    src = cache(FAKE)
+    L.lcsa_kv_cache_append(src, 3, 0)
+    bad = {
+        2: [cache(span, heads=2), cache(span, D=64), cache(span, nbx=10), cache(span, n_slots=5)],
+        3: [cache(span, dtype=L.LCSA_F32)],
+        4: [cache(FAKE + 4096), cache(FAKE)],  # overlapping rings
+    }
+    for status, dsts in bad.items():
+        for dst in dsts:
+            before = (dst.head, dst.count, list(dst.abs_tb))
+            with pytest.raises(L.LcsaError) as e:
+                L.lcsa_kv_cache_copy(dst, src, stream=0)
+            assert e.value.status == status, (status, str(e.value))
+            assert (dst.head, dst.count, list(dst.abs_tb)) == before
+    with pytest.raises(L.LcsaError) as e:
+        L.lcsa_kv_cache_copy(src, src, stream=0)
+    assert e.value.status == 4 and "same cache" in str(e.value)
